@@ -1,0 +1,131 @@
+"""CPU oracle for the Q8_0 quantized matmul (TEST INFRASTRUCTURE ONLY).
+
+Thin ctypes wrapper over ``q8o.c``: a plain, slow, single-threaded C
+restatement of the method (see the header of ``q8o.c`` for the passages it
+follows and the readings it takes).  Only the tests, the smoke check and the
+benchmark's CPU-baseline leg may import this package.  It shares no code with
+the HIP library, and the HIP library never calls it.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "q8o.c")
+_LIB = os.path.join(_HERE, "libq8o.so")
+
+BLOCK_ELEMS = 32
+BLOCK_BYTES = 34
+
+_lib = None
+
+
+def build() -> str:
+    """Compile q8o.c into oracle/libq8o.so with gcc (always recompiles)."""
+    cmd = [
+        "gcc", "-std=c11", "-O2", "-ffp-contract=off", "-fno-fast-math",
+        "-fPIC", "-shared", "-Wall", "-Wextra", "-o", _LIB + ".tmp", _SRC, "-lm",
+    ]
+    subprocess.run(cmd, check=True)
+    os.replace(_LIB + ".tmp", _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB):
+        build()
+    lib = ctypes.CDLL(_LIB)
+    i64, i32, vp = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p
+    lib.q8o_f16_from_f32.argtypes = [ctypes.c_float]
+    lib.q8o_f16_from_f32.restype = ctypes.c_uint16
+    lib.q8o_f16_to_f64.argtypes = [ctypes.c_uint16]
+    lib.q8o_f16_to_f64.restype = ctypes.c_double
+    lib.q8o_quantize.argtypes = [vp, i64, i64, vp]
+    lib.q8o_quantize.restype = ctypes.c_int
+    lib.q8o_matmul.argtypes = [vp, i64, i64, vp, i64, vp, vp, vp]
+    lib.q8o_matmul.restype = ctypes.c_int
+    lib.q8o_moe_grouped.argtypes = [vp, i32, i64, i64, vp, i32, vp, i32, i64, vp, vp]
+    lib.q8o_moe_grouped.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def _ptr(a: np.ndarray) -> int:
+    assert a.flags["C_CONTIGUOUS"], "oracle inputs must be C-contiguous"
+    return a.ctypes.data
+
+
+def f16_from_f32(v: float) -> int:
+    """binary16 bits of fp32 v, round to nearest even (written from IEEE 754)."""
+    return int(_load().q8o_f16_from_f32(float(np.float32(v))))
+
+
+def f16_to_f64(bits: int) -> float:
+    return float(_load().q8o_f16_to_f64(int(bits)))
+
+
+def quantize(x: np.ndarray) -> np.ndarray:
+    """x: fp32 [rows][k] -> uint8 [rows][k/32*34] Q8_0 blocks."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    if x.ndim == 1:
+        x = x[None, :]
+    rows, k = x.shape
+    if k % BLOCK_ELEMS:
+        raise ValueError("k must be a multiple of 32")
+    out = np.empty((rows, k // BLOCK_ELEMS * BLOCK_BYTES), dtype=np.uint8)
+    rc = _load().q8o_quantize(_ptr(x), rows, k, _ptr(out))
+    if rc != 0:
+        raise ValueError(f"q8o_quantize failed ({rc})")
+    return out
+
+
+def matmul(w: np.ndarray, xq: np.ndarray, in_dim: int, *, want_mag: bool = True,
+           want_blocksums: bool = False):
+    """w: uint8 [out_dim][row_bytes], xq: uint8 [n_tok][row_bytes].
+
+    Returns (out fp32 [n_tok][out_dim], mag fp64 or None, blocksums int32
+    [n_tok][out_dim][nb] or None)."""
+    w = np.ascontiguousarray(w, dtype=np.uint8)
+    xq = np.ascontiguousarray(xq, dtype=np.uint8)
+    nb = in_dim // BLOCK_ELEMS
+    row_bytes = nb * BLOCK_BYTES
+    out_dim = w.size // row_bytes if row_bytes else 0
+    n_tok = xq.size // row_bytes if row_bytes else 0
+    out = np.empty((n_tok, out_dim), dtype=np.float32)
+    mag = np.empty((n_tok, out_dim), dtype=np.float64) if want_mag else None
+    bs = np.empty((n_tok, out_dim, nb), dtype=np.int32) if want_blocksums else None
+    rc = _load().q8o_matmul(
+        _ptr(w), in_dim, out_dim, _ptr(xq), n_tok, _ptr(out),
+        _ptr(mag) if mag is not None else None,
+        _ptr(bs) if bs is not None else None)
+    if rc != 0:
+        raise ValueError(f"q8o_matmul failed ({rc})")
+    return out, mag, bs
+
+
+def moe_grouped(expert_w, selected: np.ndarray, xq: np.ndarray, in_dim: int,
+                out_dim: int, x_rows: int, want_mag: bool = True):
+    """expert_w: list of uint8 [out_dim][row_bytes] arrays (index = expert id).
+
+    Returns (out fp32 [n_tok][n_used][out_dim], mag or None, invalid_count)."""
+    selected = np.ascontiguousarray(selected, dtype=np.int32)
+    n_tok, n_used = selected.shape
+    xq = np.ascontiguousarray(xq, dtype=np.uint8)
+    mats = [np.ascontiguousarray(m, dtype=np.uint8) for m in expert_w]
+    table = (ctypes.c_void_p * len(mats))(*[m.ctypes.data for m in mats])
+    out = np.empty((n_tok, n_used, out_dim), dtype=np.float32)
+    mag = np.empty((n_tok, n_used, out_dim), dtype=np.float64) if want_mag else None
+    rc = _load().q8o_moe_grouped(
+        ctypes.cast(table, ctypes.c_void_p), len(mats), in_dim, out_dim,
+        _ptr(selected), n_used, _ptr(xq), x_rows, n_tok, _ptr(out),
+        _ptr(mag) if mag is not None else None)
+    if rc < 0:
+        raise ValueError(f"q8o_moe_grouped failed ({rc})")
+    return out, mag, rc
