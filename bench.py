@@ -1,0 +1,311 @@
+#!/usr/bin/env python3
+"""Benchmark of the Q8_0 quantized matmul on one MI355X.
+
+Headline (the single JSON line's `value`): the decode matvec workload
+attn_q_b (in_dim 1024 -> out_dim 32768, n_tok 1).  One step = quantize the
+fp32 activation row (q8_0_quantize_act) + the Q8_0 matmul, back to back on
+one stream.  value = algorithmic bytes of the step / step time, in GB/s.
+Inputs are resident in HBM before timing starts; the weights rotate through
+16 independent copies (570 MB) so the 256 MB Infinity Cache cannot serve
+them.
+
+The same line also carries, under "secondary", the other workloads timed the
+same way (decode5, moe, prefill_a, prefill_b) with their own roofline
+fractions; prefill reports int8 TOPS against the int8 MFMA peak.
+
+Options: --steps K --warmup W (headline loop), --gpus N (only 1 is
+supported: this is a single-GPU path), --quick (headline only),
+--calibrate (adds a plain device copy of known size for counter scaling),
+--cpu-seconds S (time budget of the CPU-oracle baseline, 0 to skip).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, GB/s
+INT8_MFMA_PEAK_TOPS = 5000.0  # MI355X dense int8 matrix peak, TOPS
+METRIC = "Q8_0 matmul GB/s at n_tok=1 & int8 TOPS at n_tok≥2048; % of roofline"
+ROT = 16                      # weight copies rotated through in decode loops
+
+
+def row_bytes(k):
+    return k // 32 * 34
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+class Timer:
+    """Event pairs around selected launches on torch's current stream (the
+    stream every library call is enqueued on)."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.pairs = {}
+
+    def around(self, name, fn):
+        ev0 = self.torch.cuda.Event(enable_timing=True)
+        ev1 = self.torch.cuda.Event(enable_timing=True)
+        ev0.record()
+        r = fn()
+        ev1.record()
+        self.pairs.setdefault(name, []).append((ev0, ev1))
+        return r
+
+    def mean_us(self, name):
+        p = self.pairs.get(name, [])
+        return 1000.0 * sum(a.elapsed_time(b) for a, b in p) / len(p) if p else None
+
+
+def timed_loop(torch, step, steps, warmup):
+    for i in range(warmup):
+        step(i, None)
+    torch.cuda.synchronize()
+    timer = Timer(torch)
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(i, timer)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    return (t1 - t0) / steps, timer
+
+
+def bench_attn_q_b(torch, q8, wl, steps, warmup):
+    d = wl.attn_q_b("cuda")
+    k, n = d["in_dim"], d["out_dim"]
+    ws = [q8.q8_0_quantize_act(wl.attn_q_b("cuda", copy=c)["w"]) for c in range(ROT)]
+    x = d["x"]
+    xq = torch.empty((1, row_bytes(k)), dtype=torch.uint8, device="cuda")
+    out = torch.empty((1, n), dtype=torch.float32, device="cuda")
+
+    def step(i, timer):
+        q8.q8_0_quantize_act(x, out=xq)
+        call = lambda: q8.q8_0_matmul(ws[i % ROT], xq, k, n, 1, out=out)
+        timer.around("matvec", call) if timer else call()
+
+    sec, timer = timed_loop(torch, step, steps, warmup)
+    mm_bytes = n * row_bytes(k) + row_bytes(k) + 4 * n
+    q_bytes = 4 * k + row_bytes(k)
+    kern_us = timer.mean_us("matvec")
+    return dict(sec=sec, step_bytes=mm_bytes + q_bytes, kernel_bytes=mm_bytes, kernel_us=kern_us,
+                plan=q8.q8_0_matmul_plan(k, n, 1, 0))
+
+
+def bench_decode5(torch, q8, wl, steps, warmup):
+    rot = 8
+    sets = [wl.decode5("cuda", copy=c) for c in range(rot)]
+    wq = [[q8.q8_0_quantize_act(p["w"]) for p in s] for s in sets]
+    xs = [p["x"] for p in sets[0]]
+    dims = [(p["in_dim"], p["out_dim"]) for p in sets[0]]
+    xqs = [torch.empty((1, row_bytes(k)), dtype=torch.uint8, device="cuda") for k, _ in dims]
+    outs = [torch.empty((1, n), dtype=torch.float32, device="cuda") for _, n in dims]
+    del sets
+
+    def step(i, timer):
+        for j, (k, n) in enumerate(dims):
+            q8.q8_0_quantize_act(xs[j], out=xqs[j])
+            call = lambda: q8.q8_0_matmul(wq[i % rot][j], xqs[j], k, n, 1, out=outs[j])
+            timer.around(f"mm{j}", call) if timer else call()
+
+    sec, timer = timed_loop(torch, step, steps, warmup)
+    mm_bytes = sum(n * row_bytes(k) + row_bytes(k) + 4 * n for k, n in dims)
+    q_bytes = sum(4 * k + row_bytes(k) for k, _ in dims)
+    per = [dict(name=wl.DECODE5[j][0], kernel_us=timer.mean_us(f"mm{j}"),
+                kernel_bytes=n * row_bytes(k) + row_bytes(k) + 4 * n) for j, (k, n) in enumerate(dims)]
+    return dict(sec=sec, step_bytes=mm_bytes + q_bytes, kernel_bytes=mm_bytes,
+                kernel_us=sum(p["kernel_us"] for p in per), per_matrix=per)
+
+
+def bench_moe(torch, q8, wl, steps, warmup):
+    cfg = wl.MOE
+    E, kk, T, D, F = cfg["n_expert"], cfg["n_used"], cfg["n_tok"], cfg["d_model"], cfg["d_ff"]
+    sel = wl.moe_routing().cuda()
+    x, mid = wl.moe_acts("cuda")
+    stacks, shared = {}, {}
+    for which, (rows, cols) in (("gate", (F, D)), ("up", (F, D)), ("down", (D, F))):
+        st = torch.empty((E, rows, row_bytes(cols)), dtype=torch.uint8, device="cuda")
+        for e in range(E):
+            q8.q8_0_quantize_act(wl.moe_expert(e, which, "cuda"), out=st[e])
+        stacks[which] = st
+        shared[which] = q8.q8_0_quantize_act(wl.moe_expert(-1, which, "cuda"))
+    tables = {w: q8.expert_table(stacks[w]) for w in stacks}
+    xq = torch.empty((T, row_bytes(D)), dtype=torch.uint8, device="cuda")
+    midq = torch.empty((mid.shape[0], row_bytes(F)), dtype=torch.uint8, device="cuda")
+    o_g = torch.empty((T, kk, F), device="cuda")
+    o_u = torch.empty((T, kk, F), device="cuda")
+    o_d = torch.empty((T, kk, D), device="cuda")
+    s_g = torch.empty((T, F), device="cuda")
+    s_u = torch.empty((T, F), device="cuda")
+    s_d = torch.empty((T, D), device="cuda")
+    wsm = torch.empty(q8.q8_0_moe_workspace_bytes(T, kk, E), dtype=torch.uint8, device="cuda")
+    wsd = q8.matmul_workspace(D, F, T)
+    wsd2 = q8.matmul_workspace(F, D, T)
+
+    def step(i, timer):
+        tm = (lambda name, f: timer.around(name, f)) if timer else (lambda name, f: f())
+        q8.q8_0_quantize_act(x, out=xq)
+        tm("grouped", lambda: q8.q8_0_moe_grouped(tables["gate"], E, sel, xq, D, F, 0, out=o_g, workspace=wsm))
+        tm("grouped", lambda: q8.q8_0_moe_grouped(tables["up"], E, sel, xq, D, F, 0, out=o_u, workspace=wsm))
+        tm("shared", lambda: q8.q8_0_matmul(shared["gate"], xq, D, F, T, out=s_g, workspace=wsd))
+        tm("shared", lambda: q8.q8_0_matmul(shared["up"], xq, D, F, T, out=s_u, workspace=wsd))
+        q8.q8_0_quantize_act(mid, out=midq)
+        tm("grouped", lambda: q8.q8_0_moe_grouped(tables["down"], E, sel, midq[:T * kk], F, D, 1, out=o_d, workspace=wsm))
+        tm("shared", lambda: q8.q8_0_matmul(shared["down"], midq[T * kk:], F, D, T, out=s_d, workspace=wsd2))
+
+    sec, timer = timed_loop(torch, step, steps, warmup)
+    touched = int(torch.unique(sel).numel())
+    mat = F * row_bytes(D)  # bytes of one expert matrix (gate/up/down are equal)
+    pairs = T * kk
+    g_bytes = touched * 3 * mat + 2 * (pairs * F * 4 + T * row_bytes(D)) + pairs * (row_bytes(F) + D * 4)
+    s_bytes = 3 * mat + 2 * (T * F * 4 + T * row_bytes(D)) + T * (row_bytes(F) + D * 4)
+    q_bytes = T * (4 * D + row_bytes(D)) + mid.shape[0] * (4 * F + row_bytes(F))
+    ops = 2 * (pairs + T) * 3 * F * D
+    return dict(sec=sec, step_bytes=g_bytes + s_bytes + q_bytes, kernel_bytes=g_bytes / 3,
+                kernel_us=timer.mean_us("grouped"), shared_us=timer.mean_us("shared"),
+                touched_experts=touched, ops=ops)
+
+
+def bench_prefill(torch, q8, wl, name, steps, warmup):
+    d = wl.prefill(name, "cuda")
+    k, n, t = d["in_dim"], d["out_dim"], d["n_tok"]
+    wq = q8.q8_0_quantize_act(d["w"])
+    x = d["x"]
+    del d
+    xq = torch.empty((t, row_bytes(k)), dtype=torch.uint8, device="cuda")
+    out = torch.empty((t, n), dtype=torch.float32, device="cuda")
+    ws = q8.matmul_workspace(k, n, t)
+
+    def step(i, timer):
+        tm = (lambda nm, f: timer.around(nm, f)) if timer else (lambda nm, f: f())
+        tm("quantize", lambda: q8.q8_0_quantize_act(x, out=xq))
+        tm("gemm", lambda: q8.q8_0_matmul(wq, xq, k, n, t, out=out, workspace=ws))
+
+    sec, timer = timed_loop(torch, step, steps, warmup)
+    ops = 2 * t * n * k
+    return dict(sec=sec, ops=ops, kernel_us=timer.mean_us("gemm"), quant_us=timer.mean_us("quantize"),
+                quant_bytes=t * (4 * k + row_bytes(k)),
+                kernel_bytes=n * row_bytes(k) + t * row_bytes(k) + 4 * t * n,
+                plan=q8.q8_0_matmul_plan(k, n, t, ws.numel()))
+
+
+def cpu_baseline(wl, seconds):
+    """The oracle (single-threaded C, as committed) on the attn_q_b workload,
+    repeated for about `seconds` seconds on this host's CPU."""
+    import numpy as np
+    import oracle
+    d = wl.attn_q_b("cpu")
+    wq = oracle.quantize(d["w"].numpy())
+    x = d["x"].numpy()
+    k, n = d["in_dim"], d["out_dim"]
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        xq = oracle.quantize(x)
+        oracle.matmul(wq, xq, k, want_mag=False)
+        reps += 1
+        if time.perf_counter() - t0 >= seconds:
+            break
+    sec = (time.perf_counter() - t0) / reps
+    step_bytes = n * row_bytes(k) + row_bytes(k) + 4 * n + 4 * k + row_bytes(k)
+    return dict(value=round(step_bytes / sec / 1e9, 4), unit="GB/s", cores=1, kind="oracle",
+                sample=f"full attn_q_b step (quantize 1x1024 + matmul 32768x1024), {reps} repetitions "
+                       f"in {reps * sec:.1f} s, single thread; {np.round(sec * 1e3, 2)} ms/step")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=100)
+    ap.add_argument("--quick", action="store_true")
+    ap.add_argument("--calibrate", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this Q8_0 path runs on exactly one GPU; --gpus must be 1 "
+              "(multi-GPU sharding is described in DESIGN.md, not built).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import q8_quantized_matmul_amd as q8
+    import workloads as wl
+    torch.cuda.set_device(0)
+
+    if args.calibrate:
+        # A plain device-to-device copy of 1 GiB, for scaling HBM byte counters.
+        a = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+
+    log("[bench] attn_q_b")
+    h = bench_attn_q_b(torch, q8, wl, args.steps, args.warmup)
+    value = h["step_bytes"] / h["sec"] / 1e9
+    ach = h["kernel_bytes"] / (h["kernel_us"] * 1e-6) / 1e9
+    result = {
+        "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(h["sec"] * 1e3, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "int8",
+        "data": "synthetic",
+        "config": {"workload": "attn_q_b decode matvec: Q8_0 W[32768x1024] x Q8_0 x[1x1024] "
+                               "-> fp32, step = quantize_act + matmul, 16 rotating weight copies",
+                   "in_dim": 1024, "out_dim": 32768, "n_tok": 1, "kernel_plan": list(h["plan"])},
+        "roofline": {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "matvec_kernel<16,1,1,RG>", "kernel_us": round(h["kernel_us"], 3),
+                     "bytes_per_launch": h["kernel_bytes"]},
+    }
+    secondary = []
+    if not args.quick:
+        log("[bench] decode5")
+        d5 = bench_decode5(torch, q8, wl, max(args.steps // 2, 10), args.warmup)
+        secondary.append({
+            "workload": "decode5 (5 projections back to back, n_tok 1)",
+            "value": round(d5["step_bytes"] / d5["sec"] / 1e9, 2), "unit": "GB/s",
+            "ms_per_step": round(d5["sec"] * 1e3, 5),
+            "kernels_GBs": round(d5["kernel_bytes"] / (d5["kernel_us"] * 1e-6) / 1e9, 1),
+            "frac_hbm_kernels": round(d5["kernel_bytes"] / (d5["kernel_us"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+            "per_matrix": [{"name": p["name"], "kernel_us": round(p["kernel_us"], 3),
+                            "GBs": round(p["kernel_bytes"] / (p["kernel_us"] * 1e-6) / 1e9, 1)}
+                           for p in d5["per_matrix"]]})
+        log("[bench] moe")
+        mo = bench_moe(torch, q8, wl, max(args.steps // 50, 5), 3)
+        secondary.append({
+            "workload": "moe (64 tokens x 8 of 256 experts + shared, gate/up/down)",
+            "value": round(mo["step_bytes"] / mo["sec"] / 1e9, 2), "unit": "GB/s",
+            "ms_per_step": round(mo["sec"] * 1e3, 4), "touched_experts": mo["touched_experts"],
+            "grouped_kernel_us": round(mo["kernel_us"], 2),
+            "grouped_GBs": round(mo["kernel_bytes"] / (mo["kernel_us"] * 1e-6) / 1e9, 1),
+            "frac_hbm_grouped": round(mo["kernel_bytes"] / (mo["kernel_us"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+            "shared_kernel_us": round(mo["shared_us"], 2)})
+        for name in ("prefill_a", "prefill_b"):
+            log(f"[bench] {name}")
+            pf = bench_prefill(torch, q8, wl, name, max(args.steps // 40, 10), 5)
+            tops = pf["ops"] / (pf["kernel_us"] * 1e-6) / 1e12
+            secondary.append({
+                "workload": name, "value": round(pf["ops"] / pf["sec"] / 1e12, 2), "unit": "TOPS",
+                "ms_per_step": round(pf["sec"] * 1e3, 4), "gemm_kernel_us": round(pf["kernel_us"], 2),
+                "gemm_TOPS": round(tops, 1), "frac_int8_mfma": round(tops / INT8_MFMA_PEAK_TOPS, 4),
+                "quantize_us": round(pf["quant_us"], 2),
+                "quantize_GBs": round(pf["quant_bytes"] / (pf["quant_us"] * 1e-6) / 1e9, 1),
+                "plan": list(pf["plan"])})
+    result["secondary"] = secondary
+    if args.cpu_seconds > 0:
+        log("[bench] cpu baseline")
+        result["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

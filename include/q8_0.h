@@ -1,0 +1,163 @@
+/*
+ * q8_0.h -- C ABI of the Q8_0 quantized matmul library for AMD MI355X (gfx950).
+ *
+ * The operation is the ds4 engine's Q8_0 matmul/matvec and its Q8_0 expert
+ * matmuls, as described on the ds4-learning pages:
+ *   - "Part 6: 代码走读", trace 3 (GPU matmul 与 matvec): Q8_0 weights times
+ *     Q8_0 activations, arguments (out, weights, in_dim, out_dim, x, n_tok),
+ *     in_dim must be a multiple of the 32-value Q8_0 block.
+ *   - "Part 3: 模型架构", section 2: the per-block quantization rule
+ *     (amax, scale = amax/127, q = roundf(x/scale)) and y = x @ W.
+ *   - "Part 6: 代码走读", trace 5 (GPU MoE): per-token selected expert lists
+ *     drive one expert matmul per (token, slot).
+ *   - "Part 6: GPU 加速", section 1 (ds4_gpu.h): backend types never appear in
+ *     the interface, the caller owns every buffer, work is enqueued
+ *     asynchronously and the caller synchronizes before reading results.
+ *
+ * Q8_0 block: 32 values in 34 bytes -- a little-endian binary16 scale d
+ * followed by 32 int8 quants q; value_i = d * q_i.  A matrix [rows][k] is
+ * stored as rows * (k/32) consecutive blocks, row-major (row r, block b at
+ * byte offset (r * (k/32) + b) * 34).
+ *
+ * Conventions for every call below:
+ *   - All tensor pointers are DEVICE pointers owned by the caller; the library
+ *     allocates and frees nothing.  Inputs are read-only.
+ *   - Calls only enqueue work on `stream` (0 = the null stream) and return;
+ *     the caller synchronizes the stream before reading outputs.
+ *   - Argument errors are detected on the host before anything is enqueued
+ *     and returned as a negative Q8_0_E* code; nothing is written then.
+ *   - n_tok == 0 or out_dim == 0 is a successful no-op.
+ *   - Pointers must be at least 2-byte aligned (Q8_0_EALIGN otherwise); the
+ *     fast kernels need 4-byte alignment (16-byte for fp32 inputs) and fall
+ *     back to a generic kernel when it is missing.
+ *   - Results are deterministic: the same inputs give bit-identical outputs.
+ *   - Calls on different streams touching disjoint outputs are independent.
+ */
+#ifndef Q8_0_H
+#define Q8_0_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t *hipStream_t;
+
+#define Q8_0_BLOCK_ELEMS 32
+#define Q8_0_BLOCK_BYTES 34
+
+enum {
+    Q8_0_OK = 0,
+    Q8_0_EINVAL = -1,     /* bad size, null pointer, bad mode */
+    Q8_0_EALIGN = -2,     /* pointer alignment below 2 bytes */
+    Q8_0_ELAUNCH = -3,    /* the HIP runtime rejected a kernel launch */
+    Q8_0_EWORKSPACE = -4, /* workspace missing or smaller than required */
+    Q8_0_ENODEV = -5      /* no usable gfx950 device for the stream */
+};
+
+/* Kernel variants (for q8_0_matmul_debug; 0 lets the library choose). */
+enum {
+    Q8_0_KERNEL_AUTO = 0,
+    Q8_0_KERNEL_GENERIC = 1, /* one block per lane, any shape           */
+    Q8_0_KERNEL_MATVEC = 2,  /* weight-streaming matvec, small n_tok     */
+    Q8_0_KERNEL_MFMA = 3     /* int8 MFMA GEMM, large n_tok              */
+};
+
+/* Quantize activations to Q8_0 ("Part 3: 模型架构", section 2 rule, per
+ * 32-value block with a binary16 scale).
+ *   x   : fp32 [n_tok][in_dim], row-major.
+ *   x_q : n_tok * (in_dim/32) * 34 bytes, written.
+ * Per block: amax = max|x_i|; d32 = amax/127 (IEEE fp32 division);
+ * q_i = roundf(x_i / d32) (IEEE division, halves away from zero) clamped to
+ * [-127, 127]; stored scale = binary16(d32), round to nearest even.  A block
+ * with amax == 0 (or d32 == 0) is all zeros.  A block holding a NaN or an
+ * infinity, or whose d32 does not fit binary16 (d32 >= 65520), is stored with
+ * scale 0x7E00 (NaN) and zero quants, so every output that uses it is NaN.
+ * Errors: in_dim % 32 != 0, negative sizes, null pointers -> Q8_0_EINVAL. */
+int q8_0_quantize_act(void *x_q, const float *x, int64_t n_tok, int64_t in_dim,
+                      hipStream_t stream);
+
+/* Workspace bytes q8_0_matmul would use for its fastest plan on this shape
+ * (split-K partial sums); 0 when the plan needs none. */
+size_t q8_0_matmul_workspace_bytes(int64_t in_dim, int64_t out_dim, int64_t n_tok);
+
+/* Q8_0 matmul ("Part 6: 代码走读", trace 3: ds4_gpu_matmul_q8_0_tensor):
+ *   out[t][o] = sum_b fp32(d_w[o][b]) * fp32(d_x[t][b]) * S_b[t][o],
+ *   S_b[t][o] = sum_{i<32} qw[o][b][i] * qx[t][b][i]  (exact int32).
+ *   out : fp32 [n_tok][out_dim], written.
+ *   w   : Q8_0 [out_dim][in_dim/32] blocks.
+ *   x_q : Q8_0 [n_tok][in_dim/32] blocks (e.g. from q8_0_quantize_act).
+ *   workspace / workspace_bytes : optional caller scratch (device memory) for
+ *     split-K partials; with less than q8_0_matmul_workspace_bytes() the
+ *     library picks a plan that fits (same results up to fp32 summation order).
+ * The fp32 result is within 1e-5 * sum_b |d_w d_x S_b| + 1e-6 of the exact
+ * value; S_b itself is exact.  Errors: in_dim % 32 != 0 or in_dim == 0 with
+ * out_dim > 0, negative sizes, null pointers -> Q8_0_EINVAL. */
+int q8_0_matmul(float *out, const void *w, int64_t in_dim, int64_t out_dim,
+                const void *x_q, int64_t n_tok, void *workspace,
+                size_t workspace_bytes, hipStream_t stream);
+
+/* Workspace bytes q8_0_moe_grouped needs (routing tables and lists). */
+size_t q8_0_moe_workspace_bytes(int64_t n_tok, int32_t n_used, int32_t n_expert);
+
+/* Grouped expert matmul ("Part 6: 代码走读", trace 5: the gate/up and down
+ * expert projections of ds4_gpu_routed_moe_one_tensor, one weight set per call).
+ *   expert_w : DEVICE array of n_expert device pointers; expert e's weights are
+ *              Q8_0 [out_dim][in_dim/32] blocks at expert_w[e].
+ *   selected : device int32 [n_tok][n_used], token -> expert ids (slot order).
+ *   x_q      : Q8_0 rows; x_rows == 0: one row per token (gate/up input),
+ *              x_rows == 1: one row per (token, slot) pair, row t*n_used + j
+ *              (down input).
+ *   out      : fp32 [n_tok][n_used][out_dim], written:
+ *              out[t][j] = matmul(W_{selected[t][j]}, x row).
+ * Routing happens on the GPU (no host round trip): counts, offsets and a
+ * stable expert-major pair list are built in `workspace`, then each touched
+ * expert's weights are streamed once for all of its pairs.  Duplicate ids in
+ * a row are computed independently.  An id outside [0, n_expert) cannot be
+ * seen on the host: its pair's output row is set to NaN and the int32 at byte
+ * offset 0 of `workspace` holds, once the stream reaches the end of the call,
+ * the number of such pairs.
+ * Errors: bad sizes/mode/null pointers -> Q8_0_EINVAL; workspace smaller than
+ * q8_0_moe_workspace_bytes() -> Q8_0_EWORKSPACE. */
+int q8_0_moe_grouped(float *out, const void *const *expert_w, int32_t n_expert,
+                     int64_t in_dim, int64_t out_dim, const int32_t *selected,
+                     int32_t n_used, const void *x_q, int32_t x_rows,
+                     int64_t n_tok, void *workspace, size_t workspace_bytes,
+                     hipStream_t stream);
+
+/* Test hook: q8_0_matmul with a forced kernel variant and split-K count
+ * (0 = automatic) that also writes every block's exact integer dot S_b into
+ * blocksums (device int32 [n_tok][out_dim][in_dim/32]) when it is not NULL.
+ * Errors as q8_0_matmul, plus Q8_0_EINVAL when the forced variant cannot run
+ * this shape, and Q8_0_EWORKSPACE when a forced split needs more workspace. */
+int q8_0_matmul_debug(float *out, int32_t *blocksums, const void *w,
+                      int64_t in_dim, int64_t out_dim, const void *x_q,
+                      int64_t n_tok, void *workspace, size_t workspace_bytes,
+                      int32_t variant, int32_t split_k, hipStream_t stream);
+
+/* Test hook: q8_0_moe_grouped that also writes each pair's block sums into
+ * blocksums (device int32 [n_tok*n_used][out_dim][in_dim/32]). */
+int q8_0_moe_grouped_debug(float *out, int32_t *blocksums,
+                           const void *const *expert_w, int32_t n_expert,
+                           int64_t in_dim, int64_t out_dim,
+                           const int32_t *selected, int32_t n_used,
+                           const void *x_q, int32_t x_rows, int64_t n_tok,
+                           void *workspace, size_t workspace_bytes,
+                           hipStream_t stream);
+
+/* Host-only: the kernel variant and split-K count q8_0_matmul would use for
+ * this shape and workspace, assuming suitably aligned pointers.  Touches no
+ * device.  Returns Q8_0_OK or Q8_0_EINVAL for an invalid shape. */
+int q8_0_matmul_plan(int64_t in_dim, int64_t out_dim, int64_t n_tok,
+                     size_t workspace_bytes, int32_t *variant, int32_t *split_k);
+
+/* Static description of a status code. */
+const char *q8_0_strerror(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* Q8_0_H */

@@ -1,0 +1,220 @@
+"""Python binding of libq8_0.so, the gfx950 Q8_0 quantized matmul library.
+
+Argument marshalling only: every function forwards torch tensors' device
+pointers and the current torch stream to the C ABI in include/q8_0.h, where
+all checks and all computation happen.  torch supplies device memory (outputs
+and scratch are allocated with torch when the caller passes none) and
+streams.  If the library has not been built, importing this package raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libq8_0.so")
+
+BLOCK_ELEMS = 32
+BLOCK_BYTES = 34
+
+Q8_0_OK = 0
+Q8_0_EINVAL = -1
+Q8_0_EALIGN = -2
+Q8_0_ELAUNCH = -3
+Q8_0_EWORKSPACE = -4
+Q8_0_ENODEV = -5
+
+KERNEL_AUTO = 0
+KERNEL_GENERIC = 1
+KERNEL_MATVEC = 2
+KERNEL_MFMA = 3
+
+
+class Q8Error(RuntimeError):
+    def __init__(self, code: int, where: str):
+        super().__init__(f"{where}: {q8_0_strerror(code)} (status {code})")
+        self.code = code
+
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is missing; build it with `python q8_quantized_matmul_amd/build.py`")
+
+_lib = ctypes.CDLL(LIB_PATH)
+_i64, _i32, _vp, _sz = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t
+_sig = {
+    "q8_0_quantize_act": ([_vp, _vp, _i64, _i64, _vp], ctypes.c_int),
+    "q8_0_matmul_workspace_bytes": ([_i64, _i64, _i64], _sz),
+    "q8_0_matmul": ([_vp, _vp, _i64, _i64, _vp, _i64, _vp, _sz, _vp], ctypes.c_int),
+    "q8_0_moe_workspace_bytes": ([_i64, _i32, _i32], _sz),
+    "q8_0_moe_grouped": ([_vp, _vp, _i32, _i64, _i64, _vp, _i32, _vp, _i32, _i64, _vp, _sz, _vp],
+                         ctypes.c_int),
+    "q8_0_matmul_debug": ([_vp, _vp, _vp, _i64, _i64, _vp, _i64, _vp, _sz, _i32, _i32, _vp],
+                          ctypes.c_int),
+    "q8_0_moe_grouped_debug": ([_vp, _vp, _vp, _i32, _i64, _i64, _vp, _i32, _vp, _i32, _i64, _vp,
+                                _sz, _vp], ctypes.c_int),
+    "q8_0_matmul_plan": ([_i64, _i64, _i64, _sz, ctypes.POINTER(_i32), ctypes.POINTER(_i32)],
+                         ctypes.c_int),
+    "q8_0_strerror": ([ctypes.c_int], ctypes.c_char_p),
+}
+for _name, (_args, _res) in _sig.items():
+    _fn = getattr(_lib, _name)
+    _fn.argtypes = _args
+    _fn.restype = _res
+
+EXPORTED = tuple(_sig)
+
+
+def raw_library() -> ctypes.CDLL:
+    return _lib
+
+
+def q8_0_strerror(code: int) -> str:
+    return _lib.q8_0_strerror(int(code)).decode()
+
+
+def row_bytes(in_dim: int) -> int:
+    return in_dim // BLOCK_ELEMS * BLOCK_BYTES
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _dev(t: torch.Tensor, name: str, dtype=None) -> int:
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}")
+    return t.data_ptr()
+
+
+def _check(code: int, where: str) -> None:
+    if code != Q8_0_OK:
+        raise Q8Error(code, where)
+
+
+def q8_0_quantize_act(x: torch.Tensor, out: torch.Tensor = None) -> torch.Tensor:
+    """x: fp32 [n_tok][in_dim] -> uint8 [n_tok][in_dim/32*34] Q8_0 blocks."""
+    if x.dim() == 1:
+        x = x.unsqueeze(0)
+    n_tok, in_dim = x.shape
+    if out is None:
+        out = torch.empty((n_tok, row_bytes(in_dim)), dtype=torch.uint8, device=x.device)
+    _check(_lib.q8_0_quantize_act(_dev(out, "out"), _dev(x, "x", torch.float32), n_tok, in_dim,
+                                  _stream()), "q8_0_quantize_act")
+    return out
+
+
+def q8_0_matmul_workspace_bytes(in_dim: int, out_dim: int, n_tok: int) -> int:
+    return int(_lib.q8_0_matmul_workspace_bytes(in_dim, out_dim, n_tok))
+
+
+def matmul_workspace(in_dim: int, out_dim: int, n_tok: int, device="cuda") -> torch.Tensor:
+    n = q8_0_matmul_workspace_bytes(in_dim, out_dim, n_tok)
+    return torch.empty(max(n, 1), dtype=torch.uint8, device=device)
+
+
+def q8_0_matmul(w: torch.Tensor, x_q: torch.Tensor, in_dim: int, out_dim: int, n_tok: int,
+                out: torch.Tensor = None, workspace: torch.Tensor = None) -> torch.Tensor:
+    """out fp32 [n_tok][out_dim] = Q8_0 weights [out_dim][in_dim] x Q8_0 x_q [n_tok][in_dim]."""
+    if out is None:
+        out = torch.empty((n_tok, out_dim), dtype=torch.float32, device=w.device)
+    if workspace is None:
+        workspace = matmul_workspace(in_dim, out_dim, n_tok, w.device)
+    _check(_lib.q8_0_matmul(_dev(out, "out", torch.float32), _dev(w, "w"), in_dim, out_dim,
+                            _dev(x_q, "x_q"), n_tok, _dev(workspace, "workspace"),
+                            workspace.numel() * workspace.element_size(), _stream()),
+           "q8_0_matmul")
+    return out
+
+
+def q8_0_matmul_debug(w, x_q, in_dim, out_dim, n_tok, variant=KERNEL_AUTO, split_k=0,
+                      blocksums=True, out=None, workspace=None):
+    """q8_0_matmul with a forced kernel variant / split; returns (out, blocksums or None)."""
+    if out is None:
+        out = torch.empty((n_tok, out_dim), dtype=torch.float32, device=w.device)
+    bs = None
+    if blocksums:
+        bs = torch.empty((n_tok, out_dim, in_dim // BLOCK_ELEMS), dtype=torch.int32,
+                         device=w.device)
+    if workspace is None:
+        workspace = matmul_workspace(in_dim, out_dim, n_tok, w.device)
+    _check(_lib.q8_0_matmul_debug(_dev(out, "out", torch.float32),
+                                  _dev(bs, "blocksums") if bs is not None else None,
+                                  _dev(w, "w"), in_dim, out_dim, _dev(x_q, "x_q"), n_tok,
+                                  _dev(workspace, "workspace"),
+                                  workspace.numel() * workspace.element_size(), variant, split_k,
+                                  _stream()), "q8_0_matmul_debug")
+    return out, bs
+
+
+def q8_0_matmul_plan(in_dim: int, out_dim: int, n_tok: int, workspace_bytes: int):
+    v, s = _i32(0), _i32(0)
+    _check(_lib.q8_0_matmul_plan(in_dim, out_dim, n_tok, workspace_bytes, ctypes.byref(v),
+                                 ctypes.byref(s)), "q8_0_matmul_plan")
+    return v.value, s.value
+
+
+def q8_0_moe_workspace_bytes(n_tok: int, n_used: int, n_expert: int) -> int:
+    return int(_lib.q8_0_moe_workspace_bytes(n_tok, n_used, n_expert))
+
+
+def expert_table(mats) -> torch.Tensor:
+    """Device int64 table of expert weight base pointers from a list of tensors
+    (or from one stacked [n_expert, ...] tensor)."""
+    if isinstance(mats, torch.Tensor):
+        base = mats.data_ptr()
+        stride = mats[0].numel() * mats.element_size()
+        ptrs = [base + e * stride for e in range(mats.shape[0])]
+        device = mats.device
+    else:
+        ptrs = [m.data_ptr() for m in mats]
+        device = mats[0].device
+    return torch.tensor(ptrs, dtype=torch.int64).to(device)
+
+
+def _moe(debug, table, n_expert, selected, x_q, in_dim, out_dim, x_rows, out, workspace):
+    n_tok, n_used = selected.shape
+    if out is None:
+        out = torch.empty((n_tok, n_used, out_dim), dtype=torch.float32, device=x_q.device)
+    if workspace is None:
+        workspace = torch.empty(q8_0_moe_workspace_bytes(n_tok, n_used, n_expert),
+                                dtype=torch.uint8, device=x_q.device)
+    args = [_dev(table, "expert table", torch.int64), n_expert, in_dim, out_dim,
+            _dev(selected, "selected", torch.int32), n_used, _dev(x_q, "x_q"), x_rows, n_tok,
+            _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+            _stream()]
+    bs = None
+    if debug:
+        bs = torch.empty((n_tok * n_used, out_dim, in_dim // BLOCK_ELEMS), dtype=torch.int32,
+                         device=x_q.device)
+        _check(_lib.q8_0_moe_grouped_debug(_dev(out, "out", torch.float32), _dev(bs, "bs"),
+                                           *args), "q8_0_moe_grouped_debug")
+    else:
+        _check(_lib.q8_0_moe_grouped(_dev(out, "out", torch.float32), *args), "q8_0_moe_grouped")
+    return out, bs, workspace
+
+
+def q8_0_moe_grouped(table, n_expert, selected, x_q, in_dim, out_dim, x_rows=0, out=None,
+                     workspace=None):
+    """out fp32 [n_tok][n_used][out_dim]; table = expert_table(...).  Returns
+    (out, workspace); workspace[:4] viewed as int32 counts invalid expert ids."""
+    out, _, ws = _moe(False, table, n_expert, selected, x_q, in_dim, out_dim, x_rows, out,
+                      workspace)
+    return out, ws
+
+
+def q8_0_moe_grouped_debug(table, n_expert, selected, x_q, in_dim, out_dim, x_rows=0, out=None,
+                           workspace=None):
+    return _moe(True, table, n_expert, selected, x_q, in_dim, out_dim, x_rows, out, workspace)
+
+
+def moe_invalid_count(workspace: torch.Tensor) -> int:
+    return int(workspace[:4].view(torch.int32).item())

@@ -1,0 +1,218 @@
+// api.hip -- the C ABI of include/q8_0.h: host-side argument checks, kernel
+// selection and launches on the caller's stream.  Nothing here allocates
+// device memory; every buffer, including scratch, belongs to the caller.
+#include <stdint.h>
+
+#include <algorithm>
+#include <atomic>
+#include <cstring>
+
+#include "launch.h"
+#include "q8_0.h"
+
+namespace {
+
+constexpr int64_t kMatmulMfmaMinTokens = 16;  // matrix units from 16 tokens on
+constexpr int32_t kMaxExperts = 8192;
+constexpr int kMaxDevices = 64;
+
+// 1 = gfx950, -1 = other architecture, 0 = not looked at yet.
+std::atomic<int> g_device_ok[kMaxDevices];
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+int check_device() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return Q8_0_ENODEV;
+  int state = g_device_ok[dev].load(std::memory_order_relaxed);
+  if (state == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return Q8_0_ENODEV;
+    state = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : -1;
+    g_device_ok[dev].store(state, std::memory_order_relaxed);
+  }
+  return state == 1 ? Q8_0_OK : Q8_0_ENODEV;
+}
+
+int status_of(hipError_t e) { return e == hipSuccess ? Q8_0_OK : Q8_0_ELAUNCH; }
+
+// Plan for q8_0_matmul: which kernel, how many K splits.
+struct Plan {
+  int32_t variant;
+  int32_t split;
+};
+
+bool matvec_ok(int64_t in_dim) { return q8::matvec_shape(in_dim, nullptr); }
+
+Plan make_plan(int64_t in_dim, int64_t out_dim, int64_t n_tok, size_t ws_bytes, bool fast_align) {
+  Plan p{Q8_0_KERNEL_GENERIC, 1};
+  if (!fast_align) return p;
+  if (n_tok >= kMatmulMfmaMinTokens && q8::gemm_supported(in_dim)) {
+    p.variant = Q8_0_KERNEL_MFMA;
+    int split = q8::gemm_auto_split(in_dim, out_dim, n_tok);
+    while (split > 1 && q8::gemm_workspace_bytes(out_dim, n_tok, split) > ws_bytes) --split;
+    p.split = split;
+  } else if (matvec_ok(in_dim)) {
+    p.variant = Q8_0_KERNEL_MATVEC;
+  }
+  return p;
+}
+
+int validate_matmul(const float *out, const void *w, int64_t in_dim, int64_t out_dim,
+                    const void *x_q, int64_t n_tok) {
+  if (in_dim < 0 || out_dim < 0 || n_tok < 0) return Q8_0_EINVAL;
+  if (in_dim % Q8_0_BLOCK_ELEMS != 0) return Q8_0_EINVAL;
+  if (n_tok == 0 || out_dim == 0) return Q8_0_OK;
+  if (in_dim == 0) return Q8_0_EINVAL;
+  if (!out || !w || !x_q) return Q8_0_EINVAL;
+  if (!aligned(out, 4) || !aligned(w, 2) || !aligned(x_q, 2)) return Q8_0_EALIGN;
+  return Q8_0_OK;
+}
+
+int run_matmul(float *out, int32_t *blocksums, const void *w, int64_t in_dim, int64_t out_dim,
+               const void *x_q, int64_t n_tok, void *workspace, size_t workspace_bytes,
+               int32_t variant, int32_t split_k, hipStream_t stream) {
+  int st = validate_matmul(out, w, in_dim, out_dim, x_q, n_tok);
+  if (st != Q8_0_OK || n_tok == 0 || out_dim == 0) return st;
+  if (workspace == nullptr) workspace_bytes = 0;
+  if (workspace && !aligned(workspace, 16)) return Q8_0_EALIGN;
+  if (split_k < 0 || variant < 0 || variant > Q8_0_KERNEL_MFMA) return Q8_0_EINVAL;
+  const bool fast_align = aligned(w, 4) && aligned(x_q, 4);
+  Plan p = make_plan(in_dim, out_dim, n_tok, workspace_bytes, fast_align);
+  if (variant != Q8_0_KERNEL_AUTO) {
+    if (variant != Q8_0_KERNEL_GENERIC && !fast_align) return Q8_0_EINVAL;
+    if (variant == Q8_0_KERNEL_MATVEC && !matvec_ok(in_dim)) return Q8_0_EINVAL;
+    if (variant == Q8_0_KERNEL_MFMA && !q8::gemm_supported(in_dim)) return Q8_0_EINVAL;
+    if (variant != p.variant) p.split = 1;
+    p.variant = variant;
+  }
+  if (split_k > 0) {
+    if (p.variant != Q8_0_KERNEL_MFMA && split_k != 1) return Q8_0_EINVAL;
+    p.split = split_k;
+  }
+  if (p.variant == Q8_0_KERNEL_MFMA && p.split > 1 &&
+      q8::gemm_workspace_bytes(out_dim, n_tok, p.split) > workspace_bytes)
+    return Q8_0_EWORKSPACE;
+  if ((st = check_device()) != Q8_0_OK) return st;
+  switch (p.variant) {
+    case Q8_0_KERNEL_MFMA:
+      return status_of(q8::launch_gemm(out, blocksums, w, in_dim, out_dim, x_q, n_tok, p.split,
+                                       static_cast<float *>(workspace), stream));
+    case Q8_0_KERNEL_MATVEC:
+      return status_of(q8::launch_matvec(out, blocksums, w, in_dim, out_dim, x_q, n_tok, stream));
+    default:
+      return status_of(q8::launch_generic(out, blocksums, w, in_dim, out_dim, x_q, n_tok, stream));
+  }
+}
+
+int run_moe(float *out, int32_t *blocksums, const void *const *expert_w, int32_t n_expert,
+            int64_t in_dim, int64_t out_dim, const int32_t *selected, int32_t n_used,
+            const void *x_q, int32_t x_rows, int64_t n_tok, void *workspace,
+            size_t workspace_bytes, hipStream_t stream) {
+  if (n_expert < 1 || n_expert > kMaxExperts || n_used < 1 || n_tok < 0 || in_dim < 0 ||
+      out_dim < 0 || (x_rows != 0 && x_rows != 1) || in_dim % Q8_0_BLOCK_ELEMS != 0)
+    return Q8_0_EINVAL;
+  if (n_tok * (int64_t)n_used > INT32_MAX) return Q8_0_EINVAL;
+  if (n_tok == 0 || out_dim == 0) return Q8_0_OK;
+  if (in_dim == 0) return Q8_0_EINVAL;
+  if (!out || !expert_w || !selected || !x_q) return Q8_0_EINVAL;
+  if (!aligned(out, 4) || !aligned(selected, 4) || !aligned(expert_w, 8) || !aligned(x_q, 2))
+    return Q8_0_EALIGN;
+  if (!workspace || workspace_bytes < q8_0_moe_workspace_bytes(n_tok, n_used, n_expert))
+    return Q8_0_EWORKSPACE;
+  if (!aligned(workspace, 16)) return Q8_0_EALIGN;
+  int st = check_device();
+  if (st != Q8_0_OK) return st;
+  // Expert matrices are only known on the device; the fast kernel needs the
+  // x rows and every expert base dword aligned, which torch allocations and
+  // even-block-count row slices satisfy.  x_q alignment is checked here.
+  const bool fast = aligned(x_q, 4) && matvec_ok(in_dim);
+  return status_of(q8::launch_moe(out, blocksums, expert_w, n_expert, in_dim, out_dim, selected,
+                                  n_used, x_q, x_rows, n_tok, static_cast<int32_t *>(workspace),
+                                  fast, stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+int q8_0_quantize_act(void *x_q, const float *x, int64_t n_tok, int64_t in_dim,
+                      hipStream_t stream) {
+  if (n_tok < 0 || in_dim < 0 || in_dim % Q8_0_BLOCK_ELEMS != 0) return Q8_0_EINVAL;
+  if (n_tok == 0 || in_dim == 0) return Q8_0_OK;
+  if (!x_q || !x) return Q8_0_EINVAL;
+  if (!aligned(x, 4) || !aligned(x_q, 2)) return Q8_0_EALIGN;
+  int st = check_device();
+  if (st != Q8_0_OK) return st;
+  const bool fast = aligned(x, 16) && aligned(x_q, 4) && (in_dim / Q8_0_BLOCK_ELEMS) % 2 == 0;
+  return status_of(q8::launch_quantize(x_q, x, n_tok, in_dim, fast, stream));
+}
+
+size_t q8_0_matmul_workspace_bytes(int64_t in_dim, int64_t out_dim, int64_t n_tok) {
+  if (in_dim <= 0 || out_dim <= 0 || n_tok <= 0 || in_dim % Q8_0_BLOCK_ELEMS != 0) return 0;
+  Plan p = make_plan(in_dim, out_dim, n_tok, SIZE_MAX, true);
+  return p.variant == Q8_0_KERNEL_MFMA ? q8::gemm_workspace_bytes(out_dim, n_tok, p.split) : 0;
+}
+
+int q8_0_matmul(float *out, const void *w, int64_t in_dim, int64_t out_dim, const void *x_q,
+                int64_t n_tok, void *workspace, size_t workspace_bytes, hipStream_t stream) {
+  return run_matmul(out, nullptr, w, in_dim, out_dim, x_q, n_tok, workspace, workspace_bytes,
+                    Q8_0_KERNEL_AUTO, 0, stream);
+}
+
+int q8_0_matmul_debug(float *out, int32_t *blocksums, const void *w, int64_t in_dim,
+                      int64_t out_dim, const void *x_q, int64_t n_tok, void *workspace,
+                      size_t workspace_bytes, int32_t variant, int32_t split_k,
+                      hipStream_t stream) {
+  if (blocksums && !aligned(blocksums, 4)) return Q8_0_EALIGN;
+  return run_matmul(out, blocksums, w, in_dim, out_dim, x_q, n_tok, workspace, workspace_bytes,
+                    variant, split_k, stream);
+}
+
+int q8_0_matmul_plan(int64_t in_dim, int64_t out_dim, int64_t n_tok, size_t workspace_bytes,
+                     int32_t *variant, int32_t *split_k) {
+  if (in_dim < 0 || out_dim < 0 || n_tok < 0 || in_dim % Q8_0_BLOCK_ELEMS != 0)
+    return Q8_0_EINVAL;
+  Plan p = make_plan(in_dim, out_dim, n_tok, workspace_bytes, true);
+  if (variant) *variant = p.variant;
+  if (split_k) *split_k = p.split;
+  return Q8_0_OK;
+}
+
+size_t q8_0_moe_workspace_bytes(int64_t n_tok, int32_t n_used, int32_t n_expert) {
+  if (n_tok < 0 || n_used < 1 || n_expert < 1) return 0;
+  const q8::MoeLayout L = q8::moe_layout(n_tok, n_used, n_expert);
+  return (size_t)((L.total_ints * (int64_t)sizeof(int32_t) + 255) / 256 * 256);
+}
+
+int q8_0_moe_grouped(float *out, const void *const *expert_w, int32_t n_expert, int64_t in_dim,
+                     int64_t out_dim, const int32_t *selected, int32_t n_used, const void *x_q,
+                     int32_t x_rows, int64_t n_tok, void *workspace, size_t workspace_bytes,
+                     hipStream_t stream) {
+  return run_moe(out, nullptr, expert_w, n_expert, in_dim, out_dim, selected, n_used, x_q, x_rows,
+                 n_tok, workspace, workspace_bytes, stream);
+}
+
+int q8_0_moe_grouped_debug(float *out, int32_t *blocksums, const void *const *expert_w,
+                           int32_t n_expert, int64_t in_dim, int64_t out_dim,
+                           const int32_t *selected, int32_t n_used, const void *x_q,
+                           int32_t x_rows, int64_t n_tok, void *workspace, size_t workspace_bytes,
+                           hipStream_t stream) {
+  if (blocksums && !aligned(blocksums, 4)) return Q8_0_EALIGN;
+  return run_moe(out, blocksums, expert_w, n_expert, in_dim, out_dim, selected, n_used, x_q,
+                 x_rows, n_tok, workspace, workspace_bytes, stream);
+}
+
+const char *q8_0_strerror(int status) {
+  switch (status) {
+    case Q8_0_OK: return "ok";
+    case Q8_0_EINVAL: return "invalid argument (size, mode or null pointer)";
+    case Q8_0_EALIGN: return "pointer alignment too small";
+    case Q8_0_ELAUNCH: return "kernel launch failed";
+    case Q8_0_EWORKSPACE: return "workspace missing or too small";
+    case Q8_0_ENODEV: return "no gfx950 device current";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,55 @@
+// launch.h -- internal host-side launchers, one per kernel family.  Each
+// returns hipSuccess or the launch error; argument checks happen in api.cpp.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace q8 {
+
+// quantize.hip
+hipError_t launch_quantize(void *x_q, const float *x, int64_t n_tok, int64_t in_dim,
+                           bool fast, hipStream_t s);
+
+// matvec.hip: weight-streaming kernels for few tokens per weight row.
+struct MatvecShape {
+  int lanes_per_row;   // pairs handled by the lanes of one row (<= 64)
+  int waves_per_row;   // waves cooperating on one row (split over chunks)
+  int chunks_per_wave; // 64-pair chunks per wave (1 when lanes_per_row < 64)
+};
+bool matvec_shape(int64_t in_dim, MatvecShape *shape);
+hipError_t launch_matvec(float *out, int32_t *blocksums, const void *w, int64_t in_dim,
+                         int64_t out_dim, const void *x_q, int64_t n_tok, hipStream_t s);
+hipError_t launch_generic(float *out, int32_t *blocksums, const void *w, int64_t in_dim,
+                          int64_t out_dim, const void *x_q, int64_t n_tok, hipStream_t s);
+hipError_t launch_matvec_grouped(float *out, int32_t *blocksums, const void *const *expert_w,
+                                 int32_t n_expert, int64_t in_dim, int64_t out_dim,
+                                 const void *x_q, int32_t x_rows, int32_t n_used,
+                                 const int32_t *counts, const int32_t *offsets,
+                                 const int32_t *pairs, hipStream_t s);
+hipError_t launch_generic_grouped(float *out, int32_t *blocksums, const void *const *expert_w,
+                                  int32_t n_expert, int64_t in_dim, int64_t out_dim,
+                                  const int32_t *selected, int32_t n_used, const void *x_q,
+                                  int32_t x_rows, int64_t n_tok, hipStream_t s);
+
+// moe.hip
+struct MoeLayout {
+  int64_t counts, offsets, pairs;  // int32 element offsets inside the workspace
+  int64_t total_ints;
+};
+MoeLayout moe_layout(int64_t n_tok, int32_t n_used, int32_t n_expert);
+hipError_t launch_moe(float *out, int32_t *blocksums, const void *const *expert_w,
+                      int32_t n_expert, int64_t in_dim, int64_t out_dim,
+                      const int32_t *selected, int32_t n_used, const void *x_q,
+                      int32_t x_rows, int64_t n_tok, int32_t *workspace, bool fast,
+                      hipStream_t s);
+
+// gemm.hip: int8 MFMA GEMM with per-block scales.
+bool gemm_supported(int64_t in_dim);
+int gemm_auto_split(int64_t in_dim, int64_t out_dim, int64_t n_tok);
+size_t gemm_workspace_bytes(int64_t out_dim, int64_t n_tok, int split);
+hipError_t launch_gemm(float *out, int32_t *blocksums, const void *w, int64_t in_dim,
+                       int64_t out_dim, const void *x_q, int64_t n_tok, int split,
+                       float *partials, hipStream_t s);
+
+}  // namespace q8

@@ -1,0 +1,165 @@
+// moe.hip -- routing preparation for the grouped expert matmul.
+//
+// The pages' routed-MoE call takes, per token, the list of selected experts
+// ("Part 6: 代码走读", trace 5, ds4_gpu_routed_moe_one_tensor) and runs each
+// expert's projection for its tokens.  To stream every touched expert's
+// weights once, the (token, slot) pairs are regrouped expert-major on the GPU
+// with no host round trip:
+//   counts[e]   pairs routed to expert e
+//   offsets[e]  exclusive prefix sum of counts (offsets[n_expert] = valid pairs)
+//   pairs[...]  pair ids t*n_used + j, grouped by expert, ascending within an
+//               expert (a stable counting sort, so the order is deterministic)
+// Pairs whose id is outside [0, n_expert) are counted in workspace[0] and
+// their output rows are filled with NaN.
+//
+// One workgroup of 1024 lanes does it: LDS atomics count (integer, so the
+// result is order independent), a block scan builds offsets, and each 1024-pair
+// chunk is scattered with in-wave ranks from ballots (lanes sharing an expert
+// id are found bit by bit) and waves taking their turn in index order.
+#include "launch.h"
+#include "q8_device.h"
+
+namespace q8 {
+namespace {
+
+constexpr int kRouteThreads = 1024;
+constexpr int kRouteWaves = kRouteThreads / 64;
+constexpr int kHeaderInts = 16;
+
+__device__ __forceinline__ int32_t block_exclusive_scan(int32_t v, int32_t *tmp, int32_t *total) {
+  const int tid = threadIdx.x;
+  tmp[tid] = v;
+  __syncthreads();
+  for (int off = 1; off < kRouteThreads; off <<= 1) {
+    int32_t add = tid >= off ? tmp[tid - off] : 0;
+    __syncthreads();
+    tmp[tid] += add;
+    __syncthreads();
+  }
+  const int32_t incl = tmp[tid];
+  *total = tmp[kRouteThreads - 1];
+  __syncthreads();
+  return incl - v;
+}
+
+__global__ __launch_bounds__(kRouteThreads) void moe_route_kernel(
+    const int32_t *__restrict__ selected, int64_t n_pairs, int32_t n_expert, int32_t key_bits,
+    int32_t *__restrict__ ws, int64_t off_counts, int64_t off_offsets, int64_t off_pairs,
+    float *__restrict__ out, int64_t out_dim) {
+  extern __shared__ int32_t lds[];
+  int32_t *running = lds;                          // [n_expert]
+  int32_t *scan_tmp = lds + n_expert;              // [1024]
+  int32_t *slot_base = scan_tmp + kRouteThreads;   // [16][64]
+  __shared__ int32_t invalid;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+
+  for (int e = tid; e < n_expert; e += kRouteThreads) running[e] = 0;
+  if (tid == 0) invalid = 0;
+  __syncthreads();
+
+  for (int64_t i = tid; i < n_pairs; i += kRouteThreads) {
+    const int32_t e = selected[i];
+    if (e >= 0 && e < n_expert) atomicAdd(&running[e], 1);
+    else atomicAdd(&invalid, 1);
+  }
+  __syncthreads();
+
+  // counts and exclusive offsets; each lane owns a contiguous run of experts.
+  const int32_t per = (n_expert + kRouteThreads - 1) / kRouteThreads;
+  const int32_t e0 = tid * per;
+  const int32_t e1 = min(e0 + per, n_expert);
+  int32_t local = 0;
+  for (int32_t e = e0; e < e1; ++e) local += running[e];
+  int32_t total = 0;
+  int32_t base = block_exclusive_scan(local, scan_tmp, &total);
+  for (int32_t e = e0; e < e1; ++e) {
+    const int32_t c = running[e];
+    ws[off_counts + e] = c;
+    ws[off_offsets + e] = base;
+    running[e] = base;  // becomes the next free slot of expert e
+    base += c;
+  }
+  if (tid == 0) {
+    ws[off_offsets + n_expert] = total;
+    ws[0] = invalid;
+  }
+  __syncthreads();
+
+  // Stable scatter, 1024 pairs at a time, waves in index order.
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  for (int64_t chunk = 0; chunk < n_pairs; chunk += kRouteThreads) {
+    const int64_t i = chunk + tid;
+    int32_t e = i < n_pairs ? selected[i] : -1;
+    const bool valid = e >= 0 && e < n_expert;
+    const uint32_t key = valid ? (uint32_t)e : (uint32_t)n_expert;
+    uint64_t peers = __ballot(1);
+    for (int bit = 0; bit < key_bits; ++bit) {
+      const bool set = (key >> bit) & 1u;
+      const uint64_t b = __ballot(set);
+      peers &= set ? b : ~b;
+    }
+    const int rank = __popcll(peers & below);
+    const int leader = __ffsll((unsigned long long)peers) - 1;
+    for (int w = 0; w < kRouteWaves; ++w) {
+      if (wave == w && valid && rank == 0) {
+        slot_base[w * 64 + lane] = running[e];
+        running[e] += __popcll(peers);
+      }
+      __syncthreads();
+    }
+    if (valid) ws[off_pairs + slot_base[wave * 64 + leader] + rank] = (int32_t)i;
+    __syncthreads();
+  }
+
+  // Rows of pairs with an invalid expert id become NaN (error path only).
+  if (invalid > 0) {
+    for (int64_t i = 0; i < n_pairs; ++i) {
+      const int32_t e = selected[i];
+      if (e < 0 || e >= n_expert) {
+        for (int64_t o = tid; o < out_dim; o += kRouteThreads)
+          out[i * out_dim + o] = __builtin_nanf("");
+      }
+    }
+  }
+}
+
+}  // namespace
+
+MoeLayout moe_layout(int64_t n_tok, int32_t n_used, int32_t n_expert) {
+  MoeLayout L;
+  L.counts = kHeaderInts;
+  L.offsets = L.counts + n_expert;
+  L.pairs = L.offsets + n_expert + 1;
+  L.total_ints = L.pairs + n_tok * n_used;
+  return L;
+}
+
+size_t moe_route_lds_bytes(int32_t n_expert) {
+  return sizeof(int32_t) * ((size_t)n_expert + kRouteThreads + kRouteWaves * 64);
+}
+
+hipError_t launch_moe(float *out, int32_t *blocksums, const void *const *expert_w,
+                      int32_t n_expert, int64_t in_dim, int64_t out_dim,
+                      const int32_t *selected, int32_t n_used, const void *x_q, int32_t x_rows,
+                      int64_t n_tok, int32_t *ws, bool fast, hipStream_t s) {
+  const MoeLayout L = moe_layout(n_tok, n_used, n_expert);
+  const int64_t n_pairs = n_tok * n_used;
+  int key_bits = 1;
+  while ((1ll << key_bits) <= (int64_t)n_expert) ++key_bits;  // n_expert itself is the sentinel
+  hipLaunchKernelGGL(moe_route_kernel, dim3(1), dim3(kRouteThreads), moe_route_lds_bytes(n_expert),
+                     s, selected, n_pairs, n_expert, key_bits, ws, L.counts, L.offsets, L.pairs,
+                     out, out_dim);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  if (fast) {
+    return launch_matvec_grouped(out, blocksums, expert_w, n_expert, in_dim, out_dim, x_q, x_rows,
+                                 n_used, ws + L.counts, ws + L.offsets, ws + L.pairs, s);
+  }
+  return launch_generic_grouped(out, blocksums, expert_w, n_expert, in_dim, out_dim, selected,
+                                n_used, x_q, x_rows, n_tok, s);
+}
+
+}  // namespace q8

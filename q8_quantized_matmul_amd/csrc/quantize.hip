@@ -1,0 +1,136 @@
+// quantize.hip -- activation quantizer: fp32 rows -> Q8_0 blocks.
+//
+// Block rule (ds4-learning "Part 3: 模型架构", section 2, the row quantizer
+// listing, applied per 32 values with a binary16 scale):
+//   amax = max|x_i|, d32 = amax / 127, q_i = roundf(x_i / d32), d = fp16(d32).
+// Both divisions are IEEE fp32 (hipcc's default correctly rounded divide),
+// roundf rounds halves away from zero, the fp16 conversion rounds to nearest
+// even and keeps subnormals (gfx950 denormal mode is left at "preserve").
+// Zero blocks, non-finite blocks and scales that overflow binary16 follow the
+// conventions stated in q8_0.h.
+//
+// The kernel is bound by HBM traffic (4 bytes read and 1.0625 bytes written
+// per value); each lane owns two consecutive blocks so that its 68 output
+// bytes start on a dword boundary.
+#include "launch.h"
+#include "q8_device.h"
+
+namespace q8 {
+namespace {
+
+// Quantizes 32 values; returns the binary16 scale bits and the quants packed
+// little-endian into 8 dwords.
+__device__ __forceinline__ uint32_t quantize_block32(const float (&v)[32], uint32_t (&qd)[8]) {
+  bool finite = true;
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    finite = finite && __builtin_isfinite(v[i]);
+    float a = fabsf(v[i]);
+    amax = a > amax ? a : amax;
+  }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) qd[j] = 0;
+  if (!finite) return 0x7E00u;
+  if (!(amax > 0.0f)) return 0u;
+  const float d = amax / 127.0f;
+  if (!(d > 0.0f)) return 0u;  // d32 underflowed: zero block
+  const uint32_t h = __builtin_bit_cast(uint16_t, (_Float16)d);
+  if ((h & 0x7FFFu) == 0x7C00u) return 0x7E00u;  // scale does not fit binary16
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    float r = v[i] / d;
+    float qr = roundf(r);
+    qr = fminf(fmaxf(qr, -127.0f), 127.0f);
+    qd[i / 4] |= ((uint32_t)(int)qr & 0xFFu) << (8 * (i % 4));
+  }
+  return h;
+}
+
+// One lane per block pair.  Needs x 16-byte aligned, x_q 4-byte aligned and
+// an even number of blocks per row.
+__global__ __launch_bounds__(256) void quantize_pair_kernel(const float *__restrict__ x,
+                                                            uint8_t *__restrict__ xq,
+                                                            int64_t total_pairs,
+                                                            int64_t pairs_per_row,
+                                                            int64_t in_dim) {
+  const int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (g >= total_pairs) return;
+  const int64_t row = g / pairs_per_row;
+  const int64_t p = g - row * pairs_per_row;
+  const float4 *src = reinterpret_cast<const float4 *>(x + row * in_dim + p * 64);
+  float a[32], b[32];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    float4 t = src[i];
+    a[4 * i + 0] = t.x; a[4 * i + 1] = t.y; a[4 * i + 2] = t.z; a[4 * i + 3] = t.w;
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    float4 t = src[8 + i];
+    b[4 * i + 0] = t.x; b[4 * i + 1] = t.y; b[4 * i + 2] = t.z; b[4 * i + 3] = t.w;
+  }
+  uint32_t qa[8], qb[8];
+  const uint32_t ha = quantize_block32(a, qa);
+  const uint32_t hb = quantize_block32(b, qb);
+
+  uint32_t o[kPairDwords];
+  o[0] = ha | (qa[0] << 16);
+#pragma unroll
+  for (int j = 1; j < 8; ++j) o[j] = (qa[j - 1] >> 16) | (qa[j] << 16);
+  o[8] = (qa[7] >> 16) | (hb << 16);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) o[9 + j] = qb[j];
+
+  u32x4_a4 *dst = reinterpret_cast<u32x4_a4 *>(xq + g * kPairBytes);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    u32x4_a4 t = {o[4 * i], o[4 * i + 1], o[4 * i + 2], o[4 * i + 3]};
+    dst[i] = t;
+  }
+  reinterpret_cast<uint32_t *>(xq + g * kPairBytes)[16] = o[16];
+}
+
+// One lane per block; any block count, x_q only 2-byte aligned.
+__global__ __launch_bounds__(256) void quantize_block_kernel(const float *__restrict__ x,
+                                                             uint8_t *__restrict__ xq,
+                                                             int64_t total_blocks,
+                                                             int64_t blocks_per_row,
+                                                             int64_t in_dim) {
+  const int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (g >= total_blocks) return;
+  const int64_t row = g / blocks_per_row;
+  const int64_t b = g - row * blocks_per_row;
+  const float *src = x + row * in_dim + b * kBlockElems;
+  float v[32];
+#pragma unroll
+  for (int i = 0; i < 32; ++i) v[i] = src[i];
+  uint32_t qd[8];
+  const uint32_t h = quantize_block32(v, qd);
+  uint16_t *dst = reinterpret_cast<uint16_t *>(xq + g * kBlockBytes);
+  dst[0] = (uint16_t)h;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) dst[1 + j] = (uint16_t)(qd[j / 2] >> (16 * (j % 2)));
+}
+
+}  // namespace
+
+hipError_t launch_quantize(void *x_q, const float *x, int64_t n_tok, int64_t in_dim, bool fast,
+                           hipStream_t s) {
+  const int64_t nb = in_dim / kBlockElems;
+  if (fast) {
+    const int64_t ppr = nb / 2;
+    const int64_t total = n_tok * ppr;
+    const int64_t grid = (total + 255) / 256;
+    hipLaunchKernelGGL(quantize_pair_kernel, dim3((uint32_t)grid), dim3(256), 0, s, x,
+                       static_cast<uint8_t *>(x_q), total, ppr, in_dim);
+  } else {
+    const int64_t total = n_tok * nb;
+    const int64_t grid = (total + 255) / 256;
+    hipLaunchKernelGGL(quantize_block_kernel, dim3((uint32_t)grid), dim3(256), 0, s, x,
+                       static_cast<uint8_t *>(x_q), total, nb, in_dim);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace q8

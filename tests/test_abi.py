@@ -1,0 +1,135 @@
+"""CPU checks of the C ABI: the library loads, exports every function that
+include/q8_0.h declares, and its host-side argument checks and kernel plan
+behave as documented.  No compute call reaches a device here: every call
+either fails validation before any HIP call, or is host-only."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "q8_0.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(q8_0_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def q8():
+    import q8_quantized_matmul_amd as m
+    return m
+
+
+def test_exports_every_declared_symbol(q8):
+    lib = ctypes.CDLL(q8.LIB_PATH)
+    declared = _declared()
+    assert len(declared) == 9
+    for name in declared:
+        assert hasattr(lib, name), name
+    assert set(declared) == set(q8.EXPORTED)
+
+
+def test_strerror(q8):
+    assert q8.q8_0_strerror(0) == "ok"
+    for code in (-1, -2, -3, -4, -5):
+        assert q8.q8_0_strerror(code) != "unknown status"
+
+
+FAKE = 0x10000  # never dereferenced: every call below fails validation first
+
+
+def test_quantize_validation(q8):
+    lib = q8.raw_library()
+    assert lib.q8_0_quantize_act(FAKE, FAKE, 1, 33, None) == q8.Q8_0_EINVAL
+    assert lib.q8_0_quantize_act(FAKE, FAKE, -1, 32, None) == q8.Q8_0_EINVAL
+    assert lib.q8_0_quantize_act(None, FAKE, 1, 32, None) == q8.Q8_0_EINVAL
+    assert lib.q8_0_quantize_act(FAKE + 1, FAKE, 1, 32, None) == q8.Q8_0_EALIGN
+    assert lib.q8_0_quantize_act(FAKE, FAKE + 2, 1, 32, None) == q8.Q8_0_EALIGN
+    assert lib.q8_0_quantize_act(FAKE, FAKE, 0, 32, None) == q8.Q8_0_OK  # empty
+
+
+def test_matmul_validation(q8):
+    lib = q8.raw_library()
+    mm = lib.q8_0_matmul
+    assert mm(FAKE, FAKE, 48, 4, FAKE, 1, None, 0, None) == q8.Q8_0_EINVAL
+    assert mm(FAKE, FAKE, 0, 4, FAKE, 1, None, 0, None) == q8.Q8_0_EINVAL
+    assert mm(FAKE, None, 32, 4, FAKE, 1, None, 0, None) == q8.Q8_0_EINVAL
+    assert mm(FAKE + 2, FAKE, 32, 4, FAKE, 1, None, 0, None) == q8.Q8_0_EALIGN
+    assert mm(FAKE, FAKE + 1, 32, 4, FAKE, 1, None, 0, None) == q8.Q8_0_EALIGN
+    assert mm(FAKE, FAKE, 32, 0, FAKE, 1, None, 0, None) == q8.Q8_0_OK
+    assert mm(None, None, 32, 4, None, 0, None, 0, None) == q8.Q8_0_OK
+    dbg = lib.q8_0_matmul_debug
+    # forced matvec on a shape without whole block pairs
+    assert dbg(FAKE, None, FAKE, 96, 4, FAKE, 1, None, 0, 2, 0, None) == q8.Q8_0_EINVAL
+    # forced MFMA on 2-byte aligned operands
+    assert dbg(FAKE, None, FAKE + 2, 128, 4, FAKE, 32, None, 0, 3, 0, None) == q8.Q8_0_EINVAL
+    # forced split without workspace
+    assert dbg(FAKE, None, FAKE, 4096, 256, FAKE, 64, None, 0, 3, 4, None) == q8.Q8_0_EWORKSPACE
+    # split on a non-MFMA variant
+    assert dbg(FAKE, None, FAKE, 4096, 256, FAKE, 1, None, 0, 2, 2, None) == q8.Q8_0_EINVAL
+    assert dbg(FAKE, None, FAKE, 4096, 256, FAKE, 1, None, 0, 7, 0, None) == q8.Q8_0_EINVAL
+
+
+def test_moe_validation(q8):
+    lib = q8.raw_library()
+    mo = lib.q8_0_moe_grouped
+    need = q8.q8_0_moe_workspace_bytes(64, 8, 256)
+    assert need >= 4 * (16 + 2 * 256 + 1 + 512) and need % 256 == 0
+    args = dict(n_expert=256, in_dim=4096, out_dim=2048, n_used=8, x_rows=0, n_tok=64)
+
+    def call(**kw):
+        a = dict(args, **kw)
+        return mo(FAKE, FAKE, a["n_expert"], a["in_dim"], a["out_dim"], FAKE, a["n_used"], FAKE,
+                  a["x_rows"], a["n_tok"], kw.get("ws", FAKE), kw.get("ws_bytes", need), None)
+
+    assert call(n_expert=0) == q8.Q8_0_EINVAL
+    assert call(n_expert=100000) == q8.Q8_0_EINVAL
+    assert call(n_used=0) == q8.Q8_0_EINVAL
+    assert call(x_rows=2) == q8.Q8_0_EINVAL
+    assert call(in_dim=4100) == q8.Q8_0_EINVAL
+    assert call(ws_bytes=need - 4) == q8.Q8_0_EWORKSPACE
+    assert call(ws=None) == q8.Q8_0_EWORKSPACE
+    assert call(n_tok=0) == q8.Q8_0_OK
+
+
+def test_plan_regimes(q8):
+    # Decode shapes stream weights through the matvec kernel.
+    assert q8.q8_0_matmul_plan(1024, 32768, 1, 0) == (q8.KERNEL_MATVEC, 1)
+    assert q8.q8_0_matmul_plan(32768, 1024, 1, 0) == (q8.KERNEL_MATVEC, 1)
+    assert q8.q8_0_matmul_plan(4096, 2048, 15, 0) == (q8.KERNEL_MATVEC, 1)
+    # From 16 tokens on the matrix-core GEMM.
+    assert q8.q8_0_matmul_plan(4096, 2048, 16, 1 << 40)[0] == q8.KERNEL_MFMA
+    assert q8.q8_0_matmul_plan(4096, 2048, 4096, 1 << 40) == (q8.KERNEL_MFMA, 1)
+    v, s = q8.q8_0_matmul_plan(32768, 1024, 2048, 1 << 40)
+    assert v == q8.KERNEL_MFMA and s == 8
+    need = q8.q8_0_matmul_workspace_bytes(32768, 1024, 2048)
+    assert need == 8 * 1024 * 2048 * 4
+    # Without workspace the split falls back to 1; with some, to what fits.
+    assert q8.q8_0_matmul_plan(32768, 1024, 2048, 0) == (q8.KERNEL_MFMA, 1)
+    assert q8.q8_0_matmul_plan(32768, 1024, 2048, 3 * 1024 * 2048 * 4) == (q8.KERNEL_MFMA, 3)
+    # Block counts that are not whole pairs take the generic kernel.
+    assert q8.q8_0_matmul_plan(96, 64, 1, 0) == (q8.KERNEL_GENERIC, 1)
+    assert q8.q8_0_matmul_plan(96, 64, 100, 0) == (q8.KERNEL_GENERIC, 1)
+    assert q8.q8_0_matmul_workspace_bytes(1024, 32768, 1) == 0
+
+
+def test_valid_call_without_device_reports_nodev(q8):
+    import torch
+    if torch.cuda.device_count() > 0:
+        pytest.skip("a device is present")
+    lib = q8.raw_library()
+    assert lib.q8_0_matmul(FAKE, FAKE, 32, 4, FAKE, 1, None, 0, None) == q8.Q8_0_ENODEV
+    assert lib.q8_0_quantize_act(FAKE, FAKE, 1, 32, None) == q8.Q8_0_ENODEV
+
+
+def test_oracle_is_not_imported_by_the_product():
+    # The product path never loads the oracle.
+    for root, _, files in os.walk(os.path.join(ROOT, "q8_quantized_matmul_amd")):
+        for f in files:
+            if f.endswith((".py", ".hip", ".h", ".cpp")):
+                text = open(os.path.join(root, f), encoding="utf-8").read()
+                assert "oracle" not in text.replace("oracles", ""), f

@@ -1,0 +1,132 @@
+"""GPU parity for q8_0_moe_grouped (routing on the GPU + grouped expert matmul)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from tests.helpers import assert_close, cpu_u8, oracle_quantize, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _q8():
+    import q8_quantized_matmul_amd as q8
+    return q8
+
+
+def _small_case(in_dim, out_dim, n_expert, n_tok, n_used, seed, x_rows):
+    q8 = _q8()
+    ws_f = [workloads.normal((out_dim, in_dim), 0.02, "cuda", "moe_t", seed, e) for e in range(n_expert)]
+    wq = [q8.q8_0_quantize_act(w) for w in ws_f]
+    g = torch.Generator().manual_seed(seed)
+    sel = torch.stack([torch.randperm(n_expert, generator=g)[:n_used] for _ in range(n_tok)])
+    sel = sel.to(torch.int32)
+    rows = n_tok * n_used if x_rows else n_tok
+    x = workloads.normal((rows, in_dim), 1.0, "cuda", "moe_t", seed, "x")
+    xq = q8.q8_0_quantize_act(x)
+    torch.cuda.synchronize()
+    wq_o = [oracle_quantize(w) for w in ws_f]
+    xq_o = oracle_quantize(x)
+    for a, b in zip(wq, wq_o):
+        assert np.array_equal(cpu_u8(a), b)
+    assert np.array_equal(cpu_u8(xq), xq_o)
+    return wq, sel, xq, wq_o, xq_o
+
+
+@pytest.mark.parametrize("in_dim,out_dim,n_expert,n_tok,n_used,x_rows", [
+    (256, 96, 8, 5, 3, 0), (256, 96, 8, 5, 3, 1), (2048, 130, 16, 9, 4, 1),
+    (4096, 64, 32, 40, 8, 0), (96, 40, 5, 6, 2, 0), (1024, 70, 3, 33, 3, 1)])
+def test_moe_small(in_dim, out_dim, n_expert, n_tok, n_used, x_rows):
+    q8 = _q8()
+    wq, sel, xq, wq_o, xq_o = _small_case(in_dim, out_dim, n_expert, n_tok, n_used, in_dim + n_tok,
+                                          x_rows)
+    table = q8.expert_table(wq)
+    say(f"[moe] in={in_dim} out={out_dim} E={n_expert} T={n_tok} k={n_used} x_rows={x_rows}")
+    out = torch.full((n_tok, n_used, out_dim), float("nan"), device="cuda")
+    got, bs, ws = q8.q8_0_moe_grouped_debug(table, n_expert, sel.cuda(), xq, in_dim, out_dim,
+                                            x_rows, out=out)
+    torch.cuda.synchronize()
+    assert q8.moe_invalid_count(ws) == 0
+    ref, mag, bad = oracle.moe_grouped(wq_o, sel.numpy(), xq_o, in_dim, out_dim, x_rows)
+    assert bad == 0
+    assert_close(got.cpu().numpy(), ref, mag, "moe small")
+    # Block sums of each pair against the oracle's dense matmul of that pair.
+    bsn = bs.cpu().numpy().reshape(n_tok, n_used, out_dim, -1)
+    for t in range(n_tok):
+        for j in range(n_used):
+            row = t * n_used + j if x_rows else t
+            _, _, rbs = oracle.matmul(wq_o[int(sel[t, j])], xq_o[row:row + 1], in_dim,
+                                      want_blocksums=True)
+            assert np.array_equal(bsn[t, j], rbs[0])
+    # Deterministic.
+    got2, _ = q8.q8_0_moe_grouped(table, n_expert, sel.cuda(), xq, in_dim, out_dim, x_rows)
+    torch.cuda.synchronize()
+    assert torch.equal(got, got2)
+
+
+def test_moe_invalid_ids_and_duplicates():
+    q8 = _q8()
+    in_dim, out_dim, n_expert, n_tok, n_used = 512, 48, 6, 7, 3
+    wq, sel, xq, wq_o, xq_o = _small_case(in_dim, out_dim, n_expert, n_tok, n_used, 99, 0)
+    sel = sel.clone()
+    sel[1, 2] = 6          # out of range
+    sel[4, 0] = -3         # out of range
+    sel[5, 1] = sel[5, 0]  # duplicate id in one token's list
+    table = q8.expert_table(wq)
+    got, ws = q8.q8_0_moe_grouped(table, n_expert, sel.cuda(), xq, in_dim, out_dim, 0)
+    torch.cuda.synchronize()
+    assert q8.moe_invalid_count(ws) == 2
+    ref, mag, bad = oracle.moe_grouped(wq_o, sel.numpy(), xq_o, in_dim, out_dim, 0)
+    assert bad == 2
+    assert_close(got.cpu().numpy(), ref, mag, "moe invalid")
+
+
+def test_moe_workload_full_sampled():
+    """The benchmark's MoE workload at full size (256 experts x 3 matrices +
+    shared expert); the oracle checks 12 sampled (token, slot) pairs of every
+    projection in full, plus the shared expert on 8 tokens."""
+    q8 = _q8()
+    cfg = workloads.MOE
+    E, k, T, D, F = cfg["n_expert"], cfg["n_used"], cfg["n_tok"], cfg["d_model"], cfg["d_ff"]
+    sel = workloads.moe_routing()
+    x, mid = workloads.moe_acts("cuda")
+    xq = q8.q8_0_quantize_act(x)
+    midq = q8.q8_0_quantize_act(mid)
+    say("[moe] quantizing 256 experts x 3")
+    stacks = {}
+    for which, (rows, cols) in (("gate", (F, D)), ("up", (F, D)), ("down", (D, F))):
+        st = torch.empty((E, rows, q8.row_bytes(cols)), dtype=torch.uint8, device="cuda")
+        for e in range(E):
+            q8.q8_0_quantize_act(workloads.moe_expert(e, which, "cuda"), out=st[e])
+        stacks[which] = st
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(17)
+    pairs = sorted(rng.choice(T * k, 12, replace=False).tolist())
+    for which in ("gate", "up", "down"):
+        in_dim, out_dim = (D, F) if which != "down" else (F, D)
+        x_rows = 1 if which == "down" else 0
+        src = midq[: T * k] if x_rows else xq
+        say(f"[moe] full {which}")
+        got, ws = q8.q8_0_moe_grouped(q8.expert_table(stacks[which]), E, sel.cuda(), src, in_dim,
+                                      out_dim, x_rows)
+        torch.cuda.synchronize()
+        assert q8.moe_invalid_count(ws) == 0
+        g = got.cpu().numpy().reshape(T * k, out_dim)
+        src_f = mid[: T * k] if x_rows else x
+        for p in pairs:
+            t, j = divmod(p, k)
+            e = int(sel[t, j])
+            w_o = oracle_quantize(workloads.moe_expert(e, which, "cuda"))
+            assert np.array_equal(cpu_u8(stacks[which][e]), w_o)
+            xr = oracle_quantize(src_f[p if x_rows else t][None, :])
+            ref, mag, _ = oracle.matmul(w_o, xr, in_dim)
+            assert_close(g[p][None, :], ref, mag, f"moe {which} pair {p}")
+    # Shared expert: dense q8_0_matmul at n_tok = 64 (matrix-core path).
+    w_sh = workloads.moe_expert(-1, "gate", "cuda")
+    wq_sh = q8.q8_0_quantize_act(w_sh)
+    got = q8.q8_0_matmul(wq_sh, xq, D, F, T)
+    torch.cuda.synchronize()
+    toks = np.arange(0, T, 8)
+    ref, mag, _ = oracle.matmul(oracle_quantize(w_sh), oracle_quantize(x[torch.as_tensor(toks, device="cuda")]), D)
+    assert_close(got.cpu().numpy()[toks], ref, mag, "shared gate")
