@@ -43,39 +43,55 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-class Timer:
-    """Event pairs around selected launches on torch's current stream (the
-    stream every library call is enqueued on)."""
-
-    def __init__(self, torch):
-        self.torch = torch
-        self.pairs = {}
-
-    def around(self, name, fn):
-        ev0 = self.torch.cuda.Event(enable_timing=True)
-        ev1 = self.torch.cuda.Event(enable_timing=True)
-        ev0.record()
-        r = fn()
-        ev1.record()
-        self.pairs.setdefault(name, []).append((ev0, ev1))
-        return r
-
-    def mean_us(self, name):
-        p = self.pairs.get(name, [])
-        return 1000.0 * sum(a.elapsed_time(b) for a, b in p) / len(p) if p else None
-
-
-def timed_loop(torch, step, steps, warmup):
-    for i in range(warmup):
-        step(i, None)
+def capture(torch, fn, n):
+    """A HIP graph of fn(0), ..., fn(n-1), captured on torch's capture stream
+    (the library enqueues on torch's current stream, so its kernels land in
+    the graph).  Eager warm-up first, so no first-call work is captured."""
+    for i in range(n):
+        fn(i)
     torch.cuda.synchronize()
-    timer = Timer(torch)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(n):
+            fn(i)
+    torch.cuda.synchronize()
+    return g
+
+
+def time_steps(torch, fn, steps, warmup, per_graph=ROT):
+    """Whole-step throughput: `steps` steps as replays of a graph holding
+    `per_graph` consecutive steps, wall clock bracketed by synchronize."""
+    g = capture(torch, fn, per_graph)
+    reps = max(1, -(-steps // per_graph))
+    for _ in range(max(1, warmup // per_graph)):
+        g.replay()
+    torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(steps):
-        step(i, timer)
+    for _ in range(reps):
+        g.replay()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    return (t1 - t0) / steps, timer
+    return (t1 - t0) / (reps * per_graph), reps * per_graph
+
+
+def time_kernel(torch, fn, n_per_graph, reps=20):
+    """Mean duration of one launch: HIP events on the current stream around
+    replays of a graph of `n_per_graph` back-to-back launches of fn(i)."""
+    g = capture(torch, fn, n_per_graph)
+    for _ in range(3):
+        g.replay()
+    torch.cuda.synchronize()
+    evs = []
+    for _ in range(reps):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        g.replay()
+        e1.record()
+        evs.append((e0, e1))
+    torch.cuda.synchronize()
+    ms = sum(a.elapsed_time(b) for a, b in evs)
+    return 1000.0 * ms / (reps * n_per_graph)
 
 
 def bench_attn_q_b(torch, q8, wl, steps, warmup):
@@ -86,17 +102,17 @@ def bench_attn_q_b(torch, q8, wl, steps, warmup):
     xq = torch.empty((1, row_bytes(k)), dtype=torch.uint8, device="cuda")
     out = torch.empty((1, n), dtype=torch.float32, device="cuda")
 
-    def step(i, timer):
+    def step(i):
         q8.q8_0_quantize_act(x, out=xq)
-        call = lambda: q8.q8_0_matmul(ws[i % ROT], xq, k, n, 1, out=out)
-        timer.around("matvec", call) if timer else call()
+        q8.q8_0_matmul(ws[i % ROT], xq, k, n, 1, out=out)
 
-    sec, timer = timed_loop(torch, step, steps, warmup)
+    sec, done = time_steps(torch, step, steps, warmup)
+    kern_us = time_kernel(torch, lambda i: q8.q8_0_matmul(ws[i % ROT], xq, k, n, 1, out=out), ROT)
+    quant_us = time_kernel(torch, lambda i: q8.q8_0_quantize_act(x, out=xq), ROT)
     mm_bytes = n * row_bytes(k) + row_bytes(k) + 4 * n
     q_bytes = 4 * k + row_bytes(k)
-    kern_us = timer.mean_us("matvec")
-    return dict(sec=sec, step_bytes=mm_bytes + q_bytes, kernel_bytes=mm_bytes, kernel_us=kern_us,
-                plan=q8.q8_0_matmul_plan(k, n, 1, 0))
+    return dict(sec=sec, steps=done, step_bytes=mm_bytes + q_bytes, kernel_bytes=mm_bytes,
+                kernel_us=kern_us, quant_us=quant_us, plan=q8.q8_0_matmul_plan(k, n, 1, 0))
 
 
 def bench_decode5(torch, q8, wl, steps, warmup):
@@ -109,17 +125,20 @@ def bench_decode5(torch, q8, wl, steps, warmup):
     outs = [torch.empty((1, n), dtype=torch.float32, device="cuda") for _, n in dims]
     del sets
 
-    def step(i, timer):
+    def step(i):
         for j, (k, n) in enumerate(dims):
             q8.q8_0_quantize_act(xs[j], out=xqs[j])
-            call = lambda: q8.q8_0_matmul(wq[i % rot][j], xqs[j], k, n, 1, out=outs[j])
-            timer.around(f"mm{j}", call) if timer else call()
+            q8.q8_0_matmul(wq[i % rot][j], xqs[j], k, n, 1, out=outs[j])
 
-    sec, timer = timed_loop(torch, step, steps, warmup)
-    mm_bytes = sum(n * row_bytes(k) + row_bytes(k) + 4 * n for k, n in dims)
+    sec, done = time_steps(torch, step, steps, warmup, per_graph=rot)
+    per = []
+    for j, (k, n) in enumerate(dims):
+        us = time_kernel(torch, lambda i, j=j, k=k, n=n: q8.q8_0_matmul(wq[i % rot][j], xqs[j], k, n, 1,
+                                                                           out=outs[j]), rot)
+        per.append(dict(name=wl.DECODE5[j][0], kernel_us=us,
+                        kernel_bytes=n * row_bytes(k) + row_bytes(k) + 4 * n))
+    mm_bytes = sum(p["kernel_bytes"] for p in per)
     q_bytes = sum(4 * k + row_bytes(k) for k, _ in dims)
-    per = [dict(name=wl.DECODE5[j][0], kernel_us=timer.mean_us(f"mm{j}"),
-                kernel_bytes=n * row_bytes(k) + row_bytes(k) + 4 * n) for j, (k, n) in enumerate(dims)]
     return dict(sec=sec, step_bytes=mm_bytes + q_bytes, kernel_bytes=mm_bytes,
                 kernel_us=sum(p["kernel_us"] for p in per), per_matrix=per)
 
@@ -149,28 +168,38 @@ def bench_moe(torch, q8, wl, steps, warmup):
     wsd = q8.matmul_workspace(D, F, T)
     wsd2 = q8.matmul_workspace(F, D, T)
 
-    def step(i, timer):
-        tm = (lambda name, f: timer.around(name, f)) if timer else (lambda name, f: f())
-        q8.q8_0_quantize_act(x, out=xq)
-        tm("grouped", lambda: q8.q8_0_moe_grouped(tables["gate"], E, sel, xq, D, F, 0, out=o_g, workspace=wsm))
-        tm("grouped", lambda: q8.q8_0_moe_grouped(tables["up"], E, sel, xq, D, F, 0, out=o_u, workspace=wsm))
-        tm("shared", lambda: q8.q8_0_matmul(shared["gate"], xq, D, F, T, out=s_g, workspace=wsd))
-        tm("shared", lambda: q8.q8_0_matmul(shared["up"], xq, D, F, T, out=s_u, workspace=wsd))
-        q8.q8_0_quantize_act(mid, out=midq)
-        tm("grouped", lambda: q8.q8_0_moe_grouped(tables["down"], E, sel, midq[:T * kk], F, D, 1, out=o_d, workspace=wsm))
-        tm("shared", lambda: q8.q8_0_matmul(shared["down"], midq[T * kk:], F, D, T, out=s_d, workspace=wsd2))
+    gate = lambda i: q8.q8_0_moe_grouped(tables["gate"], E, sel, xq, D, F, 0, out=o_g, workspace=wsm)
+    down = lambda i: q8.q8_0_moe_grouped(tables["down"], E, sel, midq[:T * kk], F, D, 1, out=o_d,
+                                          workspace=wsm)
+    sh_gate = lambda i: q8.q8_0_matmul(shared["gate"], xq, D, F, T, out=s_g, workspace=wsd)
 
-    sec, timer = timed_loop(torch, step, steps, warmup)
+    def step(i):
+        q8.q8_0_quantize_act(x, out=xq)
+        gate(i)
+        q8.q8_0_moe_grouped(tables["up"], E, sel, xq, D, F, 0, out=o_u, workspace=wsm)
+        sh_gate(i)
+        q8.q8_0_matmul(shared["up"], xq, D, F, T, out=s_u, workspace=wsd)
+        q8.q8_0_quantize_act(mid, out=midq)
+        down(i)
+        q8.q8_0_matmul(shared["down"], midq[T * kk:], F, D, T, out=s_d, workspace=wsd2)
+
+    sec, done = time_steps(torch, step, steps, warmup, per_graph=1)
+    # One q8_0_moe_grouped call = routing kernel + grouped kernel; timed whole.
+    gate_us = time_kernel(torch, gate, 1, reps=10)
+    down_us = time_kernel(torch, down, 1, reps=10)
+    sh_us = time_kernel(torch, sh_gate, 1, reps=10)
     touched = int(torch.unique(sel).numel())
     mat = F * row_bytes(D)  # bytes of one expert matrix (gate/up/down are equal)
     pairs = T * kk
-    g_bytes = touched * 3 * mat + 2 * (pairs * F * 4 + T * row_bytes(D)) + pairs * (row_bytes(F) + D * 4)
+    gate_bytes = touched * mat + pairs * F * 4 + T * row_bytes(D)
+    down_bytes = touched * mat + pairs * (row_bytes(F) + D * 4)
+    g_bytes = 2 * gate_bytes + down_bytes
     s_bytes = 3 * mat + 2 * (T * F * 4 + T * row_bytes(D)) + T * (row_bytes(F) + D * 4)
     q_bytes = T * (4 * D + row_bytes(D)) + mid.shape[0] * (4 * F + row_bytes(F))
     ops = 2 * (pairs + T) * 3 * F * D
-    return dict(sec=sec, step_bytes=g_bytes + s_bytes + q_bytes, kernel_bytes=g_bytes / 3,
-                kernel_us=timer.mean_us("grouped"), shared_us=timer.mean_us("shared"),
-                touched_experts=touched, ops=ops)
+    return dict(sec=sec, step_bytes=g_bytes + s_bytes + q_bytes, gate_us=gate_us, down_us=down_us,
+                gate_bytes=gate_bytes, down_bytes=down_bytes, shared_us=sh_us,
+                shared_bytes=mat + T * F * 4 + T * row_bytes(D), touched_experts=touched, ops=ops)
 
 
 def bench_prefill(torch, q8, wl, name, steps, warmup):
@@ -182,15 +211,17 @@ def bench_prefill(torch, q8, wl, name, steps, warmup):
     xq = torch.empty((t, row_bytes(k)), dtype=torch.uint8, device="cuda")
     out = torch.empty((t, n), dtype=torch.float32, device="cuda")
     ws = q8.matmul_workspace(k, n, t)
+    quant = lambda i: q8.q8_0_quantize_act(x, out=xq)
+    gemm = lambda i: q8.q8_0_matmul(wq, xq, k, n, t, out=out, workspace=ws)
 
-    def step(i, timer):
-        tm = (lambda nm, f: timer.around(nm, f)) if timer else (lambda nm, f: f())
-        tm("quantize", lambda: q8.q8_0_quantize_act(x, out=xq))
-        tm("gemm", lambda: q8.q8_0_matmul(wq, xq, k, n, t, out=out, workspace=ws))
+    def step(i):
+        quant(i)
+        gemm(i)
 
-    sec, timer = timed_loop(torch, step, steps, warmup)
+    sec, done = time_steps(torch, step, steps, warmup, per_graph=1)
     ops = 2 * t * n * k
-    return dict(sec=sec, ops=ops, kernel_us=timer.mean_us("gemm"), quant_us=timer.mean_us("quantize"),
+    return dict(sec=sec, ops=ops, kernel_us=time_kernel(torch, gemm, 4, reps=5),
+                quant_us=time_kernel(torch, quant, 4, reps=5),
                 quant_bytes=t * (4 * k + row_bytes(k)),
                 kernel_bytes=n * row_bytes(k) + t * row_bytes(k) + 4 * t * n,
                 plan=q8.q8_0_matmul_plan(k, n, t, ws.numel()))
@@ -253,7 +284,7 @@ def main():
     ach = h["kernel_bytes"] / (h["kernel_us"] * 1e-6) / 1e9
     result = {
         "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(h["sec"] * 1e3, 5),
+        "steps": h["steps"], "warmup": args.warmup, "ms_per_step": round(h["sec"] * 1e3, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "int8",
         "data": "synthetic",
         "config": {"workload": "attn_q_b decode matvec: Q8_0 W[32768x1024] x Q8_0 x[1x1024] "
@@ -262,12 +293,13 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None,
                      "kernel": "matvec_kernel<16,1,1,RG>", "kernel_us": round(h["kernel_us"], 3),
-                     "bytes_per_launch": h["kernel_bytes"]},
+                     "bytes_per_launch": h["kernel_bytes"],
+                     "quantize_us": round(h["quant_us"], 3)},
     }
     secondary = []
     if not args.quick:
         log("[bench] decode5")
-        d5 = bench_decode5(torch, q8, wl, max(args.steps // 2, 10), args.warmup)
+        d5 = bench_decode5(torch, q8, wl, max(args.steps // 2, 16), args.warmup)
         secondary.append({
             "workload": "decode5 (5 projections back to back, n_tok 1)",
             "value": round(d5["step_bytes"] / d5["sec"] / 1e9, 2), "unit": "GB/s",
@@ -279,17 +311,20 @@ def main():
                            for p in d5["per_matrix"]]})
         log("[bench] moe")
         mo = bench_moe(torch, q8, wl, max(args.steps // 50, 5), 3)
+        gate_gbs = mo["gate_bytes"] / (mo["gate_us"] * 1e-6) / 1e9
         secondary.append({
             "workload": "moe (64 tokens x 8 of 256 experts + shared, gate/up/down)",
             "value": round(mo["step_bytes"] / mo["sec"] / 1e9, 2), "unit": "GB/s",
             "ms_per_step": round(mo["sec"] * 1e3, 4), "touched_experts": mo["touched_experts"],
-            "grouped_kernel_us": round(mo["kernel_us"], 2),
-            "grouped_GBs": round(mo["kernel_bytes"] / (mo["kernel_us"] * 1e-6) / 1e9, 1),
-            "frac_hbm_grouped": round(mo["kernel_bytes"] / (mo["kernel_us"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
-            "shared_kernel_us": round(mo["shared_us"], 2)})
+            "grouped_gate_us": round(mo["gate_us"], 2), "grouped_gate_GBs": round(gate_gbs, 1),
+            "frac_hbm_grouped_gate": round(gate_gbs / HBM_PEAK_GBS, 4),
+            "grouped_down_us": round(mo["down_us"], 2),
+            "grouped_down_GBs": round(mo["down_bytes"] / (mo["down_us"] * 1e-6) / 1e9, 1),
+            "shared_gate_us": round(mo["shared_us"], 2),
+            "shared_gate_GBs": round(mo["shared_bytes"] / (mo["shared_us"] * 1e-6) / 1e9, 1)})
         for name in ("prefill_a", "prefill_b"):
             log(f"[bench] {name}")
-            pf = bench_prefill(torch, q8, wl, name, max(args.steps // 40, 10), 5)
+            pf = bench_prefill(torch, q8, wl, name, max(args.steps // 40, 10), 3)
             tops = pf["ops"] / (pf["kernel_us"] * 1e-6) / 1e12
             secondary.append({
                 "workload": name, "value": round(pf["ops"] / pf["sec"] / 1e12, 2), "unit": "TOPS",

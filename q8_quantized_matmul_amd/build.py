@@ -17,7 +17,7 @@ SOURCES = ["api.hip", "quantize.hip", "matvec.hip", "moe.hip", "gemm.hip"]
 # -packed-fp32-ops: keep the compiler from emitting packed fp32 VALU forms.
 # No fast-math: the quantizer relies on IEEE division and roundf.
 HIPCC_FLAGS = [
-    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared", "-Wall",
+    "--offload-arch=gfx950", "-O3", "-std=c++20", "-fPIC", "-shared", "-Wall",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
 ]
 

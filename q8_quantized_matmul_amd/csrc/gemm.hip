@@ -27,6 +27,8 @@
 //     MFMAs (register prefetch).
 //   * Split-K over grid.z writes fp32 partials to caller workspace; a second
 //     kernel sums them in split order (deterministic, no atomics).
+#include <utility>
+
 #include "launch.h"
 #include "q8_device.h"
 
@@ -43,7 +45,34 @@ struct GemmArgs {
   int64_t nb;
   int64_t row_bytes;
   int64_t blocks_per_split;
+  int32_t tiles_o;   // output-row tiles
+  int32_t tiles_t;   // token tiles
+  int32_t n_split;
 };
+
+// Workgroups are dealt round-robin to the 8 XCDs, each with its own L2.  The
+// linear workgroup id is renumbered so that each XCD receives a contiguous run
+// of tiles, and runs are laid out as bands of kGroupO output-row tiles by all
+// token tiles, split-major: the workgroups sharing an XCD then share weight
+// and activation panels in its L2.
+constexpr int kXcds = 8;
+constexpr int kGroupO = 8;
+
+__device__ __forceinline__ void tile_of(const GemmArgs &a, int &to, int &tt, int &ts) {
+  const int n = a.tiles_o * a.tiles_t * a.n_split;
+  const int lin = blockIdx.x;
+  int l = lin;
+  if (n % kXcds == 0) l = (lin % kXcds) * (n / kXcds) + lin / kXcds;
+  const int per_split = a.tiles_o * a.tiles_t;
+  ts = l / per_split;
+  const int r = l - ts * per_split;
+  const int band = r / (kGroupO * a.tiles_t);
+  const int o0 = band * kGroupO;
+  const int width = min(kGroupO, a.tiles_o - o0);
+  const int w = r - band * kGroupO * a.tiles_t;
+  to = o0 + w % width;
+  tt = w / width;
+}
 
 template <int TI, int TJ, int KB, bool STORE_S>
 __global__ __launch_bounds__(256, 2) void gemm_kernel(const GemmArgs a) {
@@ -54,7 +83,9 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(const GemmArgs a) {
   constexpr int NPAIR_W = BO * PPR;
   constexpr int NPAIR = NPAIR_W + BT * PPR;
   constexpr int PPT = (NPAIR + 255) / 256;
+  constexpr int NT = TI * TJ;         // MFMA tiles per wave
   static_assert(KB % 2 == 0, "stage must hold whole block pairs");
+  constexpr bool FULL = NPAIR % 256 == 0;  // every lane loads PPT pairs
 
   __shared__ __attribute__((aligned(16))) uint8_t qsW[BO * ROWB];
   __shared__ __attribute__((aligned(16))) uint8_t qsX[BT * ROWB];
@@ -64,12 +95,37 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(const GemmArgs a) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int64_t o_tile = (int64_t)blockIdx.x * BO;
-  const int64_t t_tile = (int64_t)blockIdx.y * BT;
-  const int64_t b_begin = (int64_t)blockIdx.z * a.blocks_per_split;
+  int to, tt, ts;
+  tile_of(a, to, tt, ts);
+  const int64_t o_tile = (int64_t)to * BO;
+  const int64_t t_tile = (int64_t)tt * BT;
+  const int64_t b_begin = (int64_t)ts * a.blocks_per_split;
   const int64_t b_end = min(b_begin + a.blocks_per_split, a.nb);
   const int o_w = (wave & 1) * 32 * TI;   // wave's first row inside the tile
   const int t_w = (wave >> 1) * 32 * TJ;  // wave's first token inside the tile
+
+  // Load descriptors: each lane fetches PPT block pairs per stage.  Rows past
+  // the matrix are clamped to its last row (their outputs are never stored);
+  // pairs past the K range re-read the last valid pair with zeroed scales.
+  const uint8_t *src[PPT];
+  uint8_t *dst_qs[PPT];
+  uint16_t *dst_sc[PPT];
+  int sc_ld[PPT];
+  int blk_off[PPT];  // first block of the lane's pair inside a stage
+#pragma unroll
+  for (int p = 0; p < PPT; ++p) {
+    const int j = min(tid + 256 * p, NPAIR - 1);
+    const bool isw = j < NPAIR_W;
+    const int jj = isw ? j : j - NPAIR_W;
+    const int row = jj / PPR;
+    const int pr = jj % PPR;
+    const int64_t grow = min((isw ? o_tile : t_tile) + row, (isw ? a.out_dim : a.n_tok) - 1);
+    src[p] = (isw ? a.w : a.x_q) + grow * a.row_bytes;
+    dst_qs[p] = (isw ? qsW : qsX) + row * ROWB + pr * 64;
+    dst_sc[p] = (isw ? &scW[2 * pr][row] : &scX[2 * pr][row]);
+    sc_ld[p] = isw ? BO : BT;
+    blk_off[p] = 2 * pr;
+  }
 
   f32x16 acc[TI][TJ];
 #pragma unroll
@@ -80,62 +136,41 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(const GemmArgs a) {
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
   uint32_t pre[PPT][kPairDwords];
-
   auto gload = [&](int64_t b0) {
 #pragma unroll
     for (int p = 0; p < PPT; ++p) {
-      const int j = tid + 256 * p;
-      if (j < NPAIR) {
-        const bool isw = j < NPAIR_W;
-        const int jj = isw ? j : j - NPAIR_W;
-        const int row = jj / PPR;
-        const int pr = jj % PPR;
-        const int64_t grow = (isw ? o_tile : t_tile) + row;
-        const int64_t lim = isw ? a.out_dim : a.n_tok;
-        const int64_t blk = b0 + 2 * pr;
-        if (grow < lim && blk < b_end) {
-          load_pair((isw ? a.w : a.x_q) + grow * a.row_bytes + blk * kBlockBytes, pre[p]);
-        } else {
-#pragma unroll
-          for (int i = 0; i < kPairDwords; ++i) pre[p][i] = 0;
-        }
+      if (!FULL && tid + 256 * p >= NPAIR) continue;
+      const int64_t blk = b0 + blk_off[p];
+      const bool kvalid = blk < b_end;
+      load_pair(src[p] + (kvalid ? blk : b_end - 2) * kBlockBytes, pre[p]);
+      if (!kvalid) {
+        pre[p][0] &= 0xFFFF0000u;  // scale of the pair's first block
+        pre[p][8] &= 0x0000FFFFu;  // scale of the pair's second block
       }
     }
   };
-
   auto lstore = [&]() {
 #pragma unroll
     for (int p = 0; p < PPT; ++p) {
-      const int j = tid + 256 * p;
-      if (j < NPAIR) {
-        const bool isw = j < NPAIR_W;
-        const int jj = isw ? j : j - NPAIR_W;
-        const int row = jj / PPR;
-        const int pr = jj % PPR;
-        uint8_t *qs = (isw ? qsW : qsX) + row * ROWB + pr * 64;
-        const uint32_t *d = pre[p];
-        i32x4 a0 = {(int)__builtin_amdgcn_alignbyte(d[1], d[0], 2),
-                    (int)__builtin_amdgcn_alignbyte(d[2], d[1], 2),
-                    (int)__builtin_amdgcn_alignbyte(d[3], d[2], 2),
-                    (int)__builtin_amdgcn_alignbyte(d[4], d[3], 2)};
-        i32x4 a1 = {(int)__builtin_amdgcn_alignbyte(d[5], d[4], 2),
-                    (int)__builtin_amdgcn_alignbyte(d[6], d[5], 2),
-                    (int)__builtin_amdgcn_alignbyte(d[7], d[6], 2),
-                    (int)__builtin_amdgcn_alignbyte(d[8], d[7], 2)};
-        i32x4 b0 = {(int)d[9], (int)d[10], (int)d[11], (int)d[12]};
-        i32x4 b1 = {(int)d[13], (int)d[14], (int)d[15], (int)d[16]};
-        reinterpret_cast<i32x4 *>(qs)[0] = a0;
-        reinterpret_cast<i32x4 *>(qs)[1] = a1;
-        reinterpret_cast<i32x4 *>(qs)[2] = b0;
-        reinterpret_cast<i32x4 *>(qs)[3] = b1;
-        if (isw) {
-          scW[2 * pr][row] = (uint16_t)(d[0] & 0xFFFFu);
-          scW[2 * pr + 1][row] = (uint16_t)(d[8] >> 16);
-        } else {
-          scX[2 * pr][row] = (uint16_t)(d[0] & 0xFFFFu);
-          scX[2 * pr + 1][row] = (uint16_t)(d[8] >> 16);
-        }
-      }
+      if (!FULL && tid + 256 * p >= NPAIR) continue;
+      const uint32_t *d = pre[p];
+      i32x4 a0 = {(int)__builtin_amdgcn_alignbyte(d[1], d[0], 2),
+                  (int)__builtin_amdgcn_alignbyte(d[2], d[1], 2),
+                  (int)__builtin_amdgcn_alignbyte(d[3], d[2], 2),
+                  (int)__builtin_amdgcn_alignbyte(d[4], d[3], 2)};
+      i32x4 a1 = {(int)__builtin_amdgcn_alignbyte(d[5], d[4], 2),
+                  (int)__builtin_amdgcn_alignbyte(d[6], d[5], 2),
+                  (int)__builtin_amdgcn_alignbyte(d[7], d[6], 2),
+                  (int)__builtin_amdgcn_alignbyte(d[8], d[7], 2)};
+      i32x4 b0 = {(int)d[9], (int)d[10], (int)d[11], (int)d[12]};
+      i32x4 b1 = {(int)d[13], (int)d[14], (int)d[15], (int)d[16]};
+      i32x4 *q = reinterpret_cast<i32x4 *>(dst_qs[p]);
+      q[0] = a0;
+      q[1] = a1;
+      q[2] = b0;
+      q[3] = b1;
+      dst_sc[p][0] = (uint16_t)(d[0] & 0xFFFFu);
+      dst_sc[p][sc_ld[p]] = (uint16_t)(d[8] >> 16);
     }
   };
 
@@ -144,57 +179,57 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(const GemmArgs a) {
   const i32x16 izero = {};
   const f32x16 fzero = {};
 
+  // Scale tile of a block: every lane feeds the binary16 scale of its row
+  // (column) into K-slot 0 of its half, so the f16 MFMA returns
+  // 2 * d_w[o] * d_x[t] exactly; the final store multiplies by 0.5.
+  auto tile_mfma = [&](int kb, int t, i32x16 &S, f32x16 &C) {
+    const int i = t / TJ, j = t % TJ;
+    const int ro = o_w + 32 * i + lrow;
+    const int rt = t_w + 32 * j + lrow;
+    const i32x4 A = *reinterpret_cast<const i32x4 *>(qsW + ro * ROWB + kb * 32 + khalf);
+    const i32x4 B = *reinterpret_cast<const i32x4 *>(qsX + rt * ROWB + kb * 32 + khalf);
+    const f16x4 SA = {__builtin_bit_cast(_Float16, scW[kb][ro]), (_Float16)0, (_Float16)0, (_Float16)0};
+    const f16x4 SB = {__builtin_bit_cast(_Float16, scX[kb][rt]), (_Float16)0, (_Float16)0, (_Float16)0};
+    S = __builtin_amdgcn_mfma_i32_32x32x32_i8(A, B, izero, 0, 0, 0);
+    C = __builtin_amdgcn_mfma_f32_32x32x8f16(SA, SB, fzero, 0, 0, 0);
+  };
+
   gload(b_begin);
   for (int64_t b0 = b_begin; b0 < b_end; b0 += KB) {
     __syncthreads();
     lstore();
     __syncthreads();
-    if (b0 + KB < b_end) gload(b0 + KB);
+    gload(b0 + KB);  // past the end: clamped, in-bounds, unused
+    // Software pipeline over (block, tile): the MFMAs of the next tile are
+    // issued before the int->float + fma epilogue of the current one.  Blocks
+    // past the K range carry zero scales, so every stage runs all KB blocks.
+    i32x16 S[2];
+    f32x16 C[2];
+    tile_mfma(0, 0, S[0], C[0]);
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-      if (b0 + kb < b_end) {
-        i32x4 A[TI], B[TJ];
-        f16x4 SA[TI], SB[TJ];
+    for (int step = 0; step < KB * NT; ++step) {
+      const int kb = step / NT, t = step % NT;
+      if (step + 1 < KB * NT) tile_mfma((step + 1) / NT, (step + 1) % NT, S[(step + 1) & 1], C[(step + 1) & 1]);
+      const int i = t / TJ, j = t % TJ;
 #pragma unroll
-        for (int i = 0; i < TI; ++i) {
-          const int r = o_w + 32 * i + lrow;
-          A[i] = *reinterpret_cast<const i32x4 *>(qsW + r * ROWB + kb * 32 + khalf);
-          const uint16_t s = lane < 32 ? scW[kb][r] : (uint16_t)0;
-          SA[i] = f16x4{__builtin_bit_cast(_Float16, s), (_Float16)0, (_Float16)0, (_Float16)0};
-        }
+      for (int r = 0; r < 16; ++r)
+        acc[i][j][r] = fmaf((float)S[step & 1][r], C[step & 1][r], acc[i][j][r]);
+      if constexpr (STORE_S) {
+        const int64_t tt = t_tile + t_w + 32 * j + lrow;
 #pragma unroll
-        for (int j = 0; j < TJ; ++j) {
-          const int r = t_w + 32 * j + lrow;
-          B[j] = *reinterpret_cast<const i32x4 *>(qsX + r * ROWB + kb * 32 + khalf);
-          const uint16_t s = lane < 32 ? scX[kb][r] : (uint16_t)0;
-          SB[j] = f16x4{__builtin_bit_cast(_Float16, s), (_Float16)0, (_Float16)0, (_Float16)0};
-        }
-#pragma unroll
-        for (int i = 0; i < TI; ++i) {
-#pragma unroll
-          for (int j = 0; j < TJ; ++j) {
-            const i32x16 S = __builtin_amdgcn_mfma_i32_32x32x32_i8(A[i], B[j], izero, 0, 0, 0);
-            const f32x16 C = __builtin_amdgcn_mfma_f32_32x32x8f16(SA[i], SB[j], fzero, 0, 0, 0);
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[i][j][r] = fmaf((float)S[r], C[r], acc[i][j][r]);
-            if constexpr (STORE_S) {
-              const int64_t t = t_tile + t_w + 32 * j + lrow;
-#pragma unroll
-              for (int r = 0; r < 16; ++r) {
-                const int64_t o = o_tile + o_w + 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-                if (t < a.n_tok && o < a.out_dim)
-                  a.blocksums[(t * a.out_dim + o) * a.nb + b0 + kb] = S[r];
-              }
-            }
-          }
+        for (int r = 0; r < 16; ++r) {
+          const int64_t o = o_tile + o_w + 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+          if (tt < a.n_tok && o < a.out_dim && b0 + kb < b_end)
+            a.blocksums[(tt * a.out_dim + o) * a.nb + b0 + kb] = S[step & 1][r];
         }
       }
     }
   }
 
   // Accumulator layout of a 32x32 MFMA tile: lane l holds column l%32 and
-  // rows 8*(r/4) + 4*(l/32) + r%4 for r = 0..15.
-  float *dst = a.out + (int64_t)blockIdx.z * a.n_tok * a.out_dim;
+  // rows 8*(r/4) + 4*(l/32) + r%4 for r = 0..15.  The 0.5 undoes the doubled
+  // scale tile (exact).
+  float *dst = a.out + (int64_t)ts * a.n_tok * a.out_dim;
 #pragma unroll
   for (int i = 0; i < TI; ++i) {
 #pragma unroll
@@ -204,8 +239,189 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(const GemmArgs a) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int64_t o = o_tile + o_w + 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-          if (o < a.out_dim) dst[t * a.out_dim + o] = acc[i][j][r];
+          if (o < a.out_dim) dst[t * a.out_dim + o] = 0.5f * acc[i][j][r];
         }
+      }
+    }
+  }
+}
+
+// ---- Direct-to-LDS variant (in_dim % 256 == 0, n_tok > 64) -------------
+// A stage is 8 blocks = 272 bytes of every row = 17 aligned 16-byte chunks.
+// global_load_lds_dwordx4 copies 64 consecutive chunks per wave instruction
+// straight into LDS (no VGPR staging, no repack), rows kept contiguous, so
+// each instruction reads ~1 KB of contiguous rows.  Two stages ring in LDS:
+// the copies of stage s+1 are in flight while stage s is multiplied, with one
+// barrier per stage.  An MFMA operand (16 quant bytes at 34*kb + 2 + 16*h in
+// the row) spans at most two chunks: two aligned ds_read_b128 and, for even
+// blocks, four v_alignbyte realign it.  Workgroup = 8 waves on a 128x128
+// tile, each wave 32 output rows x 64 tokens (two 32x32 MFMA tiles).
+namespace lds {
+constexpr int BO = 128;
+constexpr int BT = 128;
+constexpr int ROWS = BO + BT;
+constexpr int KB = 8;
+constexpr int RB = KB * kBlockBytes;    // 272
+constexpr int CPR = RB / 16;            // 17
+constexpr int REGION_W = BO * RB;       // weight rows first, then token rows
+constexpr int STAGE = ROWS * RB;        // 69632 bytes
+constexpr int INSTS = ROWS * CPR / 64;  // 68 wave loads per stage
+constexpr int WAVES = 8;
+constexpr int LPW = (INSTS + WAVES - 1) / WAVES;
+static_assert(ROWS * CPR % 64 == 0 && (BO * CPR) % 64 == 0, "whole wave loads per region");
+}  // namespace lds
+
+// 16 quant bytes of block KBI for half h, from a 16-byte-aligned row segment,
+// plus the block's binary16 scale bits for the lanes of half 0 (zero for half
+// 1).  The scale sits two bytes before the quants, so for every block but the
+// last of a stage it lies in the chunk already read for the operand.
+template <int KBI>
+__device__ __forceinline__ i32x4 fetch_operand(const uint8_t *row, int h, uint32_t &scale) {
+  constexpr int O = KBI * kBlockBytes + 2;  // quant offset for h = 0
+  constexpr int M = O % 16;
+  const uint8_t *p = row + (O - M) + 16 * h;
+  const i32x4 c0 = *reinterpret_cast<const i32x4 *>(p);
+  const uint32_t d0[4] = {(uint32_t)c0.x, (uint32_t)c0.y, (uint32_t)c0.z, (uint32_t)c0.w};
+  if constexpr (M >= 2) {
+    constexpr int SB = M - 2;  // byte of the scale inside the chunk (even)
+    scale = h ? 0u : (d0[SB / 4] >> (8 * (SB % 4))) & 0xFFFFu;
+  } else {
+    const uint16_t sv = *reinterpret_cast<const uint16_t *>(row + KBI * kBlockBytes);
+    scale = h ? 0u : (uint32_t)sv;
+  }
+  if constexpr (M == 0) {
+    return c0;
+  } else {
+    const i32x4 c1 = *reinterpret_cast<const i32x4 *>(p + 16);
+    const uint32_t d[8] = {d0[0], d0[1], d0[2], d0[3],
+                           (uint32_t)c1.x, (uint32_t)c1.y, (uint32_t)c1.z, (uint32_t)c1.w};
+    constexpr int K = M / 4;
+    if constexpr (M % 4 == 0) {
+      return i32x4{(int)d[K], (int)d[K + 1], (int)d[K + 2], (int)d[K + 3]};
+    } else {
+      return i32x4{(int)__builtin_amdgcn_alignbyte(d[K + 1], d[K], 2),
+                   (int)__builtin_amdgcn_alignbyte(d[K + 2], d[K + 1], 2),
+                   (int)__builtin_amdgcn_alignbyte(d[K + 3], d[K + 2], 2),
+                   (int)__builtin_amdgcn_alignbyte(d[K + 4], d[K + 3], 2)};
+    }
+  }
+}
+
+template <bool STORE_S>
+__global__ __launch_bounds__(512, 1) void gemm_lds_kernel(const GemmArgs a) {
+  using namespace lds;
+  __shared__ __attribute__((aligned(16))) uint8_t ring[2 * STAGE];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  int to, tt, ts;
+  tile_of(a, to, tt, ts);
+  const int64_t o_tile = (int64_t)to * BO;
+  const int64_t t_tile = (int64_t)tt * BT;
+  const int64_t b_begin = (int64_t)ts * a.blocks_per_split;
+  const int64_t b_end = min(b_begin + a.blocks_per_split, a.nb);
+  const int nstages = (int)((b_end - b_begin) / KB);  // splits are whole stages
+
+  // Copy descriptors: wave load i moves chunks [64*local, 64*local + 64) of the
+  // weight (local < 34) or token region.  Rows past the matrix are clamped to
+  // its last row; their outputs are never stored.
+  const uint8_t *src[LPW];
+  uint32_t dst[LPW];
+#pragma unroll
+  for (int i = 0; i < LPW; ++i) {
+    const int inst = min(wave + WAVES * i, INSTS - 1);
+    const bool isw = inst < INSTS / 2;
+    const int local = isw ? inst : inst - INSTS / 2;
+    const int c = local * 64 + lane;
+    const int row = c / CPR;
+    const int part = c - row * CPR;
+    const int64_t grow = min((isw ? o_tile : t_tile) + row, (isw ? a.out_dim : a.n_tok) - 1);
+    src[i] = (isw ? a.w : a.x_q) + grow * a.row_bytes + part * 16;
+    dst[i] = (isw ? 0u : (uint32_t)REGION_W) + (uint32_t)local * 1024u;
+  }
+  auto issue = [&](int64_t b0, int buf) {
+#pragma unroll
+    for (int i = 0; i < LPW; ++i) {
+      if (wave + WAVES * i < INSTS)  // uniform per wave
+        __builtin_amdgcn_global_load_lds(src[i] + b0 * kBlockBytes, ring + buf * STAGE + dst[i], 16, 0, 0);
+    }
+  };
+
+  const int wo = wave & 3;   // 32 output rows each
+  const int wt = wave >> 2;  // 64 tokens each
+  const int lrow = lane & 31;
+  const int h = lane >> 5;
+  const i32x16 izero = {};
+  const f32x16 fzero = {};
+  f32x16 acc[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[j][r] = 0.0f;
+
+  issue(b_begin, 0);
+  for (int s = 0; s < nstages; ++s) {
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's copies of stage s have landed
+    __syncthreads();                // ... and every wave's; buffer (s+1)&1 is free
+    if (s + 1 < nstages) issue(b_begin + (int64_t)(s + 1) * KB, (s + 1) & 1);
+    const uint8_t *st = ring + (s & 1) * STAGE;
+    const uint8_t *arow = st + (32 * wo + lrow) * RB;
+    const uint8_t *brow0 = st + REGION_W + (64 * wt + lrow) * RB;
+    const uint8_t *brow1 = brow0 + 32 * RB;
+
+    i32x16 S[2];
+    f32x16 C[2];
+    // Scale tile: lanes of half 0 feed their row's (column's) binary16 scale
+    // into K-slot 0 and half 1 feeds zeros, so the f16 MFMA gives d_w * d_x
+    // exactly in the accumulator layout of the int8 tile.
+    auto issue_tile = [&](auto kbc, int j, i32x16 &Sd, f32x16 &Cd) {
+      constexpr int KBI = decltype(kbc)::value;
+      const uint8_t *brow = j ? brow1 : brow0;
+      uint32_t sa, sb;
+      const i32x4 A = fetch_operand<KBI>(arow, h, sa);
+      const i32x4 B = fetch_operand<KBI>(brow, h, sb);
+      typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+      const f16x4 SA = __builtin_bit_cast(f16x4, u32x2{sa, 0u});
+      const f16x4 SB = __builtin_bit_cast(f16x4, u32x2{sb, 0u});
+      Sd = __builtin_amdgcn_mfma_i32_32x32x32_i8(A, B, izero, 0, 0, 0);
+      Cd = __builtin_amdgcn_mfma_f32_32x32x8f16(SA, SB, fzero, 0, 0, 0);
+    };
+    auto epilogue = [&](int kb, int j, const i32x16 &Sd, const f32x16 &Cd) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[j][r] = fmaf((float)Sd[r], Cd[r], acc[j][r]);
+      if constexpr (STORE_S) {
+        const int64_t t = t_tile + 64 * wt + 32 * j + lrow;
+        const int64_t b = b_begin + (int64_t)s * KB + kb;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int64_t o = o_tile + 32 * wo + 8 * (r >> 2) + 4 * h + (r & 3);
+          if (t < a.n_tok && o < a.out_dim) a.blocksums[(t * a.out_dim + o) * a.nb + b] = Sd[r];
+        }
+      }
+    };
+    // Software pipeline over (block, token tile): issue the next pair of MFMAs
+    // before the epilogue of the current one.
+    issue_tile(std::integral_constant<int, 0>{}, 0, S[0], C[0]);
+    [&]<int... STEP>(std::integer_sequence<int, STEP...>) {
+      (([&] {
+         constexpr int NEXT = STEP + 1;
+         if constexpr (NEXT < 2 * KB)
+           issue_tile(std::integral_constant<int, NEXT / 2>{}, NEXT % 2, S[NEXT & 1], C[NEXT & 1]);
+         epilogue(STEP / 2, STEP % 2, S[STEP & 1], C[STEP & 1]);
+       }()), ...);
+    }(std::make_integer_sequence<int, 2 * KB>{});
+  }
+
+  float *dstp = a.out + (int64_t)ts * a.n_tok * a.out_dim;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int64_t t = t_tile + 64 * wt + 32 * j + lrow;
+    if (t < a.n_tok) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int64_t o = o_tile + 32 * wo + 8 * (r >> 2) + 4 * h + (r & 3);
+        if (o < a.out_dim) dstp[t * a.out_dim + o] = acc[j][r];
       }
     }
   }
@@ -245,12 +461,16 @@ size_t gemm_workspace_bytes(int64_t out_dim, int64_t n_tok, int split) {
   return split > 1 ? (size_t)split * (size_t)out_dim * (size_t)n_tok * sizeof(float) : 0;
 }
 
+static bool use_lds_kernel(int64_t nb, int64_t n_tok) { return nb % lds::KB == 0 && n_tok > 64; }
+
 hipError_t launch_gemm(float *out, int32_t *blocksums, const void *w, int64_t in_dim,
                        int64_t out_dim, const void *x_q, int64_t n_tok, int split,
                        float *partials, hipStream_t s) {
   const int64_t nb = in_dim / kBlockElems;
+  const bool direct = use_lds_kernel(nb, n_tok);
+  const int stage = direct ? lds::KB : kStageBlocks;
   int64_t bps = (nb + split - 1) / split;
-  bps = (bps + kStageBlocks - 1) / kStageBlocks * kStageBlocks;
+  bps = (bps + stage - 1) / stage * stage;
   const int64_t n_split = (nb + bps - 1) / bps;
   GemmArgs a{};
   a.out = n_split > 1 ? partials : out;
@@ -262,15 +482,25 @@ hipError_t launch_gemm(float *out, int32_t *blocksums, const void *w, int64_t in
   a.nb = nb;
   a.row_bytes = nb * kBlockBytes;
   a.blocks_per_split = bps;
-  const int tj = gemm_tj(n_tok);
-  const dim3 grid((uint32_t)((out_dim + 127) / 128), (uint32_t)((n_tok + 64 * tj - 1) / (64 * tj)),
-                  (uint32_t)n_split);
-  if (tj == 1) {
-    if (blocksums) hipLaunchKernelGGL((gemm_kernel<2, 1, kStageBlocks, true>), grid, dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((gemm_kernel<2, 1, kStageBlocks, false>), grid, dim3(256), 0, s, a);
+  a.n_split = (int32_t)n_split;
+  if (direct) {
+    a.tiles_o = (int32_t)((out_dim + lds::BO - 1) / lds::BO);
+    a.tiles_t = (int32_t)((n_tok + lds::BT - 1) / lds::BT);
+    const dim3 grid((uint32_t)a.tiles_o * (uint32_t)a.tiles_t * (uint32_t)n_split);
+    if (blocksums) hipLaunchKernelGGL(gemm_lds_kernel<true>, grid, dim3(512), 0, s, a);
+    else hipLaunchKernelGGL(gemm_lds_kernel<false>, grid, dim3(512), 0, s, a);
   } else {
-    if (blocksums) hipLaunchKernelGGL((gemm_kernel<2, 2, kStageBlocks, true>), grid, dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((gemm_kernel<2, 2, kStageBlocks, false>), grid, dim3(256), 0, s, a);
+    const int tj = gemm_tj(n_tok);
+    a.tiles_o = (int32_t)((out_dim + 127) / 128);
+    a.tiles_t = (int32_t)((n_tok + 64 * tj - 1) / (64 * tj));
+    const dim3 grid((uint32_t)a.tiles_o * (uint32_t)a.tiles_t * (uint32_t)n_split);
+    if (tj == 1) {
+      if (blocksums) hipLaunchKernelGGL((gemm_kernel<2, 1, kStageBlocks, true>), grid, dim3(256), 0, s, a);
+      else hipLaunchKernelGGL((gemm_kernel<2, 1, kStageBlocks, false>), grid, dim3(256), 0, s, a);
+    } else {
+      if (blocksums) hipLaunchKernelGGL((gemm_kernel<2, 2, kStageBlocks, true>), grid, dim3(256), 0, s, a);
+      else hipLaunchKernelGGL((gemm_kernel<2, 2, kStageBlocks, false>), grid, dim3(256), 0, s, a);
+    }
   }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || n_split == 1) return err;

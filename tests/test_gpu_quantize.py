@@ -56,6 +56,23 @@ def test_quantize_special_values():
     _check(x, "special values")
 
 
+def test_quantize_near_ties():
+    # Quotients one ulp either side of exact half-integers, with scales that are
+    # not powers of two: the rounding decision depends on the IEEE quotient.
+    rows = []
+    for amax in (100.0, 3.3, 0.07, 777.7, 1e-3):
+        d = np.float32(np.float32(amax) / np.float32(127.0))
+        for start in range(-63, 63, 30):
+            x = np.zeros(32, dtype=np.float32)
+            x[0] = amax
+            for i, k in enumerate(range(start, start + 30)):
+                t = np.float32((k + 0.5) * np.float64(d))
+                x[1 + i] = np.nextafter(t, np.float32(np.inf if i % 3 == 0 else -np.inf)) if i % 3 else t
+            x[31] = -x[5]
+            rows.append(x)
+    _check(torch.from_numpy(np.stack(rows)), "near ties")
+
+
 @pytest.mark.parametrize("cfg", ["tiny", "attn_q_b", "decode5", "moe", "prefill_a", "prefill_b"])
 def test_quantize_workloads(cfg):
     if cfg == "tiny":
