@@ -39,6 +39,25 @@ def row_bytes(k):
     return k // 32 * 34
 
 
+def profiled_traffic(profile):
+    """HBM bytes per launch from the committed rocprofv3 byte-counter summary,
+    or None when the kernel sources changed since the counters were taken."""
+    import hashlib
+    import re
+    path = os.path.join(ROOT, "profiles", profile)
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m = re.search(r"traffic_bytes_per_launch: (\d+)", text)
+    h = re.search(r"source_sha256_16: ([0-9a-f]+)\s+\(([^)]*)\)", text)
+    if not m or not h:
+        return None
+    digest = hashlib.sha256()
+    for f in h.group(2).split(", "):
+        digest.update(open(os.path.join(ROOT, f), "rb").read())
+    return int(m.group(1)) if digest.hexdigest()[:16] == h.group(1) else None
+
+
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
@@ -291,7 +310,8 @@ def main():
                                "-> fp32, step = quantize_act + matmul, 16 rotating weight copies",
                    "in_dim": 1024, "out_dim": 32768, "n_tok": 1, "kernel_plan": list(h["plan"])},
         "roofline": {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None,
+                     "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4),
+                     "traffic": profiled_traffic("matvec_attn_q_b.md"),
                      "kernel": "matvec_kernel<16,1,1,RG>", "kernel_us": round(h["kernel_us"], 3),
                      "bytes_per_launch": h["kernel_bytes"],
                      "quantize_us": round(h["quant_us"], 3)},
