@@ -271,30 +271,45 @@ constexpr int LPW = (INSTS + WAVES - 1) / WAVES;
 static_assert(ROWS * CPR % 64 == 0 && (BO * CPR) % 64 == 0, "whole wave loads per region");
 }  // namespace lds
 
-// 16 quant bytes of block KBI for half h, from a 16-byte-aligned row segment,
-// plus the block's binary16 scale bits for the lanes of half 0 (zero for half
-// 1).  The scale sits two bytes before the quants, so for every block but the
-// last of a stage it lies in the chunk already read for the operand.
+// Raw LDS data of one operand of block KBI: the 16-byte chunk holding the
+// first quant byte of half h and the chunk after it.  The block's binary16
+// scale sits two bytes before its quants, i.e. inside chunk 0 for every block
+// but the last of a stage, whose scale is read separately.
+struct RawOperand {
+  i32x4 c0, c1;
+  uint32_t scale7;  // only for the last block of a stage
+};
+
 template <int KBI>
-__device__ __forceinline__ i32x4 fetch_operand(const uint8_t *row, int h, uint32_t &scale) {
+__device__ __forceinline__ RawOperand read_operand(const uint8_t *row, int h) {
   constexpr int O = KBI * kBlockBytes + 2;  // quant offset for h = 0
   constexpr int M = O % 16;
   const uint8_t *p = row + (O - M) + 16 * h;
-  const i32x4 c0 = *reinterpret_cast<const i32x4 *>(p);
-  const uint32_t d0[4] = {(uint32_t)c0.x, (uint32_t)c0.y, (uint32_t)c0.z, (uint32_t)c0.w};
+  RawOperand r;
+  r.c0 = *reinterpret_cast<const i32x4 *>(p);
+  if constexpr (M != 0) r.c1 = *reinterpret_cast<const i32x4 *>(p + 16);
+  if constexpr (M < 2) r.scale7 = *reinterpret_cast<const uint16_t *>(row + KBI * kBlockBytes);
+  return r;
+}
+
+// 16 quant bytes of the operand realigned for the MFMA, and its scale bits for
+// half 0 (zero for half 1).
+template <int KBI>
+__device__ __forceinline__ i32x4 prepare_operand(const RawOperand &r, int h, uint32_t &scale) {
+  constexpr int O = KBI * kBlockBytes + 2;
+  constexpr int M = O % 16;
+  const uint32_t d0[4] = {(uint32_t)r.c0.x, (uint32_t)r.c0.y, (uint32_t)r.c0.z, (uint32_t)r.c0.w};
   if constexpr (M >= 2) {
-    constexpr int SB = M - 2;  // byte of the scale inside the chunk (even)
+    constexpr int SB = M - 2;  // byte of the scale inside chunk 0 (even)
     scale = h ? 0u : (d0[SB / 4] >> (8 * (SB % 4))) & 0xFFFFu;
   } else {
-    const uint16_t sv = *reinterpret_cast<const uint16_t *>(row + KBI * kBlockBytes);
-    scale = h ? 0u : (uint32_t)sv;
+    scale = h ? 0u : r.scale7;
   }
   if constexpr (M == 0) {
-    return c0;
+    return r.c0;
   } else {
-    const i32x4 c1 = *reinterpret_cast<const i32x4 *>(p + 16);
     const uint32_t d[8] = {d0[0], d0[1], d0[2], d0[3],
-                           (uint32_t)c1.x, (uint32_t)c1.y, (uint32_t)c1.z, (uint32_t)c1.w};
+                           (uint32_t)r.c1.x, (uint32_t)r.c1.y, (uint32_t)r.c1.z, (uint32_t)r.c1.w};
     constexpr int K = M / 4;
     if constexpr (M % 4 == 0) {
       return i32x4{(int)d[K], (int)d[K + 1], (int)d[K + 2], (int)d[K + 3]};
@@ -360,6 +375,37 @@ __global__ __launch_bounds__(512, 1) void gemm_lds_kernel(const GemmArgs a) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[j][r] = 0.0f;
 
+  typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+  // Results of one block's MFMAs (two token tiles), consumed one block later.
+  struct BlockOut {
+    i32x16 S[2];
+    f32x16 C[2];
+  };
+  auto epilogue = [&](const BlockOut &o, int64_t b) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[j][r] = fmaf((float)o.S[j][r], o.C[j][r], acc[j][r]);
+      if constexpr (STORE_S) {
+        const int64_t t = t_tile + 64 * wt + 32 * j + lrow;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int64_t oo = o_tile + 32 * wo + 8 * (r >> 2) + 4 * h + (r & 3);
+          if (b >= 0 && t < a.n_tok && oo < a.out_dim) a.blocksums[(t * a.out_dim + oo) * a.nb + b] = o.S[j][r];
+        }
+      }
+    }
+  };
+
+  // `prev` starts as zero tiles (its epilogue adds exactly 0), so every step
+  // runs the same straight-line code.
+  BlockOut prev;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    prev.S[j] = izero;
+    prev.C[j] = fzero;
+  }
+  int64_t prev_b = -1;  // block of `prev`, -1 before the first block
   issue(b_begin, 0);
   for (int s = 0; s < nstages; ++s) {
     __builtin_amdgcn_s_waitcnt(0);  // this wave's copies of stage s have landed
@@ -369,49 +415,52 @@ __global__ __launch_bounds__(512, 1) void gemm_lds_kernel(const GemmArgs a) {
     const uint8_t *arow = st + (32 * wo + lrow) * RB;
     const uint8_t *brow0 = st + REGION_W + (64 * wt + lrow) * RB;
     const uint8_t *brow1 = brow0 + 32 * RB;
+    const int64_t b0 = b_begin + (int64_t)s * KB;
 
-    i32x16 S[2];
-    f32x16 C[2];
-    // Scale tile: lanes of half 0 feed their row's (column's) binary16 scale
-    // into K-slot 0 and half 1 feeds zeros, so the f16 MFMA gives d_w * d_x
-    // exactly in the accumulator layout of the int8 tile.
-    auto issue_tile = [&](auto kbc, int j, i32x16 &Sd, f32x16 &Cd) {
-      constexpr int KBI = decltype(kbc)::value;
-      const uint8_t *brow = j ? brow1 : brow0;
-      uint32_t sa, sb;
-      const i32x4 A = fetch_operand<KBI>(arow, h, sa);
-      const i32x4 B = fetch_operand<KBI>(brow, h, sb);
-      typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-      const f16x4 SA = __builtin_bit_cast(f16x4, u32x2{sa, 0u});
-      const f16x4 SB = __builtin_bit_cast(f16x4, u32x2{sb, 0u});
-      Sd = __builtin_amdgcn_mfma_i32_32x32x32_i8(A, B, izero, 0, 0, 0);
-      Cd = __builtin_amdgcn_mfma_f32_32x32x8f16(SA, SB, fzero, 0, 0, 0);
-    };
-    auto epilogue = [&](int kb, int j, const i32x16 &Sd, const f32x16 &Cd) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[j][r] = fmaf((float)Sd[r], Cd[r], acc[j][r]);
-      if constexpr (STORE_S) {
-        const int64_t t = t_tile + 64 * wt + 32 * j + lrow;
-        const int64_t b = b_begin + (int64_t)s * KB + kb;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int64_t o = o_tile + 32 * wo + 8 * (r >> 2) + 4 * h + (r & 3);
-          if (t < a.n_tok && o < a.out_dim) a.blocksums[(t * a.out_dim + o) * a.nb + b] = Sd[r];
-        }
-      }
-    };
-    // Software pipeline over (block, token tile): issue the next pair of MFMAs
-    // before the epilogue of the current one.
-    issue_tile(std::integral_constant<int, 0>{}, 0, S[0], C[0]);
-    [&]<int... STEP>(std::integer_sequence<int, STEP...>) {
+    // Per block, four groups kept in this order: realignment of this block's
+    // operands (read one block earlier), LDS reads of the next block's
+    // operands, the MFMAs of this block, and the int->float/fma epilogue of
+    // the previous block.  The previous
+    // block's MFMA results and the next block's LDS data thus have a whole
+    // group of work to arrive.  The scale tile comes from an f16 MFMA whose
+    // K-slot 0 holds the binary16 scales (half 1 feeds zeros), giving
+    // d_w * d_x exactly in the accumulator layout of the int8 tile.
+    RawOperand ra = read_operand<0>(arow, h);
+    RawOperand rb0 = read_operand<0>(brow0, h);
+    RawOperand rb1 = read_operand<0>(brow1, h);
+    [&]<int... KBI>(std::integer_sequence<int, KBI...>) {
       (([&] {
-         constexpr int NEXT = STEP + 1;
-         if constexpr (NEXT < 2 * KB)
-           issue_tile(std::integral_constant<int, NEXT / 2>{}, NEXT % 2, S[NEXT & 1], C[NEXT & 1]);
-         epilogue(STEP / 2, STEP % 2, S[STEP & 1], C[STEP & 1]);
+         uint32_t sa, sb0, sb1;
+         const i32x4 A = prepare_operand<KBI>(ra, h, sa);
+         const i32x4 B0 = prepare_operand<KBI>(rb0, h, sb0);
+         const i32x4 B1 = prepare_operand<KBI>(rb1, h, sb1);
+         __builtin_amdgcn_sched_barrier(0);
+         if constexpr (KBI + 1 < KB) {
+           ra = read_operand<KBI + 1>(arow, h);
+           rb0 = read_operand<KBI + 1>(brow0, h);
+           rb1 = read_operand<KBI + 1>(brow1, h);
+         }
+         __builtin_amdgcn_sched_barrier(0);
+         BlockOut cur;
+         const f16x4 SA = __builtin_bit_cast(f16x4, u32x2{sa, 0u});
+         cur.S[0] = __builtin_amdgcn_mfma_i32_32x32x32_i8(A, B0, izero, 0, 0, 0);
+         cur.C[0] = __builtin_amdgcn_mfma_f32_32x32x8f16(SA, __builtin_bit_cast(f16x4, u32x2{sb0, 0u}), fzero, 0, 0, 0);
+         cur.S[1] = __builtin_amdgcn_mfma_i32_32x32x32_i8(A, B1, izero, 0, 0, 0);
+         cur.C[1] = __builtin_amdgcn_mfma_f32_32x32x8f16(SA, __builtin_bit_cast(f16x4, u32x2{sb1, 0u}), fzero, 0, 0, 0);
+         epilogue(prev, prev_b);
+         // Interleave: each MFMA of this block followed by 16 epilogue VALU ops.
+#pragma unroll
+         for (int g = 0; g < 4; ++g) {
+           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // 1 MFMA
+           __builtin_amdgcn_sched_group_barrier(0x002, 16, 0);  // 16 VALU
+         }
+         __builtin_amdgcn_sched_barrier(0);
+         prev = cur;
+         prev_b = b0 + KBI;
        }()), ...);
-    }(std::make_integer_sequence<int, 2 * KB>{});
+    }(std::make_integer_sequence<int, KB>{});
   }
+  epilogue(prev, prev_b);
 
   float *dstp = a.out + (int64_t)ts * a.n_tok * a.out_dim;
 #pragma unroll
