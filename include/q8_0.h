@@ -127,6 +127,48 @@ int q8_0_moe_grouped(float *out, const void *const *expert_w, int32_t n_expert,
                      int64_t n_tok, void *workspace, size_t workspace_bytes,
                      hipStream_t stream);
 
+/* One projection of q8_0_matmul_list. */
+typedef struct q8_0_matmul_item {
+    float *out;        /* fp32 [n_tok][out_dim], written                      */
+    const void *w;     /* Q8_0 [out_dim][in_dim/32] blocks                     */
+    const float *x;    /* fp32 [n_tok][in_dim] to quantize first, or NULL      */
+    void *x_q;         /* Q8_0 [n_tok][in_dim/32]: read when x is NULL; when x
+                          is set it receives the quantized rows, and may be
+                          NULL if the item is quantized inside the launch (see
+                          below)                                               */
+    int64_t in_dim;
+    int64_t out_dim;
+} q8_0_matmul_item;
+
+#define Q8_0_LIST_MAX 16
+
+/* Several independent projections that read the same number of tokens, in as
+ * few launches as possible ("Part 6: GPU 加速", section 4n, the exact decode
+ * fusions: adjacent small dispatches are merged -- e.g. the router with the
+ * shared expert's gate/up, or the q_a/kv pair -- and the merged kernel must
+ * give bit-identical results; section 4m: per-token launch overhead of
+ * serial decode).
+ *   items   : HOST array of n_items descriptors (1 <= n_items <= 16), read
+ *             during the call only.
+ *   n_tok   : tokens of every item.
+ * For each item: if x is set, x_q_i = q8_0_quantize_act(x); then
+ * out = q8_0_matmul(w, x_q_i) with no workspace.  Every output and every
+ * x_q byte is bit-identical to those separate calls.
+ * Items on the weight-streaming path (n_tok < 16) share one launch.  An item
+ * with x set whose in_dim is one of 64, 128, ..., 4096 with n_tok * in_dim <=
+ * 4096 (and x 16-byte, x_q 4-byte aligned) is quantized inside that launch,
+ * so a list of such decode projections is a single kernel launch; x_q may
+ * then be NULL.  Other items with x set are quantized by a launch of their
+ * own first and need x_q.  Items off the weight-streaming path run as
+ * q8_0_matmul would.
+ * Several items may share one x (and one x_q, which they then all write with
+ * the same bytes).  Otherwise no item may write memory another item reads.
+ * Errors: n_items outside [1, 16], any item invalid as for q8_0_matmul, or
+ * x set with x_q NULL on an item that is not quantized inside the launch
+ * -> Q8_0_EINVAL (nothing is enqueued). */
+int q8_0_matmul_list(const q8_0_matmul_item *items, int32_t n_items, int64_t n_tok,
+                     hipStream_t stream);
+
 /* Test hook: q8_0_matmul with a forced kernel variant and split-K count
  * (0 = automatic) that also writes every block's exact integer dot S_b into
  * blocksums (device int32 [n_tok][out_dim][in_dim/32]) when it is not NULL.

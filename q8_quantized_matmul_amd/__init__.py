@@ -44,6 +44,15 @@ if not os.path.exists(LIB_PATH):
 
 _lib = ctypes.CDLL(LIB_PATH)
 _i64, _i32, _vp, _sz = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t
+
+LIST_MAX = 16
+
+
+class MatmulItem(ctypes.Structure):
+    """struct q8_0_matmul_item."""
+    _fields_ = [("out", _vp), ("w", _vp), ("x", _vp), ("x_q", _vp), ("in_dim", _i64),
+                ("out_dim", _i64)]
+
 _sig = {
     "q8_0_quantize_act": ([_vp, _vp, _i64, _i64, _vp], ctypes.c_int),
     "q8_0_matmul_workspace_bytes": ([_i64, _i64, _i64], _sz),
@@ -57,6 +66,7 @@ _sig = {
                                 _sz, _vp], ctypes.c_int),
     "q8_0_matmul_plan": ([_i64, _i64, _i64, _sz, ctypes.POINTER(_i32), ctypes.POINTER(_i32)],
                          ctypes.c_int),
+    "q8_0_matmul_list": ([ctypes.POINTER(MatmulItem), _i32, _i64, _vp], ctypes.c_int),
     "q8_0_strerror": ([ctypes.c_int], ctypes.c_char_p),
 }
 for _name, (_args, _res) in _sig.items():
@@ -153,6 +163,19 @@ def q8_0_matmul_debug(w, x_q, in_dim, out_dim, n_tok, variant=KERNEL_AUTO, split
                                   workspace.numel() * workspace.element_size(), variant, split_k,
                                   _stream()), "q8_0_matmul_debug")
     return out, bs
+
+
+def q8_0_matmul_list(items, n_tok: int) -> None:
+    """Several projections in as few launches as possible.  items: sequence of
+    dicts with keys out (fp32 [n_tok][out_dim]), w, in_dim, out_dim and x (fp32
+    [n_tok][in_dim]) and/or x_q (uint8 Q8_0 rows); missing keys mean NULL.
+    Outputs (and x_q when x is given) are written in place."""
+    arr = (MatmulItem * max(len(items), 1))()
+    for i, it in enumerate(items):
+        arr[i] = MatmulItem(_dev(it.get("out"), "out", torch.float32), _dev(it.get("w"), "w"),
+                            _dev(it.get("x"), "x", torch.float32), _dev(it.get("x_q"), "x_q"),
+                            int(it["in_dim"]), int(it["out_dim"]))
+    _check(_lib.q8_0_matmul_list(arr, len(items), n_tok, _stream()), "q8_0_matmul_list")
 
 
 def q8_0_matmul_plan(in_dim: int, out_dim: int, n_tok: int, workspace_bytes: int):

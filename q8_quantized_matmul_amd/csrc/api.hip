@@ -132,6 +132,84 @@ int run_moe(float *out, int32_t *blocksums, const void *const *expert_w, int32_t
                                   fast, stream));
 }
 
+// How q8_0_matmul_list runs one item.
+struct ListPlan {
+  bool active;      // out_dim > 0: the item produces output
+  bool prequant;    // x is quantized into x_q by a launch of its own first
+  bool in_list;     // the matvec runs inside the shared list launch
+  bool fused;       // ... and quantizes x inside that launch
+};
+
+int plan_list_item(const q8_0_matmul_item &it, int64_t n_tok, ListPlan *lp) {
+  *lp = ListPlan{};
+  if (it.in_dim < 0 || it.out_dim < 0 || it.in_dim % Q8_0_BLOCK_ELEMS != 0) return Q8_0_EINVAL;
+  if (it.in_dim == 0 && it.out_dim > 0) return Q8_0_EINVAL;
+  if (it.out_dim > 0 && (!it.out || !it.w || (!it.x && !it.x_q))) return Q8_0_EINVAL;
+  if ((it.out && !aligned(it.out, 4)) || (it.w && !aligned(it.w, 2)) ||
+      (it.x_q && !aligned(it.x_q, 2)) || (it.x && !aligned(it.x, 4)))
+    return Q8_0_EALIGN;
+  if (it.in_dim == 0) return Q8_0_OK;  // nothing to quantize or multiply
+  lp->active = it.out_dim > 0;
+  if (!lp->active) {  // no output: only the requested x_q, if any
+    lp->prequant = it.x && it.x_q;
+    return Q8_0_OK;
+  }
+  const bool w4 = aligned(it.w, 4);
+  if (it.x && w4 && aligned(it.x, 16) && (!it.x_q || aligned(it.x_q, 4))) {
+    const Plan p = make_plan(it.in_dim, it.out_dim, n_tok, 0, true);
+    lp->fused = p.variant == Q8_0_KERNEL_MATVEC && q8::list_item_ok(it.in_dim) &&
+                q8::list_item_fusable(it.in_dim, n_tok);
+  }
+  if (lp->fused) {
+    lp->in_list = true;
+    return Q8_0_OK;
+  }
+  if (it.x) {
+    if (!it.x_q) return Q8_0_EINVAL;
+    lp->prequant = true;
+  }
+  const Plan p = make_plan(it.in_dim, it.out_dim, n_tok, 0, w4 && aligned(it.x_q, 4));
+  lp->in_list = p.variant == Q8_0_KERNEL_MATVEC && q8::list_item_ok(it.in_dim);
+  return Q8_0_OK;
+}
+
+int run_list(const q8_0_matmul_item *items, int32_t n_items, int64_t n_tok, hipStream_t stream) {
+  if (!items || n_items < 1 || n_items > Q8_0_LIST_MAX || n_tok < 0) return Q8_0_EINVAL;
+  ListPlan lp[Q8_0_LIST_MAX];
+  bool work = false;
+  for (int32_t i = 0; i < n_items; ++i) {
+    const int st = plan_list_item(items[i], n_tok, &lp[i]);
+    if (st != Q8_0_OK) return st;
+    work = work || lp[i].active || lp[i].prequant;
+  }
+  if (n_tok == 0 || !work) return Q8_0_OK;
+  int st = check_device();
+  if (st != Q8_0_OK) return st;
+  for (int32_t i = 0; i < n_items; ++i) {
+    if (!lp[i].prequant) continue;
+    if ((st = q8_0_quantize_act(items[i].x_q, items[i].x, n_tok, items[i].in_dim, stream)) != Q8_0_OK)
+      return st;
+  }
+  q8::ListItem batch[Q8_0_LIST_MAX];
+  int n_batch = 0;
+  for (int32_t i = 0; i < n_items; ++i) {
+    if (!lp[i].in_list) continue;
+    const q8_0_matmul_item &it = items[i];
+    batch[n_batch++] = q8::ListItem{it.out, it.w, lp[i].fused ? it.x : nullptr, it.x_q, it.in_dim,
+                                    it.out_dim};
+  }
+  if (n_batch > 0 && (st = status_of(q8::launch_matvec_list(batch, n_batch, n_tok, stream))) != Q8_0_OK)
+    return st;
+  for (int32_t i = 0; i < n_items; ++i) {
+    if (!lp[i].active || lp[i].in_list) continue;
+    const q8_0_matmul_item &it = items[i];
+    st = run_matmul(it.out, nullptr, it.w, it.in_dim, it.out_dim, it.x_q, n_tok, nullptr, 0,
+                    Q8_0_KERNEL_AUTO, 0, stream);
+    if (st != Q8_0_OK) return st;
+  }
+  return Q8_0_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -201,6 +279,11 @@ int q8_0_moe_grouped_debug(float *out, int32_t *blocksums, const void *const *ex
   if (blocksums && !aligned(blocksums, 4)) return Q8_0_EALIGN;
   return run_moe(out, blocksums, expert_w, n_expert, in_dim, out_dim, selected, n_used, x_q,
                  x_rows, n_tok, workspace, workspace_bytes, stream);
+}
+
+int q8_0_matmul_list(const q8_0_matmul_item *items, int32_t n_items, int64_t n_tok,
+                     hipStream_t stream) {
+  return run_list(items, n_items, n_tok, stream);
 }
 
 const char *q8_0_strerror(int status) {

@@ -32,6 +32,20 @@ hipError_t launch_generic_grouped(float *out, int32_t *blocksums, const void *co
                                   const int32_t *selected, int32_t n_used, const void *x_q,
                                   int32_t x_rows, int64_t n_tok, hipStream_t s);
 
+// Multi-matrix small-batch launch (one grid over up to kListMax projections).
+constexpr int kListMax = 16;
+struct ListItem {
+  float *out;
+  const void *w;
+  const float *x;   // non-null: quantized inside the launch (list_item_fusable)
+  void *x_q;        // read when x is null; written when x is set and x_q non-null
+  int64_t in_dim;
+  int64_t out_dim;
+};
+bool list_item_ok(int64_t in_dim);
+bool list_item_fusable(int64_t in_dim, int64_t n_tok);
+hipError_t launch_matvec_list(const ListItem *items, int n_items, int64_t n_tok, hipStream_t s);
+
 // moe.hip
 struct MoeLayout {
   int64_t counts, offsets, pairs;  // int32 element offsets inside the workspace

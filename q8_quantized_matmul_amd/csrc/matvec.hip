@@ -45,8 +45,82 @@ struct MatvecArgs {
   int32_t x_rows;                   // grouped: 0 = row per token, 1 = row per pair
 };
 
-template <int LPR, int WPR, int CPW, int RG, bool GROUPED, bool STORE_S>
-__global__ __launch_bounds__(256) void matvec_kernel(const MatvecArgs a) {
+// Where a workgroup reads its x_q rows from.
+//
+// GlobalX: the caller's x_q in device memory (L2-resident after first touch).
+struct GlobalX {
+  const uint8_t *x_q;
+  int64_t row_bytes;
+  __device__ __forceinline__ void prefetch() {}
+  __device__ __forceinline__ void publish() {}
+  __device__ __forceinline__ void load(int64_t xrow, int64_t pair, uint32_t (&d)[kPairDwords]) const {
+    load_pair(x_q + xrow * row_bytes + pair * kPairBytes, d);
+  }
+};
+
+// LdsX: fp32 activation rows quantized by the workgroup itself into LDS, so a
+// decode projection needs no separate quantizer launch.  Up to kFusePairs
+// pairs (n_tok * in_dim <= 4096 values) are quantized in one pass, 4 lanes per
+// pair.  The fp32 loads are issued before the weight loads (prefetch) and
+// consumed after them (publish), so the quantization hides under the weight
+// stream.  One workgroup per item (the writer) also stores the rows to
+// global x_q.
+constexpr int kFusePairs = 64;  // 256 threads / 4 lanes per pair
+
+struct LdsX {
+  uint32_t *lds;          // kFusePairs * 17 dwords
+  const float *x;         // fp32 [n_tok][in_dim]
+  uint8_t *x_q_out;       // written when non-null (writer workgroup only)
+  int log2_ppr;           // pairs per row = 1 << log2_ppr (a power of two here)
+  int n_pairs;            // n_tok << log2_ppr, 1 ..= kFusePairs
+  int64_t in_dim;
+  float4 v[4];
+
+  // Every thread loads (pairs past the end re-read the last pair), so the
+  // number of loads in flight is the same on every path and the wait before
+  // publish leaves the weight loads outstanding.
+  __device__ __forceinline__ void prefetch() {
+    const int j = threadIdx.x & 3;
+    const int p = min((int)(threadIdx.x >> 2), n_pairs - 1);
+    const int row = p >> log2_ppr;
+    const int pp = p - (row << log2_ppr);
+    const float4 *src = reinterpret_cast<const float4 *>(x + row * in_dim + pp * 64 + j * 16);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) v[k] = src[k];
+  }
+  __device__ __forceinline__ void publish() {
+    const int j = threadIdx.x & 3;
+    const int p = threadIdx.x >> 2;
+    uint32_t out[5];
+    quantize_pair4(v, j, out);
+    if (p < n_pairs) {
+      const int first = pair4_first(j), count = pair4_count(j);
+      uint32_t *l = lds + p * kPairDwords + first;
+#pragma unroll
+      for (int k = 0; k < 5; ++k)
+        if (k < count) l[k] = out[k];
+      if (x_q_out) {
+        uint32_t *g = reinterpret_cast<uint32_t *>(x_q_out + p * kPairBytes) + first;
+#pragma unroll
+        for (int k = 0; k < 5; ++k)
+          if (k < count) g[k] = out[k];
+      }
+    }
+    __syncthreads();
+  }
+  __device__ __forceinline__ void load(int64_t xrow, int64_t pair, uint32_t (&d)[kPairDwords]) const {
+    const uint32_t *b = lds + (((int)xrow << log2_ppr) + (int)pair) * kPairDwords;
+#pragma unroll
+    for (int i = 0; i < kPairDwords; ++i) d[i] = b[i];
+  }
+};
+
+// One workgroup tile of the matvec: TILE_ROWS weight rows against n_items x
+// rows.  `tile` is the tile index within the matrix; `w` and `items` the
+// (possibly per-expert) weights and item list.
+template <int LPR, int WPR, int CPW, int RG, bool GROUPED, bool STORE_S, class XS>
+__device__ __forceinline__ void matvec_body(const MatvecArgs &a, int64_t tile, const uint8_t *w,
+                                            const int32_t *items, int64_t n_items, XS &xs) {
   constexpr int RPW = 64 / LPR;                   // rows per wave row-group
   constexpr int ROWS_PER_SLOT = RG * RPW;
   constexpr int TILE_ROWS = (4 / WPR) * ROWS_PER_SLOT;
@@ -57,37 +131,25 @@ __global__ __launch_bounds__(256) void matvec_kernel(const MatvecArgs a) {
   const int slot = wave / WPR;
   const int part = wave % WPR;
 
-  const uint8_t *w = a.w;
-  const int32_t *items = nullptr;
-  int64_t n_items = a.n_items;
-  if constexpr (GROUPED) {
-    const int e = blockIdx.y;
-    n_items = a.counts[e];
-    if (n_items == 0) return;  // uniform across the workgroup
-    w = a.expert_w[e];
-    items = a.pairs + a.offsets[e];
-  }
-
-  const int64_t row0 = (int64_t)blockIdx.x * TILE_ROWS + slot * ROWS_PER_SLOT + lane / LPR;
+  const int64_t row0 = tile * TILE_ROWS + slot * ROWS_PER_SLOT + lane / LPR;
   int64_t pair_of[CPW];
 #pragma unroll
   for (int c = 0; c < CPW; ++c)
     pair_of[c] = (LPR < 64) ? (int64_t)(lane % LPR) : (int64_t)(c * WPR + part) * 64 + lane;
 
+  // Every lane issues the same loads (rows past the end re-read the last row,
+  // whose results are never stored), so the wait for the prefetched x rows
+  // can leave the weight loads in flight.
+  xs.prefetch();
   uint32_t wr[RG][CPW][kPairDwords];
 #pragma unroll
   for (int g = 0; g < RG; ++g) {
     const int64_t row = row0 + g * RPW;
+    const int64_t lrow = row < a.out_dim ? row : a.out_dim - 1;
 #pragma unroll
-    for (int c = 0; c < CPW; ++c) {
-      if (row < a.out_dim) {
-        load_pair(w + row * a.row_bytes + pair_of[c] * kPairBytes, wr[g][c]);
-      } else {
-#pragma unroll
-        for (int i = 0; i < kPairDwords; ++i) wr[g][c][i] = 0;
-      }
-    }
+    for (int c = 0; c < CPW; ++c) load_pair(w + lrow * a.row_bytes + pair_of[c] * kPairBytes, wr[g][c]);
   }
+  xs.publish();
 
   for (int64_t it = 0; it < n_items; ++it) {
     int64_t xrow = it, orow = it;
@@ -102,7 +164,7 @@ __global__ __launch_bounds__(256) void matvec_kernel(const MatvecArgs a) {
 #pragma unroll
     for (int c = 0; c < CPW; ++c) {
       uint32_t xr[kPairDwords];
-      load_pair(a.x_q + xrow * a.row_bytes + pair_of[c] * kPairBytes, xr);
+      xs.load(xrow, pair_of[c], xr);
       const float dxA = f16_bits_to_f32(xr[0]);
       const float dxB = f16_bits_to_f32(xr[8] >> 16);
 #pragma unroll
@@ -153,6 +215,22 @@ __global__ __launch_bounds__(256) void matvec_kernel(const MatvecArgs a) {
       }
     }
   }
+}
+
+template <int LPR, int WPR, int CPW, int RG, bool GROUPED, bool STORE_S>
+__global__ __launch_bounds__(256) void matvec_kernel(const MatvecArgs a) {
+  const uint8_t *w = a.w;
+  const int32_t *items = nullptr;
+  int64_t n_items = a.n_items;
+  if constexpr (GROUPED) {
+    const int e = blockIdx.y;
+    n_items = a.counts[e];
+    if (n_items == 0) return;  // uniform across the workgroup
+    w = a.expert_w[e];
+    items = a.pairs + a.offsets[e];
+  }
+  GlobalX xs{a.x_q, a.row_bytes};
+  matvec_body<LPR, WPR, CPW, RG, GROUPED, STORE_S>(a, blockIdx.x, w, items, n_items, xs);
 }
 
 // ---- generic fallback: one wave per (token, row), lanes stride over blocks.
@@ -270,6 +348,129 @@ int choose_rg(const MatvecShape &sh, int64_t rows, int64_t experts) {
   return rg;
 }
 
+// ---- multi-matrix launch: independent small-batch projections in one grid.
+//
+// Workgroups are numbered across the items in order; item i owns tiles
+// [first_tile_i, first_tile_{i+1}).  Each item runs the matvec body of its own
+// row shape with one or two row groups per wave slot.  Items that carry fp32 rows
+// quantize them in the workgroup (LdsX: rows of up to 64 pairs = 4096 values,
+// shape codes 0..6, at most kFusePairs pairs over all tokens); the others read x_q from memory.  The per-output
+// arithmetic and its order are those of the single-matrix kernel, so each item's
+// result is bit-identical to a separate quantize + matvec call.
+struct ListItemDev {
+  float *out;
+  const uint8_t *w;
+  const float *x;      // non-null: quantize these fp32 rows in the workgroup
+  uint8_t *x_q;        // x set: written by the item's first workgroup if non-null; else read
+  int64_t out_dim;
+  int64_t nb;          // in_dim / 32
+  int32_t shape;       // row-shape code (shape_code)
+  int32_t rg;          // row groups per wave slot (1 or 2)
+  int32_t first_tile;  // first workgroup of the item
+  int32_t pad;
+};
+
+struct ListArgs {
+  ListItemDev item[kListMax];
+  int32_t n_items;
+  int32_t n_tok;
+};
+
+template <int LPR, int WPR, int CPW, int RG, class XS>
+__device__ __forceinline__ void list_tile(const MatvecArgs &m, int64_t tile, XS &xs) {
+  matvec_body<LPR, WPR, CPW, RG, false, false>(m, tile, m.w, nullptr, m.n_items, xs);
+}
+
+// Row shapes with one 64-pair chunk per wave take one or two row groups per
+// wave slot; the two-chunk shapes (in_dim 16384, 32768) take one.
+template <int LPR, int WPR, int CPW, class XS>
+__device__ __forceinline__ void list_tile_rg(int rg, const MatvecArgs &m, int64_t tile, XS &xs) {
+  if constexpr (CPW == 1) {
+    if (rg == 2) {
+      list_tile<LPR, WPR, CPW, 2>(m, tile, xs);
+      return;
+    }
+  }
+  list_tile<LPR, WPR, CPW, 1>(m, tile, xs);
+}
+
+template <bool FUSED, class XS>
+__device__ __forceinline__ void list_dispatch(int code, int rg, const MatvecArgs &m, int64_t tile,
+                                              XS &xs) {
+  switch (code) {
+    case 0: list_tile_rg<1, 1, 1>(rg, m, tile, xs); break;
+    case 1: list_tile_rg<2, 1, 1>(rg, m, tile, xs); break;
+    case 2: list_tile_rg<4, 1, 1>(rg, m, tile, xs); break;
+    case 3: list_tile_rg<8, 1, 1>(rg, m, tile, xs); break;
+    case 4: list_tile_rg<16, 1, 1>(rg, m, tile, xs); break;
+    case 5: list_tile_rg<32, 1, 1>(rg, m, tile, xs); break;
+    case 6: list_tile_rg<64, 1, 1>(rg, m, tile, xs); break;
+    default: break;
+  }
+  if constexpr (!FUSED) {
+    switch (code) {
+      case 7: list_tile_rg<64, 2, 1>(rg, m, tile, xs); break;
+      case 8: list_tile_rg<64, 2, 2>(rg, m, tile, xs); break;
+      case 9: list_tile_rg<64, 4, 1>(rg, m, tile, xs); break;
+      case 10: list_tile_rg<64, 4, 2>(rg, m, tile, xs); break;
+      default: break;
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void matvec_list_kernel(const ListArgs a) {
+  __shared__ uint32_t xbuf[kFusePairs * kPairDwords];
+  int i = 0;
+  for (int j = 1; j < a.n_items; ++j)
+    if ((int)blockIdx.x >= a.item[j].first_tile) i = j;
+  const ListItemDev it = a.item[i];
+  MatvecArgs m{};
+  m.out = it.out;
+  m.w = it.w;
+  m.x_q = it.x_q;
+  m.out_dim = it.out_dim;
+  m.n_items = a.n_tok;
+  m.nb = it.nb;
+  m.row_bytes = it.nb * kBlockBytes;
+  const int64_t tile = (int64_t)blockIdx.x - it.first_tile;
+  if (it.x) {
+    LdsX xs;
+    xs.lds = xbuf;
+    xs.x = it.x;
+    xs.x_q_out = tile == 0 ? it.x_q : nullptr;
+    xs.log2_ppr = __builtin_ctzll((uint64_t)(it.nb / 2));
+    xs.n_pairs = a.n_tok << xs.log2_ppr;
+    xs.in_dim = it.nb * kBlockElems;
+    list_dispatch<true>(it.shape, it.rg, m, tile, xs);
+  } else {
+    GlobalX xs{it.x_q, m.row_bytes};
+    list_dispatch<false>(it.shape, it.rg, m, tile, xs);
+  }
+}
+
+// Shape code of a matvec row shape, -1 when the list kernel has no body for
+// it: rows of 3 or 4 chunks per wave (in_dim 12288, 49152, 65536) need about
+// twice the registers and would halve the occupancy of every item in the grid.
+int shape_code(const MatvecShape &sh) {
+  switch (sh.lanes_per_row) {
+    case 1: return 0;
+    case 2: return 1;
+    case 4: return 2;
+    case 8: return 3;
+    case 16: return 4;
+    case 32: return 5;
+    default: break;
+  }
+  switch (sh.waves_per_row * 10 + sh.chunks_per_wave) {
+    case 11: return 6;
+    case 21: return 7;
+    case 22: return 8;
+    case 41: return 9;
+    case 42: return 10;
+    default: return -1;
+  }
+}
+
 }  // namespace
 
 bool matvec_shape(int64_t in_dim, MatvecShape *shape) {
@@ -373,6 +574,50 @@ hipError_t launch_generic(float *out, int32_t *blocksums, const void *w, int64_t
                        blocksums, static_cast<const uint8_t *>(w),
                        static_cast<const uint8_t *>(x_q), out_dim, n_tok, nb);
   }
+  return hipGetLastError();
+}
+
+bool list_item_ok(int64_t in_dim) {
+  MatvecShape sh;
+  return matvec_shape(in_dim, &sh) && shape_code(sh) >= 0;
+}
+
+bool list_item_fusable(int64_t in_dim, int64_t n_tok) {
+  MatvecShape sh;
+  if (!matvec_shape(in_dim, &sh)) return false;
+  const int code = shape_code(sh);
+  return code >= 0 && code <= 6 && n_tok * (in_dim / 64) <= kFusePairs;
+}
+
+hipError_t launch_matvec_list(const ListItem *items, int n_items, int64_t n_tok, hipStream_t s) {
+  if (n_items < 1 || n_items > kListMax) return hipErrorInvalidValue;
+  ListArgs a{};
+  int64_t tiles = 0;
+  for (int i = 0; i < n_items; ++i) {
+    const ListItem &src = items[i];
+    MatvecShape sh;
+    if (!matvec_shape(src.in_dim, &sh)) return hipErrorInvalidValue;
+    const int code = shape_code(sh);
+    if (code < 0 || (src.x && !list_item_fusable(src.in_dim, n_tok))) return hipErrorInvalidValue;
+    ListItemDev &d = a.item[i];
+    d.out = src.out;
+    d.w = static_cast<const uint8_t *>(src.w);
+    d.x = src.x;
+    d.x_q = static_cast<uint8_t *>(src.x_q);
+    d.out_dim = src.out_dim;
+    d.nb = src.in_dim / kBlockElems;
+    // Two row groups per wave slot where the item alone still fills 1024
+    // workgroups: fewer, fuller workgroups stay resident in one round.
+    const int rg = (sh.chunks_per_wave == 1 && choose_rg(sh, src.out_dim, 1) >= 2) ? 2 : 1;
+    d.shape = code;
+    d.rg = rg;
+    d.first_tile = (int32_t)tiles;
+    tiles += (src.out_dim + tile_rows(sh, rg) - 1) / tile_rows(sh, rg);
+    if (tiles > INT32_MAX) return hipErrorInvalidValue;
+  }
+  a.n_items = n_items;
+  a.n_tok = (int32_t)n_tok;
+  hipLaunchKernelGGL(matvec_list_kernel, dim3((uint32_t)tiles), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

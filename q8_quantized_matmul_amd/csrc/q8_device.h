@@ -57,4 +57,191 @@ __device__ __forceinline__ void pair_dots(const uint32_t (&w)[kPairDwords],
   sB = b;
 }
 
+// ---- Q8_0 activation quantization of one block pair by 16 lanes.
+//
+// Block rule ("Part 3: 模型架构", section 2, the row quantizer, applied per 32
+// values with a binary16 scale): amax = max|x_i|, d32 = amax / 127 (IEEE fp32
+// division), q_i = roundf(x_i / d32) clamped to +-127, stored scale
+// binary16(d32) rounded to nearest even with subnormals kept.  A zero block
+// (amax == 0 or d32 == 0) is all zero; a non-finite value in the block, or a
+// d32 that overflows binary16, gives scale 0x7E00 and zero quants.
+//
+// The quotient x/d32 is formed as x * (1/d32), with 1/d32 an IEEE division
+// done once per block.  That product is within 3 * 2^-24 * 127.5 < 2.3e-5 of
+// the IEEE quotient, so whenever it lies at least kTieMargin from every
+// half-integer, both round to the same integer -- and, not being a tie,
+// round-to-nearest-even of the product gives it.  A lane holding a value
+// inside the margin (rare), or a block whose d32 is subnormal (1/d32 may
+// overflow), recomputes all its quotients as IEEE divisions rounded half away
+// from zero, so the quants are exactly roundf(x / d32).
+constexpr float kTieMargin = 6.103515625e-05f;  // 2^-14
+
+// q[i] = clamp(roundf(v[i] / d), -127, 127).
+template <int N>
+__device__ __forceinline__ void quant_values(const float (&v)[N], float d, float inv, bool exact,
+                                             int (&q)[N]) {
+  float r[N];
+  bool near = exact;
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    const float p = v[i] * inv;
+    r[i] = __builtin_rintf(p);
+    near = near || fabsf(p - r[i]) > 0.5f - kTieMargin;
+  }
+  if (near) {  // rare: IEEE quotients
+#pragma unroll
+    for (int i = 0; i < N; ++i) r[i] = roundf(v[i] / d);
+  }
+#pragma unroll
+  for (int i = 0; i < N; ++i) q[i] = (int)__builtin_amdgcn_fmed3f(r[i], -127.0f, 127.0f);
+}
+
+__device__ __forceinline__ uint32_t pack4(int q0, int q1, int q2, int q3) {
+  return ((uint32_t)q0 & 0xFFu) | (((uint32_t)q1 & 0xFFu) << 8) | (((uint32_t)q2 & 0xFFu) << 16) |
+         ((uint32_t)q3 << 24);
+}
+
+// The dwords one lane stores of a quantized pair (17 dwords, see pair_dots for
+// the layout): lane `sub` stores `hi` at dword sub + 1, lane 0 also `lo` at
+// dword 0.
+struct PairWords {
+  uint32_t hi;
+  uint32_t lo;
+};
+
+// Cross-lane moves inside a 16-lane DPP row (the 16-lane groups below are
+// row aligned): kDppXor1 / kDppXor2 read lane i^1 / i^2 (quad permutes),
+// kDppHalfMirror reads lane 7-i of the same 8-lane half row, kDppNext reads
+// lane i+1 (row shift left by one).
+constexpr int kDppXor1 = 0xB1;
+constexpr int kDppXor2 = 0x4E;
+constexpr int kDppHalfMirror = 0x141;
+constexpr int kDppNext = 0x101;
+
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __builtin_bit_cast(float, dpp_u32<CTRL>(__builtin_bit_cast(uint32_t, v)));
+}
+
+// Lanes 16j..16j+15 of the wave hold one pair of 64 values, lane sub = lane &
+// 15 holding values 4*sub..4*sub+3 in v (lanes 0..7 block A, 8..15 block B).
+// Every lane of the wave must call this (it exchanges values inside its
+// 16-lane group).
+__device__ __forceinline__ PairWords quantize_pair16(float4 v, int sub) {
+  // Non-finite values count as +inf so one max-reduction also flags them.
+  // The max over the 8 lanes of a block: quads first, then the mirrored quad.
+  auto mag = [](float t) { return __builtin_isfinite(t) ? fabsf(t) : __builtin_huge_valf(); };
+  float amax = fmaxf(fmaxf(mag(v.x), mag(v.y)), fmaxf(mag(v.z), mag(v.w)));
+  amax = fmaxf(amax, dpp_f32<kDppXor1>(amax));
+  amax = fmaxf(amax, dpp_f32<kDppXor2>(amax));
+  amax = fmaxf(amax, dpp_f32<kDppHalfMirror>(amax));
+
+  uint32_t bits = 0, qd = 0;
+  if (!__builtin_isfinite(amax)) {
+    bits = 0x7E00u;
+  } else if (amax > 0.0f) {
+    const float d = amax / 127.0f;
+    if (d > 0.0f) {
+      bits = __builtin_bit_cast(uint16_t, (_Float16)d);
+      if ((bits & 0x7FFFu) == 0x7C00u) {
+        bits = 0x7E00u;  // scale does not fit binary16
+      } else {
+        const bool exact = d < 1.17549435e-38f;  // subnormal d32: 1/d32 may overflow
+        const float inv = 1.0f / d;
+        const float vals[4] = {v.x, v.y, v.z, v.w};
+        int q[4];
+        quant_values(vals, d, inv, exact, q);
+        qd = pack4(q[0], q[1], q[2], q[3]);
+      }
+    }
+  }
+
+  // Pair dwords: [dA | qA0..1] [qA2..29 in 7 dwords] [qA30..31 | dB] [qB 8 dwords].
+  // Lane g < 8 forms dword g+1 from its own quants and lane g+1's; lane 0 also
+  // forms dword 0; lanes 8..15 form dwords 9..16.
+  const uint32_t next = dpp_u32<kDppNext>(qd);     // lane sub+1's quants
+  const uint32_t bitsB = dpp_u32<kDppNext>(bits);  // at lane 7: lane 8's (block B) scale
+  PairWords r;
+  if (sub < 7) {
+    r.hi = (qd >> 16) | (next << 16);
+  } else if (sub == 7) {
+    r.hi = (qd >> 16) | (bitsB << 16);
+  } else {
+    r.hi = qd;
+  }
+  r.lo = bits | (qd << 16);
+  return r;
+}
+
+// The same block rule with 4 lanes per pair, for quantizing a whole row of up
+// to 4096 values in one pass of a 256-thread workgroup.  Lanes 4i..4i+3 hold
+// one pair; lane j = lane & 3 holds values 16j..16j+15 in v[0..3] (j = 0, 1
+// block A, j = 2, 3 block B).  Every lane of the wave must call this.
+// Lane j stores out[0 .. pair4_count(j)) at dwords pair4_first(j) onward:
+// lane 0 dwords 0..4, lane 1 dwords 5..8, lane 2 dwords 9..12, lane 3 13..16.
+__device__ __forceinline__ int pair4_first(int j) { return j == 0 ? 0 : 1 + 4 * j; }
+__device__ __forceinline__ int pair4_count(int j) { return j == 0 ? 5 : 4; }
+
+__device__ __forceinline__ void quantize_pair4(const float4 (&v)[4], int j, uint32_t (&out)[5]) {
+  auto mag = [](float t) { return __builtin_isfinite(t) ? fabsf(t) : __builtin_huge_valf(); };
+  float amax = 0.0f;
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+    amax = fmaxf(amax, fmaxf(fmaxf(mag(v[k].x), mag(v[k].y)), fmaxf(mag(v[k].z), mag(v[k].w))));
+  amax = fmaxf(amax, dpp_f32<kDppXor1>(amax));  // the other half of the block
+
+  uint32_t bits = 0, qd[4] = {0, 0, 0, 0};
+  if (!__builtin_isfinite(amax)) {
+    bits = 0x7E00u;
+  } else if (amax > 0.0f) {
+    const float d = amax / 127.0f;
+    if (d > 0.0f) {
+      bits = __builtin_bit_cast(uint16_t, (_Float16)d);
+      if ((bits & 0x7FFFu) == 0x7C00u) {
+        bits = 0x7E00u;  // scale does not fit binary16
+      } else {
+        const bool exact = d < 1.17549435e-38f;  // subnormal d32: 1/d32 may overflow
+        const float inv = 1.0f / d;
+        float vals[16];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          vals[4 * k] = v[k].x;
+          vals[4 * k + 1] = v[k].y;
+          vals[4 * k + 2] = v[k].z;
+          vals[4 * k + 3] = v[k].w;
+        }
+        int q[16];
+        quant_values(vals, d, inv, exact, q);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) qd[k] = pack4(q[4 * k], q[4 * k + 1], q[4 * k + 2], q[4 * k + 3]);
+      }
+    }
+  }
+
+  // Block A's quants start 2 bytes into the pair, so lanes 0 and 1 shift their
+  // bytes by two: lane 0 borrows lane 1's first two quants, lane 1 lane 2's
+  // (block B's) scale.  Block B's quants are dword aligned.
+  const uint32_t nxt = dpp_u32<kDppNext>(qd[0]);  // at lane 0: qA16, qA17 in the low half
+  const uint32_t bitsB = dpp_u32<kDppNext>(bits); // at lane 1: block B's scale
+  if (j == 0) {
+    out[0] = bits | (qd[0] << 16);
+#pragma unroll
+    for (int k = 1; k < 4; ++k) out[k] = (qd[k - 1] >> 16) | (qd[k] << 16);
+    out[4] = (qd[3] >> 16) | (nxt << 16);
+  } else if (j == 1) {
+#pragma unroll
+    for (int k = 0; k < 3; ++k) out[k] = (qd[k] >> 16) | (qd[k + 1] << 16);
+    out[3] = (qd[3] >> 16) | (bitsB << 16);
+    out[4] = 0;
+  } else {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) out[k] = qd[k];
+    out[4] = 0;
+  }
+}
+
 }  // namespace q8

@@ -46,28 +46,9 @@ __device__ __forceinline__ uint32_t quantize_block32(const float (&v)[32], uint3
   return h;
 }
 
-// Eight lanes per block, 16 per block pair: lane g of a block holds values
-// 4g..4g+3 (one float4; a wave reads 1 KB of contiguous x per load).
-//
-// The quotient x/d32 is formed as x * (1/d32), with 1/d32 an IEEE division
-// done once per block.  That product is within 3 * 2^-24 * 127.5 < 2.3e-5 of
-// the IEEE quotient, so whenever it lies more than kTieMargin from every
-// half-integer, both round (halves away from zero) to the same integer.
-// Values inside the margin, and blocks whose d32 is subnormal, take the IEEE
-// division itself, so the quants are exactly roundf(x / d32).
-constexpr float kTieMargin = 6.103515625e-05f;  // 2^-14
-
-__device__ __forceinline__ int quant_one(float v, float d, float inv, bool exact) {
-  float r = v * inv;
-  const float a = fabsf(r);
-  const float f = a - truncf(a);
-  if (exact || fabsf(f - 0.5f) < kTieMargin) r = v / d;  // rare: IEEE quotient
-  float q = roundf(r);
-  q = fminf(fmaxf(q, -127.0f), 127.0f);
-  return (int)q;
-}
-
-// Needs x 16-byte aligned, x_q 4-byte aligned and an even block count.
+// Needs x 16-byte aligned, x_q 4-byte aligned and an even block count.  16
+// lanes per block pair, one float4 each (a wave reads 1 KB of contiguous x per
+// load).
 __global__ __launch_bounds__(256) void quantize_pair_kernel(const float *__restrict__ x,
                                                             uint8_t *__restrict__ xq,
                                                             int64_t total_pairs,
@@ -81,49 +62,11 @@ __global__ __launch_bounds__(256) void quantize_pair_kernel(const float *__restr
   const int64_t row = pair / pairs_per_row;
   const int64_t p = pair - row * pairs_per_row;
   const float4 v = *reinterpret_cast<const float4 *>(x + row * in_dim + p * 64 + sub * 4);
-
-  // Non-finite values count as +inf so one max-reduction also flags them.
-  auto mag = [](float t) { return __builtin_isfinite(t) ? fabsf(t) : __builtin_huge_valf(); };
-  float amax = fmaxf(fmaxf(mag(v.x), mag(v.y)), fmaxf(mag(v.z), mag(v.w)));
-  amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
-  amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
-  amax = fmaxf(amax, __shfl_xor(amax, 4, 64));
-
-  uint32_t bits = 0, qd = 0;
-  if (!__builtin_isfinite(amax)) {
-    bits = 0x7E00u;
-  } else if (amax > 0.0f) {
-    const float d = amax / 127.0f;
-    if (d > 0.0f) {
-      bits = __builtin_bit_cast(uint16_t, (_Float16)d);
-      if ((bits & 0x7FFFu) == 0x7C00u) {
-        bits = 0x7E00u;  // scale does not fit binary16
-      } else {
-        const bool exact = d < 1.17549435e-38f;  // subnormal d32: 1/d32 may overflow
-        const float inv = 1.0f / d;
-        const int q0 = quant_one(v.x, d, inv, exact), q1 = quant_one(v.y, d, inv, exact);
-        const int q2 = quant_one(v.z, d, inv, exact), q3 = quant_one(v.w, d, inv, exact);
-        qd = ((uint32_t)q0 & 0xFFu) | (((uint32_t)q1 & 0xFFu) << 8) |
-             (((uint32_t)q2 & 0xFFu) << 16) | ((uint32_t)q3 << 24);
-      }
-    }
-  }
-
-  // Pair layout, 17 dwords: [dA | qA0..1] [qA2..29 in 7 dwords] [qA30..31 | dB] [qB 8 dwords].
-  // Lane g < 8 writes dword g+1 from its own quants and lane g+1's; lane 0 also
-  // writes dword 0; lanes 8..15 write dwords 9..16.
-  const uint32_t next = __shfl_down(qd, 1, 64);
-  const uint32_t bitsB = __shfl(bits, ((int)threadIdx.x & 63 & ~15) + 8, 64);
+  const PairWords pw = quantize_pair16(v, sub);
   if (!live) return;
   uint32_t *dst = reinterpret_cast<uint32_t *>(xq + pair * kPairBytes);
-  if (sub < 7) {
-    dst[sub + 1] = (qd >> 16) | (next << 16);
-  } else if (sub == 7) {
-    dst[8] = (qd >> 16) | (bitsB << 16);
-  } else {
-    dst[sub + 1] = qd;
-  }
-  if (sub == 0) dst[0] = bits | (qd << 16);
+  dst[sub + 1] = pw.hi;
+  if (sub == 0) dst[0] = pw.lo;
 }
 
 // One lane per block; any block count, x_q only 2-byte aligned.

@@ -27,7 +27,7 @@ def q8():
 def test_exports_every_declared_symbol(q8):
     lib = ctypes.CDLL(q8.LIB_PATH)
     declared = _declared()
-    assert len(declared) == 9
+    assert len(declared) == 10
     for name in declared:
         assert hasattr(lib, name), name
     assert set(declared) == set(q8.EXPORTED)
@@ -96,6 +96,36 @@ def test_moe_validation(q8):
     assert call(n_tok=0) == q8.Q8_0_OK
 
 
+def test_list_validation(q8):
+    lib = q8.raw_library()
+
+    def call(items, n_tok=1, n=None):
+        arr = (q8.MatmulItem * max(len(items), 1))(*items)
+        return lib.q8_0_matmul_list(arr, len(items) if n is None else n, n_tok, None)
+
+    def item(out=FAKE, w=FAKE, x=None, x_q=FAKE, in_dim=1024, out_dim=256):
+        return q8.MatmulItem(out, w, x, x_q, in_dim, out_dim)
+
+    assert call([item()], n=0) == q8.Q8_0_EINVAL
+    assert call([item()] * 17) == q8.Q8_0_EINVAL
+    assert lib.q8_0_matmul_list(None, 1, 1, None) == q8.Q8_0_EINVAL
+    assert call([item(), item(in_dim=1000)]) == q8.Q8_0_EINVAL
+    assert call([item(out=None)]) == q8.Q8_0_EINVAL
+    assert call([item(x=None, x_q=None)]) == q8.Q8_0_EINVAL
+    assert call([item(out=FAKE + 2)]) == q8.Q8_0_EALIGN
+    assert call([item(x=FAKE + 2, x_q=None)]) == q8.Q8_0_EALIGN
+    assert call([item(), item()], n_tok=-1) == q8.Q8_0_EINVAL
+    # x without x_q is only allowed where the launch quantizes x itself:
+    # in_dim 64 * 2^k <= 4096 with n_tok * in_dim <= 4096, 16-byte aligned x.
+    assert call([item(x=FAKE, x_q=None, in_dim=8192)]) == q8.Q8_0_EINVAL
+    assert call([item(x=FAKE, x_q=None, in_dim=4096)], n_tok=2) == q8.Q8_0_EINVAL
+    assert call([item(x=FAKE + 4, x_q=None, in_dim=1024)]) == q8.Q8_0_EINVAL
+    assert call([item(x=FAKE, x_q=None, in_dim=96)]) == q8.Q8_0_EINVAL
+    # empty work is a successful no-op
+    assert call([item()], n_tok=0) == q8.Q8_0_OK
+    assert call([item(out=None, w=None, x_q=None, out_dim=0)]) == q8.Q8_0_OK
+
+
 def test_plan_regimes(q8):
     # Decode shapes stream weights through the matvec kernel.
     assert q8.q8_0_matmul_plan(1024, 32768, 1, 0) == (q8.KERNEL_MATVEC, 1)
@@ -124,6 +154,9 @@ def test_valid_call_without_device_reports_nodev(q8):
     lib = q8.raw_library()
     assert lib.q8_0_matmul(FAKE, FAKE, 32, 4, FAKE, 1, None, 0, None) == q8.Q8_0_ENODEV
     assert lib.q8_0_quantize_act(FAKE, FAKE, 1, 32, None) == q8.Q8_0_ENODEV
+    items = (q8.MatmulItem * 2)(q8.MatmulItem(FAKE, FAKE, FAKE, None, 1024, 256),
+                                q8.MatmulItem(FAKE, FAKE, None, FAKE, 8192, 64))
+    assert lib.q8_0_matmul_list(items, 2, 1, None) == q8.Q8_0_ENODEV
 
 
 def test_oracle_is_not_imported_by_the_product():
