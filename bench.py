@@ -3,15 +3,18 @@
 
 Headline (the single JSON line's `value`): the decode matvec workload
 attn_q_b (in_dim 1024 -> out_dim 32768, n_tok 1).  One step = quantize the
-fp32 activation row (q8_0_quantize_act) + the Q8_0 matmul, back to back on
-one stream.  value = algorithmic bytes of the step / step time, in GB/s.
+fp32 activation row + the Q8_0 matmul, done by one fused launch
+(q8_0_matmul_list); the same step as two calls (q8_0_quantize_act +
+q8_0_matmul) is reported beside it.  value = algorithmic bytes of the step
+(weights, fp32 row, fp32 output) / step time, in GB/s.
 Inputs are resident in HBM before timing starts; the weights rotate through
 16 independent copies (570 MB) so the 256 MB Infinity Cache cannot serve
 them.
 
 The same line also carries, under "secondary", the other workloads timed the
-same way (decode5, moe, prefill_a, prefill_b) with their own roofline
-fractions; prefill reports int8 TOPS against the int8 MFMA peak.
+same way (decode5, router + shared expert gate/up, moe, prefill_a,
+prefill_b) with their own roofline fractions; prefill reports int8 TOPS
+against the int8 MFMA peak.
 
 Options: --steps K --warmup W (headline loop), --gpus N (only 1 is
 supported: this is a single-GPU path), --quick (headline only),
@@ -114,27 +117,40 @@ def time_kernel(torch, fn, n_per_graph, reps=20):
 
 
 def bench_attn_q_b(torch, q8, wl, steps, warmup):
+    """One step = quantize the fp32 row + the Q8_0 matvec, as one fused launch
+    (q8_0_matmul_list with the fp32 row).  The separate-call form of the same
+    step (q8_0_quantize_act + q8_0_matmul) is timed beside it."""
     d = wl.attn_q_b("cuda")
     k, n = d["in_dim"], d["out_dim"]
     ws = [q8.q8_0_quantize_act(wl.attn_q_b("cuda", copy=c)["w"]) for c in range(ROT)]
     x = d["x"]
     xq = torch.empty((1, row_bytes(k)), dtype=torch.uint8, device="cuda")
     out = torch.empty((1, n), dtype=torch.float32, device="cuda")
+    items = [[dict(out=out, w=ws[c], x=x, in_dim=k, out_dim=n)] for c in range(ROT)]
 
     def step(i):
+        q8.q8_0_matmul_list(items[i % ROT], 1)
+
+    def step_separate(i):
         q8.q8_0_quantize_act(x, out=xq)
         q8.q8_0_matmul(ws[i % ROT], xq, k, n, 1, out=out)
 
     sec, done = time_steps(torch, step, steps, warmup)
-    kern_us = time_kernel(torch, lambda i: q8.q8_0_matmul(ws[i % ROT], xq, k, n, 1, out=out), ROT)
+    sec_sep, _ = time_steps(torch, step_separate, steps, warmup)
+    kern_us = time_kernel(torch, step, ROT)
+    mv_us = time_kernel(torch, lambda i: q8.q8_0_matmul(ws[i % ROT], xq, k, n, 1, out=out), ROT)
     quant_us = time_kernel(torch, lambda i: q8.q8_0_quantize_act(x, out=xq), ROT)
-    mm_bytes = n * row_bytes(k) + row_bytes(k) + 4 * n
-    q_bytes = 4 * k + row_bytes(k)
-    return dict(sec=sec, steps=done, step_bytes=mm_bytes + q_bytes, kernel_bytes=mm_bytes,
-                kernel_us=kern_us, quant_us=quant_us, plan=q8.q8_0_matmul_plan(k, n, 1, 0))
+    fused_bytes = n * row_bytes(k) + 4 * k + 4 * n       # W + fp32 x + out
+    mv_bytes = n * row_bytes(k) + row_bytes(k) + 4 * n   # W + x_q + out
+    return dict(sec=sec, steps=done, step_bytes=fused_bytes, kernel_bytes=fused_bytes,
+                kernel_us=kern_us, sec_separate=sec_sep, matvec_us=mv_us, matvec_bytes=mv_bytes,
+                quant_us=quant_us, plan=q8.q8_0_matmul_plan(k, n, 1, 0))
 
 
 def bench_decode5(torch, q8, wl, steps, warmup):
+    """One step = the five decode projections of a layer from fp32 rows, as
+    one q8_0_matmul_list call (the in_dim-32768 row is quantized by its own
+    launch first; the other four are quantized inside the list launch)."""
     rot = 8
     sets = [wl.decode5("cuda", copy=c) for c in range(rot)]
     wq = [[q8.q8_0_quantize_act(p["w"]) for p in s] for s in sets]
@@ -143,23 +159,62 @@ def bench_decode5(torch, q8, wl, steps, warmup):
     xqs = [torch.empty((1, row_bytes(k)), dtype=torch.uint8, device="cuda") for k, _ in dims]
     outs = [torch.empty((1, n), dtype=torch.float32, device="cuda") for _, n in dims]
     del sets
+    lists = [[dict(out=outs[j], w=wq[c][j], x=xs[j], x_q=xqs[j], in_dim=k, out_dim=n)
+              for j, (k, n) in enumerate(dims)] for c in range(rot)]
 
     def step(i):
+        q8.q8_0_matmul_list(lists[i % rot], 1)
+
+    def step_separate(i):
         for j, (k, n) in enumerate(dims):
             q8.q8_0_quantize_act(xs[j], out=xqs[j])
             q8.q8_0_matmul(wq[i % rot][j], xqs[j], k, n, 1, out=outs[j])
 
     sec, done = time_steps(torch, step, steps, warmup, per_graph=rot)
+    sec_sep, _ = time_steps(torch, step_separate, steps, warmup, per_graph=rot)
     per = []
     for j, (k, n) in enumerate(dims):
         us = time_kernel(torch, lambda i, j=j, k=k, n=n: q8.q8_0_matmul(wq[i % rot][j], xqs[j], k, n, 1,
                                                                            out=outs[j]), rot)
         per.append(dict(name=wl.DECODE5[j][0], kernel_us=us,
                         kernel_bytes=n * row_bytes(k) + row_bytes(k) + 4 * n))
-    mm_bytes = sum(p["kernel_bytes"] for p in per)
-    q_bytes = sum(4 * k + row_bytes(k) for k, _ in dims)
-    return dict(sec=sec, step_bytes=mm_bytes + q_bytes, kernel_bytes=mm_bytes,
-                kernel_us=sum(p["kernel_us"] for p in per), per_matrix=per)
+    w_bytes = sum(n * row_bytes(k) for k, n in dims)
+    step_bytes = w_bytes + sum(4 * k + 4 * n for k, n in dims)  # W + fp32 x + out
+    return dict(sec=sec, sec_separate=sec_sep, step_bytes=step_bytes, w_bytes=w_bytes,
+                per_matrix=per)
+
+
+def bench_router_shared(torch, q8, wl, steps, warmup):
+    """Decode router + shared expert gate/up from one fp32 row (4096): the
+    router (ffn_gate_inp, 4096 -> 256) and the shared expert's gate and up
+    (4096 -> 2048 each) as one q8_0_matmul_list launch."""
+    rot = ROT
+    k = 4096
+    x = wl.normal((1, k), wl.X_STD, "cuda", "decode5", "ffn_gate_inp", "x")
+    sets = []
+    for c in range(rot):
+        router = wl.normal((256, k), wl.W_STD, "cuda", "decode5", "ffn_gate_inp", "w", c)
+        gate = wl.normal((2048, k), wl.W_STD, "cuda", "moe", "shared", -1, "gate", c)
+        up = wl.normal((2048, k), wl.W_STD, "cuda", "moe", "shared", -1, "up", c)
+        sets.append([q8.q8_0_quantize_act(t) for t in (router, gate, up)])
+    dims = [(k, 256), (k, 2048), (k, 2048)]
+    outs = [torch.empty((1, n), dtype=torch.float32, device="cuda") for _, n in dims]
+    xq = torch.empty((1, row_bytes(k)), dtype=torch.uint8, device="cuda")
+    lists = [[dict(out=outs[j], w=sets[c][j], x=x, in_dim=kk, out_dim=n)
+              for j, (kk, n) in enumerate(dims)] for c in range(rot)]
+
+    def step(i):
+        q8.q8_0_matmul_list(lists[i % rot], 1)
+
+    def step_separate(i):
+        q8.q8_0_quantize_act(x, out=xq)
+        for j, (kk, n) in enumerate(dims):
+            q8.q8_0_matmul(sets[i % rot][j], xq, kk, n, 1, out=outs[j])
+
+    sec, done = time_steps(torch, step, steps, warmup, per_graph=rot)
+    sec_sep, _ = time_steps(torch, step_separate, steps, warmup, per_graph=rot)
+    step_bytes = sum(n * row_bytes(kk) + 4 * n for kk, n in dims) + 4 * k
+    return dict(sec=sec, sec_separate=sec_sep, step_bytes=step_bytes)
 
 
 def bench_moe(torch, q8, wl, steps, warmup):
@@ -306,29 +361,45 @@ def main():
         "steps": h["steps"], "warmup": args.warmup, "ms_per_step": round(h["sec"] * 1e3, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "int8",
         "data": "synthetic",
-        "config": {"workload": "attn_q_b decode matvec: Q8_0 W[32768x1024] x Q8_0 x[1x1024] "
-                               "-> fp32, step = quantize_act + matmul, 16 rotating weight copies",
+        "config": {"workload": "attn_q_b decode: fp32 x[1x1024] quantized to Q8_0 and multiplied by "
+                               "Q8_0 W[32768x1024] -> fp32, one fused launch per step "
+                               "(q8_0_matmul_list), 16 rotating weight copies",
                    "in_dim": 1024, "out_dim": 32768, "n_tok": 1, "kernel_plan": list(h["plan"])},
         "roofline": {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4),
-                     "traffic": profiled_traffic("matvec_attn_q_b.md"),
-                     "kernel": "matvec_kernel<16,1,1,RG>", "kernel_us": round(h["kernel_us"], 3),
-                     "bytes_per_launch": h["kernel_bytes"],
-                     "quantize_us": round(h["quant_us"], 3)},
+                     "traffic": profiled_traffic("matvec_list_attn_q_b.md"),
+                     "kernel": "matvec_list_kernel (in-launch quantize + matvec)",
+                     "kernel_us": round(h["kernel_us"], 3), "bytes_per_launch": h["kernel_bytes"]},
+        "separate_calls": {
+            "ms_per_step": round(h["sec_separate"] * 1e3, 5),
+            "GBs": round(h["matvec_bytes"] / h["sec_separate"] / 1e9, 1),
+            "matvec_kernel_us": round(h["matvec_us"], 3),
+            "matvec_kernel_GBs": round(h["matvec_bytes"] / (h["matvec_us"] * 1e-6) / 1e9, 1),
+            "quantize_us": round(h["quant_us"], 3)},
     }
     secondary = []
     if not args.quick:
         log("[bench] decode5")
         d5 = bench_decode5(torch, q8, wl, max(args.steps // 2, 16), args.warmup)
         secondary.append({
-            "workload": "decode5 (5 projections back to back, n_tok 1)",
+            "workload": "decode5 (5 projections of a layer from fp32 rows, n_tok 1, one list call)",
             "value": round(d5["step_bytes"] / d5["sec"] / 1e9, 2), "unit": "GB/s",
             "ms_per_step": round(d5["sec"] * 1e3, 5),
-            "kernels_GBs": round(d5["kernel_bytes"] / (d5["kernel_us"] * 1e-6) / 1e9, 1),
-            "frac_hbm_kernels": round(d5["kernel_bytes"] / (d5["kernel_us"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
-            "per_matrix": [{"name": p["name"], "kernel_us": round(p["kernel_us"], 3),
-                            "GBs": round(p["kernel_bytes"] / (p["kernel_us"] * 1e-6) / 1e9, 1)}
-                           for p in d5["per_matrix"]]})
+            "frac_hbm": round(d5["step_bytes"] / d5["sec"] / 1e9 / HBM_PEAK_GBS, 4),
+            "separate_calls_ms_per_step": round(d5["sec_separate"] * 1e3, 5),
+            "per_matrix_q8_0_matmul": [
+                {"name": p["name"], "kernel_us": round(p["kernel_us"], 3),
+                 "GBs": round(p["kernel_bytes"] / (p["kernel_us"] * 1e-6) / 1e9, 1)}
+                for p in d5["per_matrix"]]})
+        log("[bench] router_shared")
+        rs = bench_router_shared(torch, q8, wl, max(args.steps // 2, 16), args.warmup)
+        secondary.append({
+            "workload": "router + shared expert gate/up (4096 -> 256, 2048, 2048) from one fp32 row, "
+                        "one fused list launch",
+            "value": round(rs["step_bytes"] / rs["sec"] / 1e9, 2), "unit": "GB/s",
+            "ms_per_step": round(rs["sec"] * 1e3, 5),
+            "frac_hbm": round(rs["step_bytes"] / rs["sec"] / 1e9 / HBM_PEAK_GBS, 4),
+            "separate_calls_ms_per_step": round(rs["sec_separate"] * 1e3, 5)})
         log("[bench] moe")
         mo = bench_moe(torch, q8, wl, max(args.steps // 50, 5), 3)
         gate_gbs = mo["gate_bytes"] / (mo["gate_us"] * 1e-6) / 1e9
