@@ -296,7 +296,7 @@ typedef void (*MatvecFn)(const MatvecArgs);
 
 template <int LPR, int WPR, int CPW, bool GROUPED, bool STORE_S>
 MatvecFn pick_rg(int rg) {
-  if constexpr (CPW == 1) {
+  if constexpr (CPW == 1 || (CPW == 2 && WPR == 4)) {
     if (rg >= 4) return matvec_kernel<LPR, WPR, CPW, 4, GROUPED, STORE_S>;
   }
   if constexpr (CPW <= 2) {
@@ -330,19 +330,27 @@ MatvecFn pick_kernel(const MatvecShape &sh, int rg) {
   }
 }
 
-int max_rg(const MatvecShape &sh) { return sh.chunks_per_wave == 1 ? 4 : (sh.chunks_per_wave == 2 ? 2 : 1); }
+int max_rg(const MatvecShape &sh) {
+  if (sh.chunks_per_wave == 1 || (sh.chunks_per_wave == 2 && sh.waves_per_row == 4)) return 4;
+  return sh.chunks_per_wave == 2 ? 2 : 1;
+}
 
 int64_t tile_rows(const MatvecShape &sh, int rg) {
   return (int64_t)(4 / sh.waves_per_row) * rg * (64 / sh.lanes_per_row);
 }
 
 // Fewest rows per workgroup that still leaves >= 1024 workgroups (4 per CU);
-// small matrices get single-row-group tiles so all 256 CUs take part.
+// small matrices get single-row-group tiles so all 256 CUs take part.  Rows
+// of 8 chunks (in_dim 32768) are the exception: there each workgroup reads
+// the whole x_q row (as many bytes as one weight row), so row groups that
+// share it win as long as 256 workgroups remain.
 int choose_rg(const MatvecShape &sh, int64_t rows, int64_t experts) {
+  const bool wide = sh.waves_per_row * sh.chunks_per_wave >= 8;
+  const int64_t want = wide ? 256 : 1024;
   int rg = max_rg(sh);
   while (rg > 1) {
     const int64_t tiles = (rows + tile_rows(sh, rg) - 1) / tile_rows(sh, rg);
-    if (tiles * experts >= 1024) break;
+    if (tiles * experts >= want) break;
     rg /= 2;
   }
   return rg;
