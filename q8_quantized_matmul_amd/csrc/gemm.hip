@@ -476,6 +476,220 @@ __global__ __launch_bounds__(512, 1) void gemm_lds_kernel(const GemmArgs a) {
   }
 }
 
+// ---- Four-tile kernel: 128 x 128 workgroup tiles, 4 waves of 64 x 64.
+//
+// Each wave owns four independent 32x32 MFMA tiles, so the scale epilogue of
+// one tile (int32 -> fp32 convert + fma, the vector-ALU bound of this
+// method) overlaps the matrix-core work of the next, and two workgroups per
+// CU give each SIMD two such waves.  That fits LDS only with 4-block stages:
+// (128 token rows + 128 weight rows) x 136 bytes = 34 KB per stage, two
+// stages per workgroup.  136-byte row slices are not 16-byte multiples, so
+// the stage is filled by dword direct-to-LDS loads; lane l of copy
+// instruction k moves flat dword 64k + l of its wave's 64-row region, a
+// pattern that repeats every 17 instructions (32 rows), so 17 per-lane
+// offsets and a per-instruction scalar base address every copy.
+//
+// The MFMA's A operand is the token tile and B the weight tile, so a lane's
+// column of the result is an output column and the stores coalesce.  Only
+// whole tiles: out_dim and n_tok multiples of 128, in_dim of 128.  It has no
+// block-sum debug output; debug calls take the direct-LDS kernel.
+namespace t4 {
+constexpr int BO = 128;                     // output rows per workgroup
+constexpr int BT = 128;                     // tokens per workgroup
+constexpr int KB = 4;                       // blocks per stage
+constexpr int RB = KB * kBlockBytes;        // 136 bytes per row per stage
+constexpr int RD = RB / 4;                  // 34 dwords
+constexpr int STAGE = (BO + BT) * RB;       // 34816 bytes
+constexpr int WAVE_BYTES = 64 * RB;         // each wave copies 64 rows
+constexpr int PERIOD = 17;                  // 17 * 64 dwords = 32 rows
+static_assert(PERIOD * 64 == 32 * RD, "copy pattern period");
+}  // namespace t4
+
+// LDS words of one operand of block B of a stage: a 24-byte (16 for B = 3)
+// 8-byte-aligned window holding the 16 quant bytes of half h, and for B = 3
+// the block's scale, which lies before that window.
+struct T4Raw {
+  uint32_t w[6];
+  uint32_t sc;
+};
+
+template <int B>
+__device__ __forceinline__ void t4_read(const uint8_t *row, int h, T4Raw &r) {
+  constexpr int M = (2 * B + 2) % 8;  // quant start modulo 8 (rows are 8-aligned)
+  typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+  const u32x2 *q = reinterpret_cast<const u32x2 *>(row + B * kBlockBytes + 2 + 16 * h - M);
+  const u32x2 a = q[0], b = q[1];
+  r.w[0] = a.x;
+  r.w[1] = a.y;
+  r.w[2] = b.x;
+  r.w[3] = b.y;
+  if constexpr (M != 0) {
+    const u32x2 c = q[2];
+    r.w[4] = c.x;
+    r.w[5] = c.y;
+  } else {
+    r.sc = *reinterpret_cast<const uint16_t *>(row + B * kBlockBytes);
+  }
+}
+
+// The 16 quant bytes realigned for the MFMA, and the scale bits for half 0
+// (zero for half 1, which feeds the unused K slots of the scale MFMA).
+template <int B>
+__device__ __forceinline__ i32x4 t4_prep(const T4Raw &r, int h, uint32_t &scale) {
+  constexpr int M = (2 * B + 2) % 8;
+  const uint32_t *w = r.w;
+  if constexpr (M == 0) {
+    scale = h ? 0u : r.sc;
+    return i32x4{(int)w[0], (int)w[1], (int)w[2], (int)w[3]};
+  } else if constexpr (M == 4) {
+    scale = h ? 0u : (w[0] >> 16);
+    return i32x4{(int)w[1], (int)w[2], (int)w[3], (int)w[4]};
+  } else {
+    constexpr int K = M == 2 ? 0 : 1;
+    scale = h ? 0u : (M == 2 ? (w[0] & 0xFFFFu) : (w[1] & 0xFFFFu));
+    return i32x4{(int)__builtin_amdgcn_alignbyte(w[K + 1], w[K], 2),
+                 (int)__builtin_amdgcn_alignbyte(w[K + 2], w[K + 1], 2),
+                 (int)__builtin_amdgcn_alignbyte(w[K + 3], w[K + 2], 2),
+                 (int)__builtin_amdgcn_alignbyte(w[K + 4], w[K + 3], 2)};
+  }
+}
+
+__global__ __launch_bounds__(256, 2) void gemm_t4_kernel(const GemmArgs a) {
+  using namespace t4;
+  __shared__ __attribute__((aligned(16))) uint8_t ring[2 * STAGE];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  int to, tt, ts;
+  tile_of(a, to, tt, ts);
+  const int64_t o_tile = (int64_t)to * BO;
+  const int64_t t_tile = (int64_t)tt * BT;
+  const int64_t b_begin = (int64_t)ts * a.blocks_per_split;
+  const int64_t b_end = min(b_begin + a.blocks_per_split, a.nb);
+  const int nstages = (int)((b_end - b_begin) / KB);  // splits are whole stages
+
+  // Copies: waves 0, 1 move token rows t_tile + 64 w + r, waves 2, 3 weight
+  // rows o_tile + 64 (w - 2) + r, into stage rows 64 w + r.  The base is
+  // uniform per wave; each lane adds its 32-bit offset.
+  uint32_t off[PERIOD];
+#pragma unroll
+  for (int k = 0; k < PERIOD; ++k) {
+    const int f = 64 * k + lane;
+    const int r = f / RD;
+    off[k] = (uint32_t)(r * (int)a.row_bytes + 4 * (f - r * RD));
+  }
+  const uint8_t *copy_base = wave < 2 ? a.x_q + (t_tile + 64 * wave) * a.row_bytes
+                                      : a.w + (o_tile + 64 * (wave - 2)) * a.row_bytes;
+  auto issue = [&](int64_t b0, int buf) {
+    uint8_t *lds = ring + buf * STAGE + wave * WAVE_BYTES;
+#pragma unroll
+    for (int k = 0; k < 2 * PERIOD; ++k) {
+      const uint8_t *g = copy_base + (k / PERIOD) * 32 * a.row_bytes + b0 * kBlockBytes;
+      __builtin_amdgcn_global_load_lds(g + off[k % PERIOD], lds + 256 * k, 4, 0, 0);
+    }
+  };
+
+  const int wt = wave & 1;   // tokens [64 wt, 64 wt + 64) of the tile
+  const int wo = wave >> 1;  // outputs [64 wo, 64 wo + 64)
+  const int lrow = lane & 31;
+  const int h = lane >> 5;
+  const i32x16 izero = {};
+  const f32x16 fzero = {};
+  f32x16 acc[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[q][r] = 0.0f;
+
+  typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+  // MFMA results of one tile.  Tile q of a block goes to slot q & 1 and its
+  // epilogue runs after the next tile's MFMAs are issued, from that slot; with
+  // four tiles per block the previous tile is always in the other slot.
+  struct TileOut {
+    i32x16 S;
+    f32x16 C;
+  };
+  TileOut slot[2];
+  slot[1].S = izero;  // the tile "before" the first: adds exactly 0
+  slot[1].C = fzero;
+  auto epilogue = [&]<int Q>(const TileOut &o) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[Q][r] = fmaf((float)o.S[r], o.C[r], acc[Q][r]);
+  };
+
+  issue(b_begin, 0);
+  for (int s = 0; s < nstages; ++s) {
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's copies of stage s have landed
+    __syncthreads();                // ... and every wave's; buffer (s+1)&1 is free
+    if (s + 1 < nstages) issue(b_begin + (int64_t)(s + 1) * KB, (s + 1) & 1);
+    const uint8_t *st = ring + (s & 1) * STAGE;
+    const uint8_t *arow0 = st + (64 * wt + lrow) * RB;         // token rows
+    const uint8_t *arow1 = arow0 + 32 * RB;
+    const uint8_t *brow0 = st + (BT + 64 * wo + lrow) * RB;    // weight rows
+    const uint8_t *brow1 = brow0 + 32 * RB;
+    const int64_t b0 = b_begin + (int64_t)s * KB;
+
+    T4Raw ra0, ra1, rb0, rb1;
+    t4_read<0>(arow0, h, ra0);
+    t4_read<0>(arow1, h, ra1);
+    t4_read<0>(brow0, h, rb0);
+    t4_read<0>(brow1, h, rb1);
+    [&]<int... B>(std::integer_sequence<int, B...>) {
+      (([&] {
+         uint32_t sa0, sa1, sb0, sb1;
+         const i32x4 A0 = t4_prep<B>(ra0, h, sa0);
+         const i32x4 A1 = t4_prep<B>(ra1, h, sa1);
+         const i32x4 B0 = t4_prep<B>(rb0, h, sb0);
+         const i32x4 B1 = t4_prep<B>(rb1, h, sb1);
+         __builtin_amdgcn_sched_barrier(0);
+         if constexpr (B + 1 < KB) {
+           t4_read<B + 1>(arow0, h, ra0);
+           t4_read<B + 1>(arow1, h, ra1);
+           t4_read<B + 1>(brow0, h, rb0);
+           t4_read<B + 1>(brow1, h, rb1);
+         }
+         __builtin_amdgcn_sched_barrier(0);
+         const f16x4 SA[2] = {__builtin_bit_cast(f16x4, u32x2{sa0, 0u}),
+                              __builtin_bit_cast(f16x4, u32x2{sa1, 0u})};
+         const f16x4 SB[2] = {__builtin_bit_cast(f16x4, u32x2{sb0, 0u}),
+                              __builtin_bit_cast(f16x4, u32x2{sb1, 0u})};
+         const i32x4 AA[2] = {A0, A1};
+         const i32x4 BB[2] = {B0, B1};
+         [&]<int... Q>(std::integer_sequence<int, Q...>) {
+           (([&] {
+              TileOut &cur = slot[Q & 1];
+              const TileOut &prev = slot[(Q + 1) & 1];
+              cur.S = __builtin_amdgcn_mfma_i32_32x32x32_i8(AA[Q >> 1], BB[Q & 1], izero, 0, 0, 0);
+              cur.C = __builtin_amdgcn_mfma_f32_32x32x8f16(SA[Q >> 1], SB[Q & 1], fzero, 0, 0, 0);
+              epilogue.template operator()<(Q + 3) & 3>(prev);
+#pragma unroll
+              for (int g = 0; g < 2; ++g) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // 1 MFMA
+                __builtin_amdgcn_sched_group_barrier(0x002, 16, 0);  // 16 VALU
+              }
+              __builtin_amdgcn_sched_barrier(0);
+            }()), ...);
+         }(std::make_integer_sequence<int, 4>{});
+       }()), ...);
+    }(std::make_integer_sequence<int, KB>{});
+  }
+  epilogue.template operator()<3>(slot[1]);
+
+  // acc[q]: tokens t_tile + 64 wt + 32 (q >> 1) + 8 (r >> 2) + 4 h + (r & 3),
+  // output column o_tile + 64 wo + 32 (q & 1) + lrow.
+  float *dstp = a.out + (int64_t)ts * a.n_tok * a.out_dim;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int64_t o = o_tile + 64 * wo + 32 * (q & 1) + lrow;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int64_t t = t_tile + 64 * wt + 32 * (q >> 1) + 8 * (r >> 2) + 4 * h + (r & 3);
+      dstp[t * a.out_dim + o] = acc[q][r];
+    }
+  }
+}
+
 // out[i] = sum over splits s = 0..n_split-1 (in order) of partials[s][i].
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(float *__restrict__ out,
                                                             const float *__restrict__ part,
@@ -512,12 +726,18 @@ size_t gemm_workspace_bytes(int64_t out_dim, int64_t n_tok, int split) {
 
 static bool use_lds_kernel(int64_t nb, int64_t n_tok) { return nb % lds::KB == 0 && n_tok > 64; }
 
+// The four-tile kernel takes whole 128 x 128 tiles and 4-block stages.
+static bool use_t4_kernel(int64_t nb, int64_t out_dim, int64_t n_tok) {
+  return nb % t4::KB == 0 && out_dim % t4::BO == 0 && n_tok % t4::BT == 0;
+}
+
 hipError_t launch_gemm(float *out, int32_t *blocksums, const void *w, int64_t in_dim,
                        int64_t out_dim, const void *x_q, int64_t n_tok, int split,
                        float *partials, hipStream_t s) {
   const int64_t nb = in_dim / kBlockElems;
-  const bool direct = use_lds_kernel(nb, n_tok);
-  const int stage = direct ? lds::KB : kStageBlocks;
+  const bool four = !blocksums && use_t4_kernel(nb, out_dim, n_tok);
+  const bool direct = !four && use_lds_kernel(nb, n_tok);
+  const int stage = four ? t4::KB : (direct ? lds::KB : kStageBlocks);
   int64_t bps = (nb + split - 1) / split;
   bps = (bps + stage - 1) / stage * stage;
   const int64_t n_split = (nb + bps - 1) / bps;
@@ -532,7 +752,12 @@ hipError_t launch_gemm(float *out, int32_t *blocksums, const void *w, int64_t in
   a.row_bytes = nb * kBlockBytes;
   a.blocks_per_split = bps;
   a.n_split = (int32_t)n_split;
-  if (direct) {
+  if (four) {
+    a.tiles_o = (int32_t)(out_dim / t4::BO);
+    a.tiles_t = (int32_t)(n_tok / t4::BT);
+    const dim3 grid((uint32_t)a.tiles_o * (uint32_t)a.tiles_t * (uint32_t)n_split);
+    hipLaunchKernelGGL(gemm_t4_kernel, grid, dim3(256), 0, s, a);
+  } else if (direct) {
     a.tiles_o = (int32_t)((out_dim + lds::BO - 1) / lds::BO);
     a.tiles_t = (int32_t)((n_tok + lds::BT - 1) / lds::BT);
     const dim3 grid((uint32_t)a.tiles_o * (uint32_t)a.tiles_t * (uint32_t)n_split);

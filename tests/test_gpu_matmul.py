@@ -90,6 +90,82 @@ def test_mfma_ragged(out_dim, n_tok, in_dim, split):
     _run_and_check(wq, xq, wq_o, xq_o, in_dim, out_dim, n_tok, 3, split, where="mfma")
 
 
+def _run_outputs(wq, xq, wq_o, xq_o, in_dim, out_dim, n_tok, split, where):
+    """MFMA path without block sums (whole-tile shapes then take the four-tile
+    kernel, which has no block-sum output): outputs against the oracle."""
+    q8 = _q8()
+    say(f"[matmul] {where} in={in_dim} out={out_dim} n_tok={n_tok} split={split}")
+    out = torch.full((n_tok, out_dim), float("nan"), device="cuda")
+    ws = torch.empty(16 * out_dim * n_tok * 4, dtype=torch.uint8, device="cuda")
+    got, _ = q8.q8_0_matmul_debug(wq, xq, in_dim, out_dim, n_tok, variant=3, split_k=split,
+                                  blocksums=False, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    ref, mag, _ = oracle.matmul(wq_o, xq_o, in_dim)
+    assert_close(got.cpu().numpy(), ref, mag, where)
+    return got.cpu().numpy(), ref
+
+
+@pytest.mark.parametrize("out_dim,n_tok,in_dim,split", [
+    (256, 256, 512, 1), (384, 128, 1152, 3), (128, 384, 4096, 1), (256, 128, 2048, 4)])
+def test_mfma_whole_tiles(out_dim, n_tok, in_dim, split):
+    # Whole 128 x 128 tiles with 4-block stages: the four-tile kernel, also
+    # with split-K.
+    w = workloads.normal((out_dim, in_dim), 0.02, "cuda", "mf4", out_dim, in_dim, "w")
+    x = workloads.normal((n_tok, in_dim), 1.0, "cuda", "mf4", n_tok, in_dim, "x")
+    x[5, 100:110] *= 40.0  # outlier block
+    wq, xq, wq_o, xq_o = _prep(w, x)
+    _run_outputs(wq, xq, wq_o, xq_o, in_dim, out_dim, n_tok, split, "mfma4")
+
+
+def test_mfma_whole_tiles_special_scales():
+    in_dim, out_dim, n_tok = 512, 128, 128
+    w = workloads.normal((out_dim, in_dim), 2e-7, "cuda", "sub4", "w")
+    x = workloads.normal((n_tok, in_dim), 1.0, "cuda", "sub4", "x")
+    x[3, 17] = float("nan")
+    x[70, 64:96] = 0.0
+    wq, xq, wq_o, xq_o = _prep(w, x)
+    _run_outputs(wq, xq, wq_o, xq_o, in_dim, out_dim, n_tok, 1, "mfma4 special")
+
+
+def _unit_scale_blocks(rows, nb, seed, only_block=None):
+    """Q8_0 bytes with every scale binary16 1.0 and uniform int8 quants in
+    [-127, 127] (all quants zero outside `only_block` when it is given)."""
+    rng = np.random.default_rng(seed)
+    q = rng.integers(-127, 128, size=(rows, nb, 32), dtype=np.int64).astype(np.int8)
+    if only_block is not None:
+        keep = np.zeros(nb, dtype=bool)
+        keep[only_block] = True
+        q[:, ~keep, :] = 0
+    blk = np.zeros((rows, nb, 34), dtype=np.uint8)
+    blk[:, :, 0] = 0x00
+    blk[:, :, 1] = 0x3C  # binary16 1.0, little-endian
+    blk[:, :, 2:] = q.view(np.uint8)
+    return blk.reshape(rows, nb * 34)
+
+
+@pytest.mark.parametrize("only_block", [None, 0, 1, 2, 3, 5, 14])
+@pytest.mark.parametrize("split", [1, 2])
+def test_mfma_whole_tiles_exact_integer_sums(only_block, split):
+    # With unit scales every term is an integer and every partial sum stays
+    # below 2^24, so the fp32 output must equal the exact sum of the block
+    # dots; with one nonzero block it is that block's S_b.  This pins the
+    # integer path of the four-tile kernel (which has no block-sum output)
+    # bit-exactly, block by block across stage positions and stages.
+    in_dim, out_dim, n_tok = 512, 256, 128
+    nb = in_dim // 32
+    w_b = _unit_scale_blocks(out_dim, nb, 11, only_block)
+    x_b = _unit_scale_blocks(n_tok, nb, 12, only_block)
+    wq = torch.from_numpy(w_b).cuda()
+    xq = torch.from_numpy(x_b).cuda()
+    got, ref = _run_outputs(wq, xq, w_b, x_b, in_dim, out_dim, n_tok, split,
+                            f"mfma4 unit scales block={only_block}")
+    _, _, bs = oracle.matmul(w_b, x_b, in_dim, want_blocksums=True)
+    exact = bs.astype(np.int64).sum(axis=2)
+    assert np.abs(exact).max() < 2 ** 24
+    assert np.array_equal(got.astype(np.float64), exact.astype(np.float64))
+    assert np.array_equal(ref.astype(np.float64), exact.astype(np.float64))
+
+
 def test_subnormal_and_nan_scales():
     # Tiny weights give binary16-subnormal scales; a NaN-marked x block must
     # poison exactly the outputs of its token on every path.
