@@ -53,6 +53,10 @@ def _load():
     lib.q8o_matmul.restype = ctypes.c_int
     lib.q8o_moe_grouped.argtypes = [vp, i32, i64, i64, vp, i32, vp, i32, i64, vp, vp]
     lib.q8o_moe_grouped.restype = ctypes.c_int
+    lib.q8o_swiglu.argtypes = [vp, vp, i64, ctypes.c_float, vp]
+    lib.q8o_swiglu.restype = None
+    lib.q8o_moe_combine.argtypes = [vp, vp, i64, i32, i64, vp, vp]
+    lib.q8o_moe_combine.restype = None
     _lib = lib
     return lib
 
@@ -129,3 +133,27 @@ def moe_grouped(expert_w, selected: np.ndarray, xq: np.ndarray, in_dim: int,
     if rc < 0:
         raise ValueError(f"q8o_moe_grouped failed ({rc})")
     return out, mag, rc
+
+
+def swiglu(gate: np.ndarray, up: np.ndarray, clamp: float = 0.0) -> np.ndarray:
+    """mid = silu(gate) * up elementwise (optional clamp), fp32 of the double."""
+    gate = np.ascontiguousarray(gate, dtype=np.float32)
+    up = np.ascontiguousarray(up, dtype=np.float32)
+    assert gate.shape == up.shape
+    mid = np.empty_like(gate)
+    _load().q8o_swiglu(_ptr(gate), _ptr(up), gate.size, float(clamp), _ptr(mid))
+    return mid
+
+
+def moe_combine(y: np.ndarray, weights: np.ndarray, want_mag: bool = True):
+    """y fp32 [n_tok][n_used][dim], weights fp32 [n_tok][n_used] ->
+    (out fp32 [n_tok][dim], mag float64 or None)."""
+    y = np.ascontiguousarray(y, dtype=np.float32)
+    weights = np.ascontiguousarray(weights, dtype=np.float32)
+    n_tok, n_used, dim = y.shape
+    assert weights.shape == (n_tok, n_used)
+    out = np.empty((n_tok, dim), dtype=np.float32)
+    mag = np.empty((n_tok, dim), dtype=np.float64) if want_mag else None
+    _load().q8o_moe_combine(_ptr(y), _ptr(weights), n_tok, n_used, dim, _ptr(out),
+                            _ptr(mag) if mag is not None else None)
+    return out, mag

@@ -205,3 +205,33 @@ int q8o_moe_grouped(const uint8_t *const *expert_w, int32_t n_expert,
     }
     return invalid;
 }
+
+void q8o_swiglu(const float *gate, const float *up, int64_t n, float clamp, float *mid) {
+  for (int64_t i = 0; i < n; ++i) {
+    float g = gate[i], u = up[i];
+    if (clamp > 0.0f) {
+      if (g > clamp) g = clamp;
+      if (u > clamp) u = clamp;
+      if (u < -clamp) u = -clamp;
+    }
+    const double gd = (double)g;
+    const double silu = gd / (1.0 + exp(-gd));
+    mid[i] = (float)(silu * (double)u);
+  }
+}
+
+void q8o_moe_combine(const float *y, const float *weights, int64_t n_tok, int32_t n_used,
+                     int64_t dim, float *out, double *mag) {
+  for (int64_t t = 0; t < n_tok; ++t) {
+    for (int64_t o = 0; o < dim; ++o) {
+      double acc = 0.0, m = 0.0;
+      for (int32_t j = 0; j < n_used; ++j) {
+        const double term = (double)weights[t * n_used + j] * (double)y[(t * n_used + j) * dim + o];
+        acc += term;
+        m += fabs(term);
+      }
+      out[t * dim + o] = (float)acc;
+      if (mag) mag[t * dim + o] = m;
+    }
+  }
+}

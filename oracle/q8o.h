@@ -57,6 +57,21 @@ int q8o_moe_grouped(const uint8_t *const *expert_w, int32_t n_expert,
                     const uint8_t *xq, int32_t x_rows, int64_t n_tok,
                     float *out, double *mag);
 
+/* Expert FFN activation, SwiGLU ("Part 3: 模型架构", section 4, SwiGLU
+ * activation): for each i, g = gate[i] and u = up[i]; when clamp > 0 the
+ * 2-bit path's limits apply first (g > clamp -> clamp; u > clamp -> clamp;
+ * u < -clamp -> -clamp; NaN passes through); then
+ * mid[i] = silu(g) * u with silu(g) = g * sigmoid(g) = g / (1 + exp(-g)),
+ * evaluated in double and rounded once to fp32.  clamp <= 0: no clamp. */
+void q8o_swiglu(const float *gate, const float *up, int64_t n, float clamp, float *mid);
+
+/* Weighted combine of the experts' outputs ("Part 6: 代码走读", trace 5, the
+ * routed MoE's last step): out[t][o] = sum over j = 0..n_used-1 of
+ * weights[t][j] * y[t][j][o], in double in ascending j, rounded once to fp32;
+ * mag[t][o] (optional) = sum_j |weights[t][j] * y[t][j][o]|. */
+void q8o_moe_combine(const float *y, const float *weights, int64_t n_tok, int32_t n_used,
+                     int64_t dim, float *out, double *mag);
+
 #ifdef __cplusplus
 }
 #endif
