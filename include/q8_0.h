@@ -127,6 +127,59 @@ int q8_0_moe_grouped(float *out, const void *const *expert_w, int32_t n_expert,
                      int64_t n_tok, void *workspace, size_t workspace_bytes,
                      hipStream_t stream);
 
+/* Arguments of q8_0_moe_ffn. */
+typedef struct q8_0_moe_ffn_args {
+    float *out;                  /* fp32 [n_tok][d_model], written                  */
+    const void *const *gate_w;   /* DEVICE table of n_expert device pointers; expert
+                                    e's gate projection, Q8_0 [d_ff][d_model/32]     */
+    const void *const *up_w;     /* DEVICE table: up projections, [d_ff][d_model/32] */
+    const void *const *down_w;   /* DEVICE table: down projections, [d_model][d_ff/32] */
+    int32_t n_expert;
+    int32_t n_used;              /* experts per token                               */
+    int64_t d_model;             /* expert input and output width                   */
+    int64_t d_ff;                /* expert hidden width                             */
+    int64_t n_tok;
+    const int32_t *selected;     /* device int32 [n_tok][n_used]: expert ids         */
+    const float *weights;        /* device fp32 [n_tok][n_used]: routing weights     */
+    const void *x_q;             /* device Q8_0 [n_tok][d_model/32]                  */
+    float clamp;                 /* SwiGLU limit (10 in the pages' 2-bit path); <= 0
+                                    or NaN: no clamp                                */
+    float *mid;                  /* optional fp32 [n_tok*n_used][d_ff] (NULL: kept in
+                                    the workspace)                                   */
+    void *mid_q;                 /* optional Q8_0 [n_tok*n_used][d_ff/32] (NULL: idem) */
+    float *y;                    /* optional fp32 [n_tok*n_used][d_model], each pair's
+                                    down output (NULL: idem)                         */
+} q8_0_moe_ffn_args;
+
+/* Workspace bytes q8_0_moe_ffn needs: routing tables plus room for mid, mid_q
+ * and y (used only for those the caller does not supply). */
+size_t q8_0_moe_ffn_workspace_bytes(int64_t n_tok, int32_t n_used, int32_t n_expert,
+                                    int64_t d_model, int64_t d_ff);
+
+/* The routed expert FFN ("Part 6: 代码走读", trace 5,
+ * ds4_gpu_routed_moe_one_tensor: gate+up projections of the selected experts,
+ * SwiGLU, down projections, weighted sum; "Part 3: 模型架构", section 4, the
+ * SwiGLU activation and its clamp).  For token t and slot j, e = selected[t][j]:
+ *   gate = W_gate[e] x_t, up = W_up[e] x_t          (Q8_0 matmuls as q8_0_matmul)
+ *   mid  = silu(gate) * up, silu(g) = g / (1 + exp(-g)), after the optional
+ *          limits (gate from above, up to +-clamp)  (fp32)
+ *   mid_q = q8_0_quantize_act(mid)                  (the pair's Q8_0 row)
+ *   y    = W_down[e] mid_q                          (as q8_0_matmul)
+ *   out[t] = sum_j weights[t][j] * y[t][j], in slot order, one fp32 fma per slot.
+ * Gate and up of a pair are computed in one pass over both matrices.  Each
+ * touched expert's three matrices are streamed once for all of its pairs.
+ * Ids outside [0, n_expert): the pair's y row is NaN (so is the token's out
+ * row), its mid and mid_q rows are unspecified, and the int32 at byte 0 of the
+ * workspace counts such pairs once the stream reaches the end of the call.
+ * Shapes: d_model one of 64 * 2^k up to 4096, or 8192 or 16384 (the paired
+ * gate+up kernel); d_ff any in_dim the weight-streaming matvec takes (a
+ * multiple of 64: 64 * 2^k below 4096, or a multiple of 4096 up to 65536
+ * with 1-3 chunks of 4096 per wave); other shapes give Q8_0_EINVAL.
+ * Errors: bad sizes or null pointers -> Q8_0_EINVAL; workspace smaller than
+ * q8_0_moe_ffn_workspace_bytes() -> Q8_0_EWORKSPACE. */
+int q8_0_moe_ffn(const q8_0_moe_ffn_args *args, void *workspace, size_t workspace_bytes,
+                 hipStream_t stream);
+
 /* One projection of q8_0_matmul_list. */
 typedef struct q8_0_matmul_item {
     float *out;        /* fp32 [n_tok][out_dim], written                      */

@@ -48,6 +48,14 @@ _i64, _i32, _vp, _sz = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c
 LIST_MAX = 16
 
 
+class MoeFfnArgs(ctypes.Structure):
+    """struct q8_0_moe_ffn_args."""
+    _fields_ = [("out", _vp), ("gate_w", _vp), ("up_w", _vp), ("down_w", _vp),
+                ("n_expert", _i32), ("n_used", _i32), ("d_model", _i64), ("d_ff", _i64),
+                ("n_tok", _i64), ("selected", _vp), ("weights", _vp), ("x_q", _vp),
+                ("clamp", ctypes.c_float), ("mid", _vp), ("mid_q", _vp), ("y", _vp)]
+
+
 class MatmulItem(ctypes.Structure):
     """struct q8_0_matmul_item."""
     _fields_ = [("out", _vp), ("w", _vp), ("x", _vp), ("x_q", _vp), ("in_dim", _i64),
@@ -67,6 +75,8 @@ _sig = {
     "q8_0_matmul_plan": ([_i64, _i64, _i64, _sz, ctypes.POINTER(_i32), ctypes.POINTER(_i32)],
                          ctypes.c_int),
     "q8_0_matmul_list": ([ctypes.POINTER(MatmulItem), _i32, _i64, _vp], ctypes.c_int),
+    "q8_0_moe_ffn_workspace_bytes": ([_i64, _i32, _i32, _i64, _i64], _sz),
+    "q8_0_moe_ffn": ([ctypes.POINTER(MoeFfnArgs), _vp, _sz, _vp], ctypes.c_int),
     "q8_0_strerror": ([ctypes.c_int], ctypes.c_char_p),
 }
 for _name, (_args, _res) in _sig.items():
@@ -241,3 +251,34 @@ def q8_0_moe_grouped_debug(table, n_expert, selected, x_q, in_dim, out_dim, x_ro
 
 def moe_invalid_count(workspace: torch.Tensor) -> int:
     return int(workspace[:4].view(torch.int32).item())
+
+
+def q8_0_moe_ffn_workspace_bytes(n_tok: int, n_used: int, n_expert: int, d_model: int,
+                                 d_ff: int) -> int:
+    return int(_lib.q8_0_moe_ffn_workspace_bytes(n_tok, n_used, n_expert, d_model, d_ff))
+
+
+def q8_0_moe_ffn(gate_table, up_table, down_table, n_expert, selected, weights, x_q, d_model,
+                 d_ff, clamp=0.0, out=None, mid=None, mid_q=None, y=None, workspace=None):
+    """Routed expert FFN: out fp32 [n_tok][d_model].  Tables from expert_table();
+    selected int32 / weights fp32 [n_tok][n_used]; mid, mid_q, y optional
+    intermediate buffers.  Returns (out, workspace); workspace[:4] as int32
+    counts invalid expert ids."""
+    n_tok, n_used = selected.shape
+    if out is None:
+        out = torch.empty((n_tok, d_model), dtype=torch.float32, device=x_q.device)
+    if workspace is None:
+        workspace = torch.empty(
+            max(q8_0_moe_ffn_workspace_bytes(n_tok, n_used, n_expert, d_model, d_ff), 256),
+            dtype=torch.uint8, device=x_q.device)
+    args = MoeFfnArgs(_dev(out, "out", torch.float32), _dev(gate_table, "gate table", torch.int64),
+                      _dev(up_table, "up table", torch.int64),
+                      _dev(down_table, "down table", torch.int64), n_expert, n_used, d_model,
+                      d_ff, n_tok, _dev(selected, "selected", torch.int32),
+                      _dev(weights, "weights", torch.float32), _dev(x_q, "x_q"), float(clamp),
+                      _dev(mid, "mid", torch.float32), _dev(mid_q, "mid_q"),
+                      _dev(y, "y", torch.float32))
+    _check(_lib.q8_0_moe_ffn(ctypes.byref(args), _dev(workspace, "workspace"),
+                             workspace.numel() * workspace.element_size(), _stream()),
+           "q8_0_moe_ffn")
+    return out, workspace

@@ -132,6 +132,68 @@ int run_moe(float *out, int32_t *blocksums, const void *const *expert_w, int32_t
                                   fast, stream));
 }
 
+// Byte layout of the q8_0_moe_ffn workspace: routing ints, then mid, mid_q
+// and y, each 256-byte aligned.
+struct FfnLayout {
+  size_t route, mid, mid_q, y, total;
+};
+
+size_t align256(size_t v) { return (v + 255) / 256 * 256; }
+
+FfnLayout ffn_layout(int64_t n_tok, int32_t n_used, int32_t n_expert, int64_t d_model,
+                     int64_t d_ff) {
+  FfnLayout L{};
+  const int64_t pairs = n_tok * n_used;
+  L.route = 0;
+  L.mid = align256(q8_0_moe_workspace_bytes(n_tok, n_used, n_expert));
+  L.mid_q = L.mid + align256((size_t)(pairs * d_ff) * sizeof(float));
+  L.y = L.mid_q + align256((size_t)(pairs * (d_ff / Q8_0_BLOCK_ELEMS) * Q8_0_BLOCK_BYTES));
+  L.total = L.y + align256((size_t)(pairs * d_model) * sizeof(float));
+  return L;
+}
+
+int run_moe_ffn(const q8_0_moe_ffn_args *a, void *workspace, size_t workspace_bytes,
+                hipStream_t stream) {
+  if (!a) return Q8_0_EINVAL;
+  if (a->n_expert < 1 || a->n_expert > kMaxExperts || a->n_used < 1 || a->n_tok < 0 ||
+      a->d_model <= 0 || a->d_ff <= 0)
+    return Q8_0_EINVAL;
+  if (a->n_tok * (int64_t)a->n_used > INT32_MAX) return Q8_0_EINVAL;
+  if (!q8::matvec_pair_ok(a->d_model) || !matvec_ok(a->d_ff)) return Q8_0_EINVAL;
+  if (a->n_tok == 0) return Q8_0_OK;
+  if (!a->out || !a->gate_w || !a->up_w || !a->down_w || !a->selected || !a->weights || !a->x_q)
+    return Q8_0_EINVAL;
+  if (!aligned(a->out, 4) || !aligned(a->gate_w, 8) || !aligned(a->up_w, 8) ||
+      !aligned(a->down_w, 8) || !aligned(a->selected, 4) || !aligned(a->weights, 4) ||
+      !aligned(a->x_q, 4) || (a->mid && !aligned(a->mid, 16)) ||
+      (a->mid_q && !aligned(a->mid_q, 4)) || (a->y && !aligned(a->y, 4)))
+    return Q8_0_EALIGN;
+  const FfnLayout L = ffn_layout(a->n_tok, a->n_used, a->n_expert, a->d_model, a->d_ff);
+  if (!workspace || workspace_bytes < L.total) return Q8_0_EWORKSPACE;
+  if (!aligned(workspace, 256)) return Q8_0_EALIGN;
+  int st = check_device();
+  if (st != Q8_0_OK) return st;
+  uint8_t *ws = static_cast<uint8_t *>(workspace);
+  q8::MoeFfn f{};
+  f.out = a->out;
+  f.gate_w = a->gate_w;
+  f.up_w = a->up_w;
+  f.down_w = a->down_w;
+  f.n_expert = a->n_expert;
+  f.n_used = a->n_used;
+  f.d_model = a->d_model;
+  f.d_ff = a->d_ff;
+  f.n_tok = a->n_tok;
+  f.selected = a->selected;
+  f.weights = a->weights;
+  f.x_q = a->x_q;
+  f.clamp = a->clamp;
+  f.mid = a->mid ? a->mid : reinterpret_cast<float *>(ws + L.mid);
+  f.mid_q = a->mid_q ? a->mid_q : static_cast<void *>(ws + L.mid_q);
+  f.y = a->y ? a->y : reinterpret_cast<float *>(ws + L.y);
+  return status_of(q8::launch_moe_ffn(f, reinterpret_cast<int32_t *>(ws), stream));
+}
+
 // How q8_0_matmul_list runs one item.
 struct ListPlan {
   bool active;      // out_dim > 0: the item produces output
@@ -279,6 +341,17 @@ int q8_0_moe_grouped_debug(float *out, int32_t *blocksums, const void *const *ex
   if (blocksums && !aligned(blocksums, 4)) return Q8_0_EALIGN;
   return run_moe(out, blocksums, expert_w, n_expert, in_dim, out_dim, selected, n_used, x_q,
                  x_rows, n_tok, workspace, workspace_bytes, stream);
+}
+
+size_t q8_0_moe_ffn_workspace_bytes(int64_t n_tok, int32_t n_used, int32_t n_expert,
+                                    int64_t d_model, int64_t d_ff) {
+  if (n_tok < 0 || n_used < 1 || n_expert < 1 || d_model <= 0 || d_ff <= 0) return 0;
+  return ffn_layout(n_tok, n_used, n_expert, d_model, d_ff).total;
+}
+
+int q8_0_moe_ffn(const q8_0_moe_ffn_args *args, void *workspace, size_t workspace_bytes,
+                 hipStream_t stream) {
+  return run_moe_ffn(args, workspace, workspace_bytes, stream);
 }
 
 int q8_0_matmul_list(const q8_0_matmul_item *items, int32_t n_items, int64_t n_tok,

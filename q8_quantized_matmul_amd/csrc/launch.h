@@ -46,12 +46,37 @@ bool list_item_ok(int64_t in_dim);
 bool list_item_fusable(int64_t in_dim, int64_t n_tok);
 hipError_t launch_matvec_list(const ListItem *items, int n_items, int64_t n_tok, hipStream_t s);
 
+bool matvec_pair_ok(int64_t in_dim);
+hipError_t launch_matvec_grouped_pair(float *out, const void *const *gate_w,
+                                      const void *const *up_w, int32_t n_expert, int64_t in_dim,
+                                      int64_t out_dim, const void *x_q, int32_t n_used,
+                                      const int32_t *counts, const int32_t *offsets,
+                                      const int32_t *pairs, float clamp, hipStream_t s);
+
 // moe.hip
 struct MoeLayout {
   int64_t counts, offsets, pairs;  // int32 element offsets inside the workspace
   int64_t total_ints;
 };
 MoeLayout moe_layout(int64_t n_tok, int32_t n_used, int32_t n_expert);
+hipError_t launch_moe_route(const int32_t *selected, int64_t n_tok, int32_t n_used,
+                            int32_t n_expert, int32_t *ws, float *nan_rows, int64_t nan_dim,
+                            hipStream_t s);
+// The routed expert FFN: buffers already validated, intermediates placed.
+struct MoeFfn {
+  float *out;
+  const void *const *gate_w, *const *up_w, *const *down_w;
+  int32_t n_expert, n_used;
+  int64_t d_model, d_ff, n_tok;
+  const int32_t *selected;
+  const float *weights;
+  const void *x_q;
+  float clamp;
+  float *mid;   // [n_tok*n_used][d_ff]
+  void *mid_q;  // [n_tok*n_used][d_ff/32] blocks
+  float *y;     // [n_tok*n_used][d_model]
+};
+hipError_t launch_moe_ffn(const MoeFfn &f, int32_t *ws, hipStream_t s);
 hipError_t launch_moe(float *out, int32_t *blocksums, const void *const *expert_w,
                       int32_t n_expert, int64_t in_dim, int64_t out_dim,
                       const int32_t *selected, int32_t n_used, const void *x_q,

@@ -22,6 +22,8 @@
 //     shuffles in a fixed order, so results are deterministic.
 //   * Each workgroup loads all of its weight rows before touching x, so every
 //     wave has RG * CPW * 272 bytes in flight per lane group.
+#include <algorithm>
+
 #include "launch.h"
 #include "q8_device.h"
 
@@ -43,7 +45,21 @@ struct MatvecArgs {
   int64_t nb;                       // in_dim / 32
   int32_t n_used;                   // grouped
   int32_t x_rows;                   // grouped: 0 = row per token, 1 = row per pair
+  const uint8_t *const *expert_w2;  // paired: second table (up projections)
+  float clamp;                      // paired: SwiGLU limit, <= 0 for none
 };
+
+// SwiGLU of one output ("Part 3: 模型架构", section 4): the optional 2-bit
+// path limits (gate from above, up to +-clamp; NaN passes), then
+// silu(g) * u with silu(g) = g / (1 + exp(-g)).
+__device__ __forceinline__ float swiglu_one(float g, float u, float clamp) {
+  if (clamp > 0.0f) {
+    if (g > clamp) g = clamp;
+    if (u > clamp) u = clamp;
+    if (u < -clamp) u = -clamp;
+  }
+  return (g / (1.0f + expf(-g))) * u;
+}
 
 // Where a workgroup reads its x_q rows from.
 //
@@ -118,13 +134,18 @@ struct LdsX {
 // One workgroup tile of the matvec: TILE_ROWS weight rows against n_items x
 // rows.  `tile` is the tile index within the matrix; `w` and `items` the
 // (possibly per-expert) weights and item list.
-template <int LPR, int WPR, int CPW, int RG, bool GROUPED, bool STORE_S, class XS>
+// PAIR: two weight matrices of the same shape (w and w2, the gate and up
+// projections) against the same x rows; the stored output is their SwiGLU.
+template <int LPR, int WPR, int CPW, int RG, bool GROUPED, bool STORE_S, class XS,
+          bool PAIR = false>
 __device__ __forceinline__ void matvec_body(const MatvecArgs &a, int64_t tile, const uint8_t *w,
-                                            const int32_t *items, int64_t n_items, XS &xs) {
+                                            const int32_t *items, int64_t n_items, XS &xs,
+                                            const uint8_t *w2 = nullptr) {
   constexpr int RPW = 64 / LPR;                   // rows per wave row-group
   constexpr int ROWS_PER_SLOT = RG * RPW;
   constexpr int TILE_ROWS = (4 / WPR) * ROWS_PER_SLOT;
-  __shared__ float red[4][RG];
+  constexpr int NM = PAIR ? 2 : 1;                // weight matrices
+  __shared__ float red[4][NM][RG];
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -141,13 +162,16 @@ __device__ __forceinline__ void matvec_body(const MatvecArgs &a, int64_t tile, c
   // whose results are never stored), so the wait for the prefetched x rows
   // can leave the weight loads in flight.
   xs.prefetch();
-  uint32_t wr[RG][CPW][kPairDwords];
+  uint32_t wr[NM][RG][CPW][kPairDwords];
 #pragma unroll
   for (int g = 0; g < RG; ++g) {
     const int64_t row = row0 + g * RPW;
     const int64_t lrow = row < a.out_dim ? row : a.out_dim - 1;
 #pragma unroll
-    for (int c = 0; c < CPW; ++c) load_pair(w + lrow * a.row_bytes + pair_of[c] * kPairBytes, wr[g][c]);
+    for (int c = 0; c < CPW; ++c) {
+      load_pair(w + lrow * a.row_bytes + pair_of[c] * kPairBytes, wr[0][g][c]);
+      if constexpr (PAIR) load_pair(w2 + lrow * a.row_bytes + pair_of[c] * kPairBytes, wr[NM - 1][g][c]);
+    }
   }
   xs.publish();
 
@@ -158,9 +182,11 @@ __device__ __forceinline__ void matvec_body(const MatvecArgs &a, int64_t tile, c
       orow = pr;
       xrow = a.x_rows ? pr : pr / a.n_used;
     }
-    float acc[RG];
+    float acc[NM][RG];
 #pragma unroll
-    for (int g = 0; g < RG; ++g) acc[g] = 0.0f;
+    for (int m = 0; m < NM; ++m)
+#pragma unroll
+      for (int g = 0; g < RG; ++g) acc[m][g] = 0.0f;
 #pragma unroll
     for (int c = 0; c < CPW; ++c) {
       uint32_t xr[kPairDwords];
@@ -168,41 +194,52 @@ __device__ __forceinline__ void matvec_body(const MatvecArgs &a, int64_t tile, c
       const float dxA = f16_bits_to_f32(xr[0]);
       const float dxB = f16_bits_to_f32(xr[8] >> 16);
 #pragma unroll
-      for (int g = 0; g < RG; ++g) {
-        int sA, sB;
-        pair_dots(wr[g][c], xr, sA, sB);
-        const float scA = f16_bits_to_f32(wr[g][c][0]) * dxA;
-        const float scB = f16_bits_to_f32(wr[g][c][8] >> 16) * dxB;
-        acc[g] += scA * (float)sA;
-        acc[g] += scB * (float)sB;
-        if constexpr (STORE_S) {
-          const int64_t row = row0 + g * RPW;
-          if (row < a.out_dim) {
-            int32_t *bs = a.blocksums + (orow * a.out_dim + row) * a.nb + 2 * pair_of[c];
-            bs[0] = sA;
-            bs[1] = sB;
+      for (int m = 0; m < NM; ++m) {
+#pragma unroll
+        for (int g = 0; g < RG; ++g) {
+          int sA, sB;
+          pair_dots(wr[m][g][c], xr, sA, sB);
+          const float scA = f16_bits_to_f32(wr[m][g][c][0]) * dxA;
+          const float scB = f16_bits_to_f32(wr[m][g][c][8] >> 16) * dxB;
+          acc[m][g] += scA * (float)sA;
+          acc[m][g] += scB * (float)sB;
+          if constexpr (STORE_S) {
+            const int64_t row = row0 + g * RPW;
+            if (row < a.out_dim) {
+              int32_t *bs = a.blocksums + (orow * a.out_dim + row) * a.nb + 2 * pair_of[c];
+              bs[0] = sA;
+              bs[1] = sB;
+            }
           }
         }
       }
     }
 #pragma unroll
-    for (int g = 0; g < RG; ++g) {
+    for (int m = 0; m < NM; ++m) {
 #pragma unroll
-      for (int m = LPR / 2; m >= 1; m >>= 1) acc[g] += __shfl_xor(acc[g], m, 64);
+      for (int g = 0; g < RG; ++g) {
+#pragma unroll
+        for (int k = LPR / 2; k >= 1; k >>= 1) acc[m][g] += __shfl_xor(acc[m][g], k, 64);
+      }
     }
     if constexpr (WPR > 1) {
       if (lane == 0) {
 #pragma unroll
-        for (int g = 0; g < RG; ++g) red[wave][g] = acc[g];
+        for (int m = 0; m < NM; ++m)
+#pragma unroll
+          for (int g = 0; g < RG; ++g) red[wave][m][g] = acc[m][g];
       }
       __syncthreads();
       if (part == 0) {
 #pragma unroll
-        for (int g = 0; g < RG; ++g) {
-          float v = red[wave][g];
+        for (int m = 0; m < NM; ++m) {
 #pragma unroll
-          for (int p = 1; p < WPR; ++p) v += red[wave + p][g];
-          acc[g] = v;
+          for (int g = 0; g < RG; ++g) {
+            float v = red[wave][m][g];
+#pragma unroll
+            for (int p = 1; p < WPR; ++p) v += red[wave + p][m][g];
+            acc[m][g] = v;
+          }
         }
       }
       __syncthreads();
@@ -211,7 +248,9 @@ __device__ __forceinline__ void matvec_body(const MatvecArgs &a, int64_t tile, c
 #pragma unroll
       for (int g = 0; g < RG; ++g) {
         const int64_t row = row0 + g * RPW;
-        if (row < a.out_dim) a.out[orow * a.out_dim + row] = acc[g];
+        float v = acc[0][g];
+        if constexpr (PAIR) v = swiglu_one(acc[0][g], acc[NM - 1][g], a.clamp);
+        if (row < a.out_dim) a.out[orow * a.out_dim + row] = v;
       }
     }
   }
@@ -231,6 +270,19 @@ __global__ __launch_bounds__(256) void matvec_kernel(const MatvecArgs a) {
   }
   GlobalX xs{a.x_q, a.row_bytes};
   matvec_body<LPR, WPR, CPW, RG, GROUPED, STORE_S>(a, blockIdx.x, w, items, n_items, xs);
+}
+
+// Grouped gate+up pair with the SwiGLU epilogue (one x load feeds both
+// matrices; the mid row is written once).
+template <int LPR, int WPR, int CPW, int RG>
+__global__ __launch_bounds__(256) void matvec_pair_kernel(const MatvecArgs a) {
+  const int e = blockIdx.y;
+  const int64_t n_items = a.counts[e];
+  if (n_items == 0) return;  // uniform across the workgroup
+  GlobalX xs{a.x_q, a.row_bytes};
+  matvec_body<LPR, WPR, CPW, RG, true, false, GlobalX, true>(a, blockIdx.x, a.expert_w[e],
+                                                             a.pairs + a.offsets[e], n_items, xs,
+                                                             a.expert_w2[e]);
 }
 
 // ---- generic fallback: one wave per (token, row), lanes stride over blocks.
@@ -544,6 +596,68 @@ hipError_t launch_matvec_grouped(float *out, int32_t *blocksums, const void *con
   a.row_bytes = a.nb * kBlockBytes;
   a.n_used = n_used;
   a.x_rows = x_rows;
+  const int64_t tiles = (out_dim + tile_rows(sh, rg) - 1) / tile_rows(sh, rg);
+  hipLaunchKernelGGL(fn, dim3((uint32_t)tiles, (uint32_t)n_expert), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+typedef void (*PairFn)(const MatvecArgs);
+
+template <int LPR, int WPR, int CPW>
+PairFn pick_pair_rg(int rg) {
+  if (rg >= 2) return matvec_pair_kernel<LPR, WPR, CPW, 2>;
+  return matvec_pair_kernel<LPR, WPR, CPW, 1>;
+}
+
+// Paired (gate, up) rows hold twice the weight registers, so shapes with more
+// than one chunk per wave, or more than two row groups, are not offered.
+PairFn pick_pair_kernel(const MatvecShape &sh, int rg) {
+  switch (sh.lanes_per_row) {
+    case 1: return pick_pair_rg<1, 1, 1>(rg);
+    case 2: return pick_pair_rg<2, 1, 1>(rg);
+    case 4: return pick_pair_rg<4, 1, 1>(rg);
+    case 8: return pick_pair_rg<8, 1, 1>(rg);
+    case 16: return pick_pair_rg<16, 1, 1>(rg);
+    case 32: return pick_pair_rg<32, 1, 1>(rg);
+    default: break;
+  }
+  switch (sh.waves_per_row * 10 + sh.chunks_per_wave) {
+    case 11: return pick_pair_rg<64, 1, 1>(rg);
+    case 21: return pick_pair_rg<64, 2, 1>(rg);
+    case 41: return pick_pair_rg<64, 4, 1>(rg);
+    default: return nullptr;
+  }
+}
+
+bool matvec_pair_ok(int64_t in_dim) {
+  MatvecShape sh;
+  return matvec_shape(in_dim, &sh) && pick_pair_kernel(sh, 1) != nullptr;
+}
+
+hipError_t launch_matvec_grouped_pair(float *out, const void *const *gate_w,
+                                      const void *const *up_w, int32_t n_expert, int64_t in_dim,
+                                      int64_t out_dim, const void *x_q, int32_t n_used,
+                                      const int32_t *counts, const int32_t *offsets,
+                                      const int32_t *pairs, float clamp, hipStream_t s) {
+  MatvecShape sh;
+  if (!matvec_shape(in_dim, &sh)) return hipErrorInvalidValue;
+  const int rg = std::min(choose_rg(sh, out_dim, n_expert), 2);
+  PairFn fn = pick_pair_kernel(sh, rg);
+  if (!fn) return hipErrorInvalidValue;
+  MatvecArgs a{};
+  a.out = out;
+  a.expert_w = reinterpret_cast<const uint8_t *const *>(gate_w);
+  a.expert_w2 = reinterpret_cast<const uint8_t *const *>(up_w);
+  a.x_q = static_cast<const uint8_t *>(x_q);
+  a.counts = counts;
+  a.offsets = offsets;
+  a.pairs = pairs;
+  a.out_dim = out_dim;
+  a.nb = in_dim / kBlockElems;
+  a.row_bytes = a.nb * kBlockBytes;
+  a.n_used = n_used;
+  a.x_rows = 0;
+  a.clamp = clamp;
   const int64_t tiles = (out_dim + tile_rows(sh, rg) - 1) / tile_rows(sh, rg);
   hipLaunchKernelGGL(fn, dim3((uint32_t)tiles, (uint32_t)n_expert), dim3(256), 0, s, a);
   return hipGetLastError();

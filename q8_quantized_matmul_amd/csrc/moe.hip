@@ -141,18 +141,25 @@ size_t moe_route_lds_bytes(int32_t n_expert) {
   return sizeof(int32_t) * ((size_t)n_expert + kRouteThreads + kRouteWaves * 64);
 }
 
-hipError_t launch_moe(float *out, int32_t *blocksums, const void *const *expert_w,
-                      int32_t n_expert, int64_t in_dim, int64_t out_dim,
-                      const int32_t *selected, int32_t n_used, const void *x_q, int32_t x_rows,
-                      int64_t n_tok, int32_t *ws, bool fast, hipStream_t s) {
+hipError_t launch_moe_route(const int32_t *selected, int64_t n_tok, int32_t n_used,
+                            int32_t n_expert, int32_t *ws, float *nan_rows, int64_t nan_dim,
+                            hipStream_t s) {
   const MoeLayout L = moe_layout(n_tok, n_used, n_expert);
   const int64_t n_pairs = n_tok * n_used;
   int key_bits = 1;
   while ((1ll << key_bits) <= (int64_t)n_expert) ++key_bits;  // n_expert itself is the sentinel
   hipLaunchKernelGGL(moe_route_kernel, dim3(1), dim3(kRouteThreads), moe_route_lds_bytes(n_expert),
                      s, selected, n_pairs, n_expert, key_bits, ws, L.counts, L.offsets, L.pairs,
-                     out, out_dim);
-  hipError_t err = hipGetLastError();
+                     nan_rows, nan_dim);
+  return hipGetLastError();
+}
+
+hipError_t launch_moe(float *out, int32_t *blocksums, const void *const *expert_w,
+                      int32_t n_expert, int64_t in_dim, int64_t out_dim,
+                      const int32_t *selected, int32_t n_used, const void *x_q, int32_t x_rows,
+                      int64_t n_tok, int32_t *ws, bool fast, hipStream_t s) {
+  const MoeLayout L = moe_layout(n_tok, n_used, n_expert);
+  hipError_t err = launch_moe_route(selected, n_tok, n_used, n_expert, ws, out, out_dim, s);
   if (err != hipSuccess) return err;
   if (fast) {
     return launch_matvec_grouped(out, blocksums, expert_w, n_expert, in_dim, out_dim, x_q, x_rows,
@@ -160,6 +167,53 @@ hipError_t launch_moe(float *out, int32_t *blocksums, const void *const *expert_
   }
   return launch_generic_grouped(out, blocksums, expert_w, n_expert, in_dim, out_dim, selected,
                                 n_used, x_q, x_rows, n_tok, s);
+}
+
+namespace {
+
+// out[t][o] = sum over j = 0..n_used-1 (in that order) of
+// weights[t][j] * y[t*n_used + j][o], one fma per slot: the routed MoE's
+// weighted combine ("Part 6: 代码走读", trace 5, step 4), deterministic.
+__global__ __launch_bounds__(256) void moe_combine_kernel(float *__restrict__ out,
+                                                          const float *__restrict__ y,
+                                                          const float *__restrict__ weights,
+                                                          int64_t n_tok, int32_t n_used,
+                                                          int64_t dim) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n_tok * dim) return;
+  const int64_t t = i / dim;
+  const int64_t o = i - t * dim;
+  const float *yt = y + t * n_used * dim + o;
+  const float *wt = weights + t * n_used;
+  float acc = 0.0f;
+  for (int32_t j = 0; j < n_used; ++j) acc = fmaf(wt[j], yt[(int64_t)j * dim], acc);
+  out[i] = acc;
+}
+
+}  // namespace
+
+hipError_t launch_moe_ffn(const MoeFfn &f, int32_t *ws, hipStream_t s) {
+  const MoeLayout L = moe_layout(f.n_tok, f.n_used, f.n_expert);
+  const int64_t n_pairs = f.n_tok * f.n_used;
+  // 1. Routing; the down outputs of pairs with an invalid id are set to NaN.
+  hipError_t err = launch_moe_route(f.selected, f.n_tok, f.n_used, f.n_expert, ws, f.y, f.d_model, s);
+  if (err != hipSuccess) return err;
+  // 2. gate and up of every pair in one pass, SwiGLU into mid.
+  err = launch_matvec_grouped_pair(f.mid, f.gate_w, f.up_w, f.n_expert, f.d_model, f.d_ff, f.x_q,
+                                   f.n_used, ws + L.counts, ws + L.offsets, ws + L.pairs, f.clamp, s);
+  if (err != hipSuccess) return err;
+  // 3. mid -> Q8_0 rows, one per pair.
+  err = launch_quantize(f.mid_q, f.mid, n_pairs, f.d_ff, true, s);
+  if (err != hipSuccess) return err;
+  // 4. down projection of every pair.
+  err = launch_matvec_grouped(f.y, nullptr, f.down_w, f.n_expert, f.d_ff, f.d_model, f.mid_q, 1,
+                              f.n_used, ws + L.counts, ws + L.offsets, ws + L.pairs, s);
+  if (err != hipSuccess) return err;
+  // 5. weighted combine per token.
+  const int64_t n = f.n_tok * f.d_model;
+  hipLaunchKernelGGL(moe_combine_kernel, dim3((uint32_t)((n + 255) / 256)), dim3(256), 0, s, f.out,
+                     f.y, f.weights, f.n_tok, f.n_used, f.d_model);
+  return hipGetLastError();
 }
 
 }  // namespace q8

@@ -27,7 +27,7 @@ def q8():
 def test_exports_every_declared_symbol(q8):
     lib = ctypes.CDLL(q8.LIB_PATH)
     declared = _declared()
-    assert len(declared) == 10
+    assert len(declared) == 12
     for name in declared:
         assert hasattr(lib, name), name
     assert set(declared) == set(q8.EXPORTED)
@@ -124,6 +124,34 @@ def test_list_validation(q8):
     # empty work is a successful no-op
     assert call([item()], n_tok=0) == q8.Q8_0_OK
     assert call([item(out=None, w=None, x_q=None, out_dim=0)]) == q8.Q8_0_OK
+
+
+def test_moe_ffn_validation(q8):
+    lib = q8.raw_library()
+    need = q8.q8_0_moe_ffn_workspace_bytes(64, 8, 256, 4096, 2048)
+    pairs = 512
+    assert need >= pairs * 2048 * 4 + pairs * 64 * 34 + pairs * 4096 * 4
+
+    def call(ws=FAKE, ws_bytes=need, **kw):
+        f = dict(out=FAKE, gate_w=FAKE, up_w=FAKE, down_w=FAKE, n_expert=256, n_used=8,
+                 d_model=4096, d_ff=2048, n_tok=64, selected=FAKE, weights=FAKE, x_q=FAKE,
+                 clamp=0.0, mid=None, mid_q=None, y=None)
+        f.update(kw)
+        a = q8.MoeFfnArgs(**f)
+        return lib.q8_0_moe_ffn(ctypes.byref(a), ws, ws_bytes, None)
+
+    assert lib.q8_0_moe_ffn(None, FAKE, need, None) == q8.Q8_0_EINVAL
+    assert call(n_expert=0) == q8.Q8_0_EINVAL
+    assert call(n_used=0) == q8.Q8_0_EINVAL
+    assert call(d_model=4100) == q8.Q8_0_EINVAL
+    assert call(d_model=12288) == q8.Q8_0_EINVAL      # 3 chunks per wave: no paired kernel
+    assert call(d_ff=96) == q8.Q8_0_EINVAL
+    assert call(weights=None) == q8.Q8_0_EINVAL
+    assert call(mid=FAKE + 4) == q8.Q8_0_EALIGN
+    assert call(ws_bytes=need - 1) == q8.Q8_0_EWORKSPACE
+    assert call(ws=None) == q8.Q8_0_EWORKSPACE
+    assert call(ws=FAKE + 16) == q8.Q8_0_EALIGN
+    assert call(n_tok=0) == q8.Q8_0_OK
 
 
 def test_plan_regimes(q8):
