@@ -262,6 +262,15 @@ def bench_moe(torch, q8, wl, steps, warmup):
     gate_us = time_kernel(torch, gate, 1, reps=10)
     down_us = time_kernel(torch, down, 1, reps=10)
     sh_us = time_kernel(torch, sh_gate, 1, reps=10)
+    # The routed FFN as one q8_0_moe_ffn call (route, gate+up with SwiGLU,
+    # mid quantize, down, weighted combine) on the same x_q.
+    route_w = torch.rand((T, kk), generator=torch.Generator().manual_seed(23)).cuda()
+    f_out = torch.empty((T, D), device="cuda")
+    wsf = torch.empty(q8.q8_0_moe_ffn_workspace_bytes(T, kk, E, D, F), dtype=torch.uint8,
+                      device="cuda")
+    ffn = lambda i: q8.q8_0_moe_ffn(tables["gate"], tables["up"], tables["down"], E, sel, route_w,
+                                    xq, D, F, 0.0, out=f_out, workspace=wsf)
+    ffn_us = time_kernel(torch, ffn, 1, reps=10)
     touched = int(torch.unique(sel).numel())
     mat = F * row_bytes(D)  # bytes of one expert matrix (gate/up/down are equal)
     pairs = T * kk
@@ -271,7 +280,9 @@ def bench_moe(torch, q8, wl, steps, warmup):
     s_bytes = 3 * mat + 2 * (T * F * 4 + T * row_bytes(D)) + T * (row_bytes(F) + D * 4)
     q_bytes = T * (4 * D + row_bytes(D)) + mid.shape[0] * (4 * F + row_bytes(F))
     ops = 2 * (pairs + T) * 3 * F * D
+    ffn_bytes = 3 * touched * mat + T * row_bytes(D) + pairs * 8 + T * D * 4
     return dict(sec=sec, step_bytes=g_bytes + s_bytes + q_bytes, gate_us=gate_us, down_us=down_us,
+                ffn_us=ffn_us, ffn_bytes=ffn_bytes,
                 gate_bytes=gate_bytes, down_bytes=down_bytes, shared_us=sh_us,
                 shared_bytes=mat + T * F * 4 + T * row_bytes(D), touched_experts=touched, ops=ops)
 
@@ -412,7 +423,11 @@ def main():
             "grouped_down_us": round(mo["down_us"], 2),
             "grouped_down_GBs": round(mo["down_bytes"] / (mo["down_us"] * 1e-6) / 1e9, 1),
             "shared_gate_us": round(mo["shared_us"], 2),
-            "shared_gate_GBs": round(mo["shared_bytes"] / (mo["shared_us"] * 1e-6) / 1e9, 1)})
+            "shared_gate_GBs": round(mo["shared_bytes"] / (mo["shared_us"] * 1e-6) / 1e9, 1),
+            "routed_ffn_us": round(mo["ffn_us"], 2),
+            "routed_ffn_GBs": round(mo["ffn_bytes"] / (mo["ffn_us"] * 1e-6) / 1e9, 1),
+            "frac_hbm_routed_ffn": round(mo["ffn_bytes"] / (mo["ffn_us"] * 1e-6) / 1e9
+                                         / HBM_PEAK_GBS, 4)})
         for name in ("prefill_a", "prefill_b"):
             log(f"[bench] {name}")
             pf = bench_prefill(torch, q8, wl, name, max(args.steps // 40, 10), 3)

@@ -69,9 +69,82 @@ struct GlobalX {
   int64_t row_bytes;
   __device__ __forceinline__ void prefetch() {}
   __device__ __forceinline__ void publish() {}
-  __device__ __forceinline__ void load(int64_t xrow, int64_t pair, uint32_t (&d)[kPairDwords]) const {
+  __device__ __forceinline__ void advance(int64_t) {}
+  __device__ __forceinline__ void load(int64_t, int64_t xrow, int64_t pair,
+                                       uint32_t (&d)[kPairDwords]) const {
     load_pair(x_q + xrow * row_bytes + pair * kPairBytes, d);
   }
+};
+
+// StagedX: the x_q rows of the workgroup's items, XT at a time, copied into
+// LDS by direct global->LDS dword copies (64 consecutive dwords per wave
+// instruction; wave w copies the rows w, w+4, ...).  The copies of the first
+// XT rows are issued before the weight loads, so their latency hides under
+// the weight stream, and every wave then reads its pairs from LDS instead of
+// issuing per-item global loads.  ROW_DW = dwords of one x_q row; rows sit at
+// a stride rounded up to 64 dwords, the lanes past a row's end re-read its
+// last dword into the padding.
+template <int ROW_DW, int XT>
+struct StagedX {
+  static constexpr int STRIDE = (ROW_DW + 63) / 64 * 64;
+  static constexpr int NI = STRIDE / 64;
+  uint32_t *lds;             // XT * STRIDE dwords
+  const uint8_t *x_q;
+  int64_t row_bytes;
+  const int32_t *items;      // grouped: pair ids; null: item i is x row i
+  int64_t n_items;
+  uint32_t n_used;
+  int32_t x_rows;
+  int64_t base = 0;          // first item held in LDS
+
+  __device__ __forceinline__ void stage(int64_t first) {
+    base = first;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    const int rows = (int)min((int64_t)XT, n_items - first);
+    for (int t = wave; t < rows; t += 4) {
+      int64_t xrow = first + t;
+      if (items) {
+        const uint32_t pr = (uint32_t)items[first + t];
+        xrow = x_rows ? pr : pr / n_used;
+      }
+      const uint8_t *src = x_q + xrow * row_bytes;
+#pragma unroll
+      for (int k = 0; k < NI; ++k) {
+        const int d = min(64 * k + lane, ROW_DW - 1);
+        __builtin_amdgcn_global_load_lds(src + 4 * d, lds + t * STRIDE + 64 * k, 4, 0, 0);
+      }
+    }
+  }
+  __device__ __forceinline__ void prefetch() { stage(0); }
+  __device__ __forceinline__ void publish() {
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's copies (and weights) have landed
+    __syncthreads();                // ... and every wave's copies
+  }
+  // Called at the top of item `it` (uniform across the workgroup).
+  __device__ __forceinline__ void advance(int64_t it) {
+    if (it - base == XT) {
+      __syncthreads();  // every wave is done with the previous rows
+      stage(it);
+      publish();
+    }
+  }
+  __device__ __forceinline__ void load(int64_t it, int64_t, int64_t pair,
+                                       uint32_t (&d)[kPairDwords]) const {
+    const uint32_t *b = lds + (int)(it - base) * STRIDE + (int)pair * kPairDwords;
+#pragma unroll
+    for (int i = 0; i < kPairDwords; ++i) d[i] = b[i];
+  }
+};
+
+// x rows staged per workgroup: as many as fit in about 20 KB of LDS, 1 to 16.
+template <int LPR, int WPR, int CPW>
+struct StagedShape {
+  static constexpr int ROW_DW = kPairDwords * (LPR < 64 ? LPR : 64 * WPR * CPW);
+  static constexpr int STRIDE = (ROW_DW + 63) / 64 * 64;
+  static constexpr int XT_RAW = 20480 / (4 * STRIDE);
+  static constexpr int XT = XT_RAW < 1 ? 1 : (XT_RAW > 16 ? 16 : XT_RAW);
+  using X = StagedX<ROW_DW, XT>;
 };
 
 // LdsX: fp32 activation rows quantized by the workgroup itself into LDS, so a
@@ -124,7 +197,9 @@ struct LdsX {
     }
     __syncthreads();
   }
-  __device__ __forceinline__ void load(int64_t xrow, int64_t pair, uint32_t (&d)[kPairDwords]) const {
+  __device__ __forceinline__ void advance(int64_t) {}
+  __device__ __forceinline__ void load(int64_t, int64_t xrow, int64_t pair,
+                                       uint32_t (&d)[kPairDwords]) const {
     const uint32_t *b = lds + (((int)xrow << log2_ppr) + (int)pair) * kPairDwords;
 #pragma unroll
     for (int i = 0; i < kPairDwords; ++i) d[i] = b[i];
@@ -176,6 +251,7 @@ __device__ __forceinline__ void matvec_body(const MatvecArgs &a, int64_t tile, c
   xs.publish();
 
   for (int64_t it = 0; it < n_items; ++it) {
+    xs.advance(it);
     int64_t xrow = it, orow = it;
     if constexpr (GROUPED) {
       const int64_t pr = items[it];
@@ -190,7 +266,7 @@ __device__ __forceinline__ void matvec_body(const MatvecArgs &a, int64_t tile, c
 #pragma unroll
     for (int c = 0; c < CPW; ++c) {
       uint32_t xr[kPairDwords];
-      xs.load(xrow, pair_of[c], xr);
+      xs.load(it, xrow, pair_of[c], xr);
       const float dxA = f16_bits_to_f32(xr[0]);
       const float dxB = f16_bits_to_f32(xr[8] >> 16);
 #pragma unroll
@@ -256,7 +332,9 @@ __device__ __forceinline__ void matvec_body(const MatvecArgs &a, int64_t tile, c
   }
 }
 
-template <int LPR, int WPR, int CPW, int RG, bool GROUPED, bool STORE_S>
+// STAGED: x rows staged in LDS (StagedX); otherwise read from global memory
+// by every wave (GlobalX), which is cheaper for a single token row.
+template <int LPR, int WPR, int CPW, int RG, bool GROUPED, bool STORE_S, bool STAGED>
 __global__ __launch_bounds__(256) void matvec_kernel(const MatvecArgs a) {
   const uint8_t *w = a.w;
   const int32_t *items = nullptr;
@@ -268,8 +346,15 @@ __global__ __launch_bounds__(256) void matvec_kernel(const MatvecArgs a) {
     w = a.expert_w[e];
     items = a.pairs + a.offsets[e];
   }
-  GlobalX xs{a.x_q, a.row_bytes};
-  matvec_body<LPR, WPR, CPW, RG, GROUPED, STORE_S>(a, blockIdx.x, w, items, n_items, xs);
+  if constexpr (STAGED) {
+    using SX = typename StagedShape<LPR, WPR, CPW>::X;
+    __shared__ __attribute__((aligned(16))) uint32_t xbuf[StagedShape<LPR, WPR, CPW>::XT * SX::STRIDE];
+    SX xs{xbuf, a.x_q, a.row_bytes, items, n_items, (uint32_t)a.n_used, a.x_rows};
+    matvec_body<LPR, WPR, CPW, RG, GROUPED, STORE_S>(a, blockIdx.x, w, items, n_items, xs);
+  } else {
+    GlobalX xs{a.x_q, a.row_bytes};
+    matvec_body<LPR, WPR, CPW, RG, GROUPED, STORE_S>(a, blockIdx.x, w, items, n_items, xs);
+  }
 }
 
 // Grouped gate+up pair with the SwiGLU epilogue (one x load feeds both
@@ -279,10 +364,12 @@ __global__ __launch_bounds__(256) void matvec_pair_kernel(const MatvecArgs a) {
   const int e = blockIdx.y;
   const int64_t n_items = a.counts[e];
   if (n_items == 0) return;  // uniform across the workgroup
-  GlobalX xs{a.x_q, a.row_bytes};
-  matvec_body<LPR, WPR, CPW, RG, true, false, GlobalX, true>(a, blockIdx.x, a.expert_w[e],
-                                                             a.pairs + a.offsets[e], n_items, xs,
-                                                             a.expert_w2[e]);
+  using SX = typename StagedShape<LPR, WPR, CPW>::X;
+  __shared__ __attribute__((aligned(16))) uint32_t xbuf[StagedShape<LPR, WPR, CPW>::XT * SX::STRIDE];
+  const int32_t *items = a.pairs + a.offsets[e];
+  SX xs{xbuf, a.x_q, a.row_bytes, items, n_items, (uint32_t)a.n_used, a.x_rows};
+  matvec_body<LPR, WPR, CPW, RG, true, false, SX, true>(a, blockIdx.x, a.expert_w[e], items,
+                                                        n_items, xs, a.expert_w2[e]);
 }
 
 // ---- generic fallback: one wave per (token, row), lanes stride over blocks.
@@ -346,38 +433,50 @@ __global__ __launch_bounds__(256) void generic_grouped_kernel(
 
 typedef void (*MatvecFn)(const MatvecArgs);
 
-template <int LPR, int WPR, int CPW, bool GROUPED, bool STORE_S>
-MatvecFn pick_rg(int rg) {
+template <int LPR, int WPR, int CPW, bool GROUPED, bool STORE_S, bool STAGED>
+MatvecFn pick_rg_x(int rg) {
   if constexpr (CPW == 1 || (CPW == 2 && WPR == 4)) {
-    if (rg >= 4) return matvec_kernel<LPR, WPR, CPW, 4, GROUPED, STORE_S>;
+    if (rg >= 4) return matvec_kernel<LPR, WPR, CPW, 4, GROUPED, STORE_S, STAGED>;
   }
   if constexpr (CPW <= 2) {
-    if (rg >= 2) return matvec_kernel<LPR, WPR, CPW, 2, GROUPED, STORE_S>;
+    if (rg >= 2) return matvec_kernel<LPR, WPR, CPW, 2, GROUPED, STORE_S, STAGED>;
   }
-  return matvec_kernel<LPR, WPR, CPW, 1, GROUPED, STORE_S>;
+  return matvec_kernel<LPR, WPR, CPW, 1, GROUPED, STORE_S, STAGED>;
+}
+
+// Grouped launches always stage their x rows; plain ones stage them from two
+// tokens up (the `staged` argument).
+template <int LPR, int WPR, int CPW, bool GROUPED, bool STORE_S>
+MatvecFn pick_rg(int rg, bool staged) {
+  if constexpr (GROUPED) {
+    return pick_rg_x<LPR, WPR, CPW, true, STORE_S, true>(rg);
+  } else {
+    return staged ? pick_rg_x<LPR, WPR, CPW, false, STORE_S, true>(rg)
+                  : pick_rg_x<LPR, WPR, CPW, false, STORE_S, false>(rg);
+  }
 }
 
 template <bool GROUPED, bool STORE_S>
-MatvecFn pick_kernel(const MatvecShape &sh, int rg) {
+MatvecFn pick_kernel(const MatvecShape &sh, int rg, bool staged) {
   switch (sh.lanes_per_row) {
-    case 1: return pick_rg<1, 1, 1, GROUPED, STORE_S>(rg);
-    case 2: return pick_rg<2, 1, 1, GROUPED, STORE_S>(rg);
-    case 4: return pick_rg<4, 1, 1, GROUPED, STORE_S>(rg);
-    case 8: return pick_rg<8, 1, 1, GROUPED, STORE_S>(rg);
-    case 16: return pick_rg<16, 1, 1, GROUPED, STORE_S>(rg);
-    case 32: return pick_rg<32, 1, 1, GROUPED, STORE_S>(rg);
+    case 1: return pick_rg<1, 1, 1, GROUPED, STORE_S>(rg, staged);
+    case 2: return pick_rg<2, 1, 1, GROUPED, STORE_S>(rg, staged);
+    case 4: return pick_rg<4, 1, 1, GROUPED, STORE_S>(rg, staged);
+    case 8: return pick_rg<8, 1, 1, GROUPED, STORE_S>(rg, staged);
+    case 16: return pick_rg<16, 1, 1, GROUPED, STORE_S>(rg, staged);
+    case 32: return pick_rg<32, 1, 1, GROUPED, STORE_S>(rg, staged);
     default: break;
   }
   const int key = sh.waves_per_row * 10 + sh.chunks_per_wave;
   switch (key) {
-    case 11: return pick_rg<64, 1, 1, GROUPED, STORE_S>(rg);
-    case 13: return pick_rg<64, 1, 3, GROUPED, STORE_S>(rg);
-    case 21: return pick_rg<64, 2, 1, GROUPED, STORE_S>(rg);
-    case 22: return pick_rg<64, 2, 2, GROUPED, STORE_S>(rg);
-    case 41: return pick_rg<64, 4, 1, GROUPED, STORE_S>(rg);
-    case 42: return pick_rg<64, 4, 2, GROUPED, STORE_S>(rg);
-    case 43: return pick_rg<64, 4, 3, GROUPED, STORE_S>(rg);
-    case 44: return pick_rg<64, 4, 4, GROUPED, STORE_S>(rg);
+    case 11: return pick_rg<64, 1, 1, GROUPED, STORE_S>(rg, staged);
+    case 13: return pick_rg<64, 1, 3, GROUPED, STORE_S>(rg, staged);
+    case 21: return pick_rg<64, 2, 1, GROUPED, STORE_S>(rg, staged);
+    case 22: return pick_rg<64, 2, 2, GROUPED, STORE_S>(rg, staged);
+    case 41: return pick_rg<64, 4, 1, GROUPED, STORE_S>(rg, staged);
+    case 42: return pick_rg<64, 4, 2, GROUPED, STORE_S>(rg, staged);
+    case 43: return pick_rg<64, 4, 3, GROUPED, STORE_S>(rg, staged);
+    case 44: return pick_rg<64, 4, 4, GROUPED, STORE_S>(rg, staged);
     default: return nullptr;
   }
 }
@@ -557,7 +656,9 @@ hipError_t launch_matvec(float *out, int32_t *blocksums, const void *w, int64_t 
   MatvecShape sh;
   if (!matvec_shape(in_dim, &sh)) return hipErrorInvalidValue;
   const int rg = choose_rg(sh, out_dim, 1);
-  MatvecFn fn = blocksums ? pick_kernel<false, true>(sh, rg) : pick_kernel<false, false>(sh, rg);
+  const bool staged = n_tok >= 2;
+  MatvecFn fn = blocksums ? pick_kernel<false, true>(sh, rg, staged)
+                          : pick_kernel<false, false>(sh, rg, staged);
   if (!fn) return hipErrorInvalidValue;
   MatvecArgs a{};
   a.out = out;
@@ -581,7 +682,7 @@ hipError_t launch_matvec_grouped(float *out, int32_t *blocksums, const void *con
   MatvecShape sh;
   if (!matvec_shape(in_dim, &sh)) return hipErrorInvalidValue;
   const int rg = choose_rg(sh, out_dim, n_expert);
-  MatvecFn fn = blocksums ? pick_kernel<true, true>(sh, rg) : pick_kernel<true, false>(sh, rg);
+  MatvecFn fn = blocksums ? pick_kernel<true, true>(sh, rg, true) : pick_kernel<true, false>(sh, rg, true);
   if (!fn) return hipErrorInvalidValue;
   MatvecArgs a{};
   a.out = out;

@@ -69,6 +69,26 @@ def test_matvec_shapes(in_dim):
     _run_and_check(wq, xq, wq_o, xq_o, in_dim, out_dim, n_tok, 1, where="generic")
 
 
+@pytest.mark.parametrize("n_tok", [1, 2, 5, 17, 33])
+@pytest.mark.parametrize("in_dim", [256, 1024, 4096, 16384])
+def test_matvec_token_counts(in_dim, n_tok):
+    # From two tokens up the x rows go through LDS a bounded number at a time
+    # (16 rows of 256 or 1024 values, 4 of 4096, 1 of 16384): these counts
+    # cross those boundaries.
+    out_dim = 45
+    w = workloads.normal((out_dim, in_dim), 0.02, "cuda", "mvt", in_dim, "w")
+    x = workloads.normal((n_tok, in_dim), 1.0, "cuda", "mvt", in_dim, n_tok, "x")
+    wq, xq, wq_o, xq_o = _prep(w, x)
+    got = _run_and_check(wq, xq, wq_o, xq_o, in_dim, out_dim, n_tok, 2, where="matvec tokens")
+    # The product entry point (no block sums) on the same inputs.
+    q8 = _q8()
+    if q8.q8_0_matmul_plan(in_dim, out_dim, n_tok, 0)[0] == 2:
+        prod = q8.q8_0_matmul(wq, xq, in_dim, out_dim, n_tok,
+                              workspace=torch.empty(1, dtype=torch.uint8, device="cuda"))
+        torch.cuda.synchronize()
+        assert torch.equal(prod.view(torch.int32), got.view(torch.int32))
+
+
 @pytest.mark.parametrize("in_dim", [32, 96, 160, 3072, 4160])
 def test_generic_only_shapes(in_dim):
     q8 = _q8()
