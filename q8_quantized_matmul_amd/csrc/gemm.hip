@@ -554,6 +554,20 @@ __device__ __forceinline__ i32x4 t4_prep(const T4Raw &r, int h, uint32_t &scale)
   }
 }
 
+// Direct global->LDS dword copy through a buffer resource: a 32-bit lane
+// offset and a scalar offset, so the copy needs no 64-bit address per lane.
+typedef int32_t rsrc_t __attribute__((ext_vector_type(4)));
+__device__ void buffer_load_lds_raw(rsrc_t rsrc, __attribute__((address_space(3))) uint32_t *lds,
+                                    int size, int voffset, int soffset, int offset,
+                                    int aux) __asm("llvm.amdgcn.raw.buffer.load.lds");
+
+// Raw buffer resource over [base, base + bytes): stride 0, 32-bit dword format.
+__device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+  const uint64_t b = reinterpret_cast<uint64_t>(base);
+  return rsrc_t{(int32_t)(uint32_t)b, (int32_t)(uint32_t)(b >> 32) & 0xFFFF, (int32_t)bytes,
+                0x00020000};
+}
+
 __global__ __launch_bounds__(256, 2) void gemm_t4_kernel(const GemmArgs a) {
   using namespace t4;
   __shared__ __attribute__((aligned(16))) uint8_t ring[2 * STAGE];
@@ -579,14 +593,22 @@ __global__ __launch_bounds__(256, 2) void gemm_t4_kernel(const GemmArgs a) {
     const int r = f / RD;
     off[k] = (uint32_t)(r * (int)a.row_bytes + 4 * (f - r * RD));
   }
+  // The wave's 64 rows as one buffer (64 * row_bytes <= 2^30: the launcher
+  // takes this kernel only for rows of at most 2^24 bytes); the row-group
+  // and stage offsets go in the scalar offset.
   const uint8_t *copy_base = wave < 2 ? a.x_q + (t_tile + 64 * wave) * a.row_bytes
                                       : a.w + (o_tile + 64 * (wave - 2)) * a.row_bytes;
+  const rsrc_t rsrc = make_rsrc(copy_base, (uint32_t)(64 * a.row_bytes));
+  const int half_rows = (int)(32 * a.row_bytes);
   auto issue = [&](int64_t b0, int buf) {
-    uint8_t *lds = ring + buf * STAGE + wave * WAVE_BYTES;
+    const uint32_t lds = (uint32_t)reinterpret_cast<uintptr_t>(ring + buf * STAGE + wave * WAVE_BYTES);
+    const int sb = (int)(b0 * kBlockBytes);
 #pragma unroll
     for (int k = 0; k < 2 * PERIOD; ++k) {
-      const uint8_t *g = copy_base + (k / PERIOD) * 32 * a.row_bytes + b0 * kBlockBytes;
-      __builtin_amdgcn_global_load_lds(g + off[k % PERIOD], lds + 256 * k, 4, 0, 0);
+      buffer_load_lds_raw(rsrc,
+                          reinterpret_cast<__attribute__((address_space(3))) uint32_t *>(
+                              (uintptr_t)(lds + 256 * k)),
+                          4, (int)off[k % PERIOD], sb + (k / PERIOD) * half_rows, 0, 0);
     }
   };
 
@@ -727,8 +749,11 @@ size_t gemm_workspace_bytes(int64_t out_dim, int64_t n_tok, int split) {
 static bool use_lds_kernel(int64_t nb, int64_t n_tok) { return nb % lds::KB == 0 && n_tok > 64; }
 
 // The four-tile kernel takes whole 128 x 128 tiles and 4-block stages.
+// Its copies address a wave's 64 rows with 32-bit buffer offsets, so rows
+// are limited to 2^24 bytes.
 static bool use_t4_kernel(int64_t nb, int64_t out_dim, int64_t n_tok) {
-  return nb % t4::KB == 0 && out_dim % t4::BO == 0 && n_tok % t4::BT == 0;
+  return nb % t4::KB == 0 && out_dim % t4::BO == 0 && n_tok % t4::BT == 0 &&
+         nb * kBlockBytes <= (int64_t{1} << 24);
 }
 
 hipError_t launch_gemm(float *out, int32_t *blocksums, const void *w, int64_t in_dim,
