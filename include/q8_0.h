@@ -207,7 +207,7 @@ typedef struct q8_0_matmul_item {
  * For each item: if x is set, x_q_i = q8_0_quantize_act(x); then
  * out = q8_0_matmul(w, x_q_i) with no workspace.  Every output and every
  * x_q byte is bit-identical to those separate calls.
- * Items on the weight-streaming path (n_tok < 16) share one launch.  An item
+ * Items on the weight-streaming path with n_tok < 16 share one launch.  An item
  * with x set whose in_dim is one of 64, 128, ..., 4096 with n_tok * in_dim <=
  * 4096 (and x 16-byte, x_q 4-byte aligned) is quantized inside that launch,
  * so a list of such decode projections is a single kernel launch; x_q may

@@ -12,7 +12,13 @@
 
 namespace {
 
-constexpr int64_t kMatmulMfmaMinTokens = 16;  // matrix units from 16 tokens on
+// Matrix units from 32 tokens on: below that the weight-streaming matvec is
+// faster for every measured shape (4096->2048, 2048->4096, 4096->1024 up to
+// 32 tokens, 1024->32768 up to 24).
+constexpr int64_t kMatmulMfmaMinTokens = 32;
+// The shared list launch reads each token's x row per wave from global
+// memory; from 16 tokens an item runs as its own (LDS-staged) matvec launch.
+constexpr int64_t kListMaxTokens = 15;
 constexpr int32_t kMaxExperts = 8192;
 constexpr int kMaxDevices = 64;
 
@@ -231,7 +237,8 @@ int plan_list_item(const q8_0_matmul_item &it, int64_t n_tok, ListPlan *lp) {
     lp->prequant = true;
   }
   const Plan p = make_plan(it.in_dim, it.out_dim, n_tok, 0, w4 && aligned(it.x_q, 4));
-  lp->in_list = p.variant == Q8_0_KERNEL_MATVEC && q8::list_item_ok(it.in_dim);
+  lp->in_list = p.variant == Q8_0_KERNEL_MATVEC && q8::list_item_ok(it.in_dim) &&
+                n_tok <= kListMaxTokens;
   return Q8_0_OK;
 }
 

@@ -735,7 +735,7 @@ int gemm_auto_split(int64_t in_dim, int64_t out_dim, int64_t n_tok) {
   const int64_t nb = in_dim / kBlockElems;
   const int tj = gemm_tj(n_tok);
   const int64_t tiles = ((out_dim + 127) / 128) * ((n_tok + 64 * tj - 1) / (64 * tj));
-  int64_t split = (512 + tiles - 1) / tiles;           // aim for >= 512 workgroups
+  int64_t split = (256 + tiles - 1) / tiles;           // aim for >= 256 workgroups
   split = std::max<int64_t>(split, (nb + 127) / 128);  // fp32 chains of <= 128 blocks
   split = std::min<int64_t>(split, nb / (2 * kStageBlocks));
   split = std::min<int64_t>(split, 16);

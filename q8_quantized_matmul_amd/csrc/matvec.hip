@@ -294,12 +294,11 @@ __device__ __forceinline__ void matvec_body(const MatvecArgs &a, int64_t tile, c
     for (int m = 0; m < NM; ++m) {
 #pragma unroll
       for (int g = 0; g < RG; ++g) {
-#pragma unroll
-        for (int k = LPR / 2; k >= 1; k >>= 1) acc[m][g] += __shfl_xor(acc[m][g], k, 64);
+        acc[m][g] = group_sum<LPR>(acc[m][g]);
       }
     }
     if constexpr (WPR > 1) {
-      if (lane == 0) {
+      if (group_sum_lane<64>(lane)) {
 #pragma unroll
         for (int m = 0; m < NM; ++m)
 #pragma unroll
@@ -320,7 +319,7 @@ __device__ __forceinline__ void matvec_body(const MatvecArgs &a, int64_t tile, c
       }
       __syncthreads();
     }
-    if (part == 0 && (lane % LPR) == 0) {
+    if (part == 0 && group_sum_lane<LPR>(lane)) {
 #pragma unroll
       for (int g = 0; g < RG; ++g) {
         const int64_t row = row0 + g * RPW;

@@ -117,6 +117,9 @@ constexpr int kDppXor1 = 0xB1;
 constexpr int kDppXor2 = 0x4E;
 constexpr int kDppHalfMirror = 0x141;
 constexpr int kDppNext = 0x101;
+constexpr int kDppMirror = 0x140;    // lane 15-i of the same 16-lane row
+constexpr int kDppBcast15 = 0x142;   // lane 15 of the previous row
+constexpr int kDppBcast31 = 0x143;   // lane 31, to rows 2 and 3
 
 template <int CTRL>
 __device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
@@ -125,6 +128,33 @@ __device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
 template <int CTRL>
 __device__ __forceinline__ float dpp_f32(float v) {
   return __builtin_bit_cast(float, dpp_u32<CTRL>(__builtin_bit_cast(uint32_t, v)));
+}
+
+// Sum over aligned groups of N lanes (N a power of two <= 64) with DPP adds:
+// a butterfly over lanes within 16-lane rows, then row broadcasts.  Every
+// level adds two equal-size partial sums, so the result has the same value
+// as a xor-shuffle butterfly.  For N <= 16 every lane of a group holds the
+// sum; for N = 32 the lanes 16..31 of the group; for N = 64 the lanes
+// 48..63 (group_sum_lane gives one of them).
+template <int N>
+__device__ __forceinline__ float group_sum(float v) {
+  if constexpr (N >= 2) v += dpp_f32<kDppXor1>(v);
+  if constexpr (N >= 4) v += dpp_f32<kDppXor2>(v);
+  if constexpr (N >= 8) v += dpp_f32<kDppHalfMirror>(v);
+  if constexpr (N >= 16) v += dpp_f32<kDppMirror>(v);
+  if constexpr (N >= 32) {
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                                       0, __builtin_bit_cast(int, v), kDppBcast15, 0xA, 0xF, false));
+  }
+  if constexpr (N >= 64) {
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                                       0, __builtin_bit_cast(int, v), kDppBcast31, 0xC, 0xF, false));
+  }
+  return v;
+}
+template <int N>
+__device__ __forceinline__ bool group_sum_lane(int lane) {
+  return N <= 16 ? (lane % N) == 0 : (lane % N) == N - 1;
 }
 
 // Lanes 16j..16j+15 of the wave hold one pair of 64 values, lane sub = lane &

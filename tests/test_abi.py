@@ -158,9 +158,12 @@ def test_plan_regimes(q8):
     # Decode shapes stream weights through the matvec kernel.
     assert q8.q8_0_matmul_plan(1024, 32768, 1, 0) == (q8.KERNEL_MATVEC, 1)
     assert q8.q8_0_matmul_plan(32768, 1024, 1, 0) == (q8.KERNEL_MATVEC, 1)
-    assert q8.q8_0_matmul_plan(4096, 2048, 15, 0) == (q8.KERNEL_MATVEC, 1)
-    # From 16 tokens on the matrix-core GEMM.
-    assert q8.q8_0_matmul_plan(4096, 2048, 16, 1 << 40)[0] == q8.KERNEL_MFMA
+    assert q8.q8_0_matmul_plan(4096, 2048, 31, 0) == (q8.KERNEL_MATVEC, 1)
+    # From 32 tokens on the matrix-core GEMM.
+    assert q8.q8_0_matmul_plan(4096, 2048, 32, 1 << 40)[0] == q8.KERNEL_MFMA
+    # Split-K aims for 256 workgroups: 256 output tiles need none.
+    assert q8.q8_0_matmul_plan(1024, 32768, 64, 1 << 40) == (q8.KERNEL_MFMA, 1)
+    assert q8.q8_0_matmul_plan(4096, 2048, 64, 1 << 40) == (q8.KERNEL_MFMA, 16)
     assert q8.q8_0_matmul_plan(4096, 2048, 4096, 1 << 40) == (q8.KERNEL_MFMA, 1)
     v, s = q8.q8_0_matmul_plan(32768, 1024, 2048, 1 << 40)
     assert v == q8.KERNEL_MFMA and s == 8

@@ -117,10 +117,11 @@ def test_list_mixed_paths():
     _run(specs, 3, "mixed")
 
 
-@pytest.mark.parametrize("n_tok", [2, 4, 5, 15, 20])
+@pytest.mark.parametrize("n_tok", [2, 4, 5, 15, 20, 40])
 def test_list_token_counts(n_tok):
     # n_tok * 16 pairs <= 64 fuses; 5 and 15 tokens pre-quantize; 20 tokens
-    # leave the weight-streaming path (matrix-core GEMM, outside the list).
+    # run as separate staged matvec launches; 40 leave the weight-streaming
+    # path (matrix-core GEMM, outside the list).
     specs = [dict(in_dim=1024, out_dim=300, mode="x+xq"),
              dict(in_dim=256, out_dim=129, mode="x+xq"),
              dict(in_dim=4096, out_dim=64, mode="xq")]

@@ -126,10 +126,11 @@ def _run_outputs(wq, xq, wq_o, xq_o, in_dim, out_dim, n_tok, split, where):
 
 
 @pytest.mark.parametrize("out_dim,n_tok,in_dim,split", [
-    (256, 256, 512, 1), (384, 128, 1152, 3), (128, 384, 4096, 1), (256, 128, 2048, 4)])
+    (256, 256, 512, 1), (384, 128, 1152, 3), (128, 384, 4096, 1), (256, 128, 2048, 4),
+    (512, 128, 128, 1), (768, 256, 384, 1), (1024, 128, 640, 1), (256, 256, 1024, 2)])
 def test_mfma_whole_tiles(out_dim, n_tok, in_dim, split):
-    # Whole 128 x 128 tiles with 4-block stages: the four-tile kernel, also
-    # with split-K.
+    # Whole 128 x 128 tiles with 4-block stages: the four-tile kernel, with
+    # one to five stages per split, also with split-K.
     w = workloads.normal((out_dim, in_dim), 0.02, "cuda", "mf4", out_dim, in_dim, "w")
     x = workloads.normal((n_tok, in_dim), 1.0, "cuda", "mf4", n_tok, in_dim, "x")
     x[5, 100:110] *= 40.0  # outlier block
@@ -165,13 +166,14 @@ def _unit_scale_blocks(rows, nb, seed, only_block=None):
 
 @pytest.mark.parametrize("only_block", [None, 0, 1, 2, 3, 5, 14])
 @pytest.mark.parametrize("split", [1, 2])
-def test_mfma_whole_tiles_exact_integer_sums(only_block, split):
+@pytest.mark.parametrize("out_dim", [256, 128])
+def test_mfma_whole_tiles_exact_integer_sums(only_block, split, out_dim):
     # With unit scales every term is an integer and every partial sum stays
     # below 2^24, so the fp32 output must equal the exact sum of the block
     # dots; with one nonzero block it is that block's S_b.  This pins the
     # integer path of the four-tile kernel (which has no block-sum output)
     # bit-exactly, block by block across stage positions and stages.
-    in_dim, out_dim, n_tok = 512, 256, 128
+    in_dim, n_tok = 512, 128
     nb = in_dim // 32
     w_b = _unit_scale_blocks(out_dim, nb, 11, only_block)
     x_b = _unit_scale_blocks(n_tok, nb, 12, only_block)
