@@ -81,27 +81,31 @@ struct GlobalX {
 // instruction; wave w copies the rows w, w+4, ...).  The copies of the first
 // XT rows are issued before the weight loads, so their latency hides under
 // the weight stream, and every wave then reads its pairs from LDS instead of
-// issuing per-item global loads.  ROW_DW = dwords of one x_q row; rows sit at
-// a stride rounded up to 64 dwords, the lanes past a row's end re-read its
-// last dword into the padding.
+// issuing per-item global loads.  With more than XT items two buffers
+// alternate: the next XT rows are copied while the current ones are used.
+// ROW_DW = dwords of one x_q row; rows sit at a stride rounded up to 64
+// dwords, the lanes past a row's end re-read its last dword into the padding.
 template <int ROW_DW, int XT>
 struct StagedX {
   static constexpr int STRIDE = (ROW_DW + 63) / 64 * 64;
   static constexpr int NI = STRIDE / 64;
-  uint32_t *lds;             // XT * STRIDE dwords
+  static constexpr int BUF = XT * STRIDE;  // dwords per buffer
+  uint32_t *lds;             // 2 * BUF dwords
   const uint8_t *x_q;
   int64_t row_bytes;
   const int32_t *items;      // grouped: pair ids; null: item i is x row i
   int64_t n_items;
   uint32_t n_used;
   int32_t x_rows;
-  int64_t base = 0;          // first item held in LDS
+  int64_t base = 0;          // first item of the rows being read
+  int cur = 0;               // buffer holding them
 
-  __device__ __forceinline__ void stage(int64_t first) {
-    base = first;
+  // Issue the copies of items [first, first + XT) into buffer `buf`.
+  __device__ __forceinline__ void stage(int64_t first, int buf) {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     const int rows = (int)min((int64_t)XT, n_items - first);
+    uint32_t *dst = lds + buf * BUF;
     for (int t = wave; t < rows; t += 4) {
       int64_t xrow = first + t;
       if (items) {
@@ -112,32 +116,37 @@ struct StagedX {
 #pragma unroll
       for (int k = 0; k < NI; ++k) {
         const int d = min(64 * k + lane, ROW_DW - 1);
-        __builtin_amdgcn_global_load_lds(src + 4 * d, lds + t * STRIDE + 64 * k, 4, 0, 0);
+        __builtin_amdgcn_global_load_lds(src + 4 * d, dst + t * STRIDE + 64 * k, 4, 0, 0);
       }
     }
   }
-  __device__ __forceinline__ void prefetch() { stage(0); }
+  __device__ __forceinline__ void prefetch() { stage(0, 0); }
+  // Wait for this wave's copies (and the weights) and then every wave's;
+  // then start the next rows, if any, into the other buffer.
   __device__ __forceinline__ void publish() {
-    __builtin_amdgcn_s_waitcnt(0);  // this wave's copies (and weights) have landed
-    __syncthreads();                // ... and every wave's copies
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (base + XT < n_items) stage(base + XT, cur ^ 1);
   }
-  // Called at the top of item `it` (uniform across the workgroup).
+  // Called at the top of item `it` (uniform across the workgroup).  The
+  // barrier inside publish() also means every wave is done with the rows
+  // before, so their buffer can take the rows after next.
   __device__ __forceinline__ void advance(int64_t it) {
     if (it - base == XT) {
-      __syncthreads();  // every wave is done with the previous rows
-      stage(it);
+      base = it;
+      cur ^= 1;
       publish();
     }
   }
   __device__ __forceinline__ void load(int64_t it, int64_t, int64_t pair,
                                        uint32_t (&d)[kPairDwords]) const {
-    const uint32_t *b = lds + (int)(it - base) * STRIDE + (int)pair * kPairDwords;
+    const uint32_t *b = lds + cur * BUF + (int)(it - base) * STRIDE + (int)pair * kPairDwords;
 #pragma unroll
     for (int i = 0; i < kPairDwords; ++i) d[i] = b[i];
   }
 };
 
-// x rows staged per workgroup: as many as fit in about 20 KB of LDS, 1 to 16.
+// x rows per staging buffer: as many as fit in about 20 KB of LDS, 1 to 16.
 template <int LPR, int WPR, int CPW>
 struct StagedShape {
   static constexpr int ROW_DW = kPairDwords * (LPR < 64 ? LPR : 64 * WPR * CPW);
@@ -347,7 +356,7 @@ __global__ __launch_bounds__(256) void matvec_kernel(const MatvecArgs a) {
   }
   if constexpr (STAGED) {
     using SX = typename StagedShape<LPR, WPR, CPW>::X;
-    __shared__ __attribute__((aligned(16))) uint32_t xbuf[StagedShape<LPR, WPR, CPW>::XT * SX::STRIDE];
+    __shared__ __attribute__((aligned(16))) uint32_t xbuf[2 * SX::BUF];
     SX xs{xbuf, a.x_q, a.row_bytes, items, n_items, (uint32_t)a.n_used, a.x_rows};
     matvec_body<LPR, WPR, CPW, RG, GROUPED, STORE_S>(a, blockIdx.x, w, items, n_items, xs);
   } else {
@@ -364,7 +373,7 @@ __global__ __launch_bounds__(256) void matvec_pair_kernel(const MatvecArgs a) {
   const int64_t n_items = a.counts[e];
   if (n_items == 0) return;  // uniform across the workgroup
   using SX = typename StagedShape<LPR, WPR, CPW>::X;
-  __shared__ __attribute__((aligned(16))) uint32_t xbuf[StagedShape<LPR, WPR, CPW>::XT * SX::STRIDE];
+  __shared__ __attribute__((aligned(16))) uint32_t xbuf[2 * SX::BUF];
   const int32_t *items = a.pairs + a.offsets[e];
   SX xs{xbuf, a.x_q, a.row_bytes, items, n_items, (uint32_t)a.n_used, a.x_rows};
   matvec_body<LPR, WPR, CPW, RG, true, false, SX, true>(a, blockIdx.x, a.expert_w[e], items,
