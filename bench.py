@@ -261,7 +261,7 @@ def bench_moe(torch, q8, wl, steps, warmup):
     # One q8_0_moe_grouped call = routing kernel + grouped kernel; timed whole.
     gate_us = time_kernel(torch, gate, 1, reps=10)
     down_us = time_kernel(torch, down, 1, reps=10)
-    sh_us = time_kernel(torch, sh_gate, 1, reps=10)
+    sh_us = time_kernel(torch, sh_gate, 8, reps=5)
     # The routed FFN as one q8_0_moe_ffn call (route, gate+up with SwiGLU,
     # mid quantize, down, weighted combine) on the same x_q.
     route_w = torch.rand((T, kk), generator=torch.Generator().manual_seed(23)).cuda()

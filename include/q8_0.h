@@ -62,7 +62,8 @@ enum {
     Q8_0_KERNEL_AUTO = 0,
     Q8_0_KERNEL_GENERIC = 1, /* one block per lane, any shape           */
     Q8_0_KERNEL_MATVEC = 2,  /* weight-streaming matvec, small n_tok     */
-    Q8_0_KERNEL_MFMA = 3     /* int8 MFMA GEMM, large n_tok              */
+    Q8_0_KERNEL_MFMA = 3,    /* int8 MFMA GEMM, large n_tok              */
+    Q8_0_KERNEL_SKINNY = 4   /* int8 MFMA, weights streamed, n_tok <= 64 */
 };
 
 /* Quantize activations to Q8_0 ("Part 3: 模型架构", section 2 rule, per

@@ -30,6 +30,7 @@ KERNEL_AUTO = 0
 KERNEL_GENERIC = 1
 KERNEL_MATVEC = 2
 KERNEL_MFMA = 3
+KERNEL_SKINNY = 4
 
 
 class Q8Error(RuntimeError):

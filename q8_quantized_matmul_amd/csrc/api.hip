@@ -12,10 +12,11 @@
 
 namespace {
 
-// Matrix units from 32 tokens on: below that the weight-streaming matvec is
-// faster for every measured shape (4096->2048, 2048->4096, 4096->1024 up to
-// 32 tokens, 1024->32768 up to 24).
-constexpr int64_t kMatmulMfmaMinTokens = 32;
+// Regimes by token count (measured on 4096->2048, 2048->4096, 4096->1024 and
+// 1024->32768): the weight-streaming matvec below 20 tokens, the skinny
+// matrix-core kernel (weights streamed into MFMA registers) from 20 to 64,
+// the LDS-tiled GEMM above.
+constexpr int64_t kSkinnyMinTokens = 20;
 // The shared list launch reads each token's x row per wave from global
 // memory; from 16 tokens an item runs as its own (LDS-staged) matvec launch.
 constexpr int64_t kListMaxTokens = 15;
@@ -53,7 +54,12 @@ bool matvec_ok(int64_t in_dim) { return q8::matvec_shape(in_dim, nullptr); }
 Plan make_plan(int64_t in_dim, int64_t out_dim, int64_t n_tok, size_t ws_bytes, bool fast_align) {
   Plan p{Q8_0_KERNEL_GENERIC, 1};
   if (!fast_align) return p;
-  if (n_tok >= kMatmulMfmaMinTokens && q8::gemm_supported(in_dim)) {
+  if (n_tok >= kSkinnyMinTokens && q8::skinny_supported(in_dim, n_tok)) {
+    p.variant = Q8_0_KERNEL_SKINNY;
+    int split = q8::skinny_auto_split(in_dim, out_dim);
+    while (split > 1 && q8::skinny_workspace_bytes(out_dim, n_tok, split) > ws_bytes) --split;
+    p.split = split;
+  } else if (n_tok > q8::kSkinnyMaxTokens && q8::gemm_supported(in_dim)) {
     p.variant = Q8_0_KERNEL_MFMA;
     int split = q8::gemm_auto_split(in_dim, out_dim, n_tok);
     while (split > 1 && q8::gemm_workspace_bytes(out_dim, n_tok, split) > ws_bytes) --split;
@@ -82,28 +88,39 @@ int run_matmul(float *out, int32_t *blocksums, const void *w, int64_t in_dim, in
   if (st != Q8_0_OK || n_tok == 0 || out_dim == 0) return st;
   if (workspace == nullptr) workspace_bytes = 0;
   if (workspace && !aligned(workspace, 16)) return Q8_0_EALIGN;
-  if (split_k < 0 || variant < 0 || variant > Q8_0_KERNEL_MFMA) return Q8_0_EINVAL;
+  if (split_k < 0 || variant < 0 || variant > Q8_0_KERNEL_SKINNY) return Q8_0_EINVAL;
   const bool fast_align = aligned(w, 4) && aligned(x_q, 4);
   Plan p = make_plan(in_dim, out_dim, n_tok, workspace_bytes, fast_align);
   if (variant != Q8_0_KERNEL_AUTO) {
     if (variant != Q8_0_KERNEL_GENERIC && !fast_align) return Q8_0_EINVAL;
     if (variant == Q8_0_KERNEL_MATVEC && !matvec_ok(in_dim)) return Q8_0_EINVAL;
     if (variant == Q8_0_KERNEL_MFMA && !q8::gemm_supported(in_dim)) return Q8_0_EINVAL;
+    if (variant == Q8_0_KERNEL_SKINNY && (!q8::skinny_supported(in_dim, n_tok) || blocksums))
+      return Q8_0_EINVAL;
     if (variant != p.variant) p.split = 1;
     p.variant = variant;
   }
   if (split_k > 0) {
-    if (p.variant != Q8_0_KERNEL_MFMA && split_k != 1) return Q8_0_EINVAL;
+    if (p.variant != Q8_0_KERNEL_MFMA && p.variant != Q8_0_KERNEL_SKINNY && split_k != 1)
+      return Q8_0_EINVAL;
     p.split = split_k;
   }
+  // A block-sum debug call takes the GEMM where the plan chose the skinny kernel.
+  if (blocksums && p.variant == Q8_0_KERNEL_SKINNY) p.variant = Q8_0_KERNEL_MFMA;
   if (p.variant == Q8_0_KERNEL_MFMA && p.split > 1 &&
       q8::gemm_workspace_bytes(out_dim, n_tok, p.split) > workspace_bytes)
+    return Q8_0_EWORKSPACE;
+  if (p.variant == Q8_0_KERNEL_SKINNY && p.split > 1 &&
+      q8::skinny_workspace_bytes(out_dim, n_tok, p.split) > workspace_bytes)
     return Q8_0_EWORKSPACE;
   if ((st = check_device()) != Q8_0_OK) return st;
   switch (p.variant) {
     case Q8_0_KERNEL_MFMA:
       return status_of(q8::launch_gemm(out, blocksums, w, in_dim, out_dim, x_q, n_tok, p.split,
                                        static_cast<float *>(workspace), stream));
+    case Q8_0_KERNEL_SKINNY:
+      return status_of(q8::launch_skinny(out, w, in_dim, out_dim, x_q, n_tok, p.split,
+                                         static_cast<float *>(workspace), stream));
     case Q8_0_KERNEL_MATVEC:
       return status_of(q8::launch_matvec(out, blocksums, w, in_dim, out_dim, x_q, n_tok, stream));
     default:
@@ -298,6 +315,7 @@ int q8_0_quantize_act(void *x_q, const float *x, int64_t n_tok, int64_t in_dim,
 size_t q8_0_matmul_workspace_bytes(int64_t in_dim, int64_t out_dim, int64_t n_tok) {
   if (in_dim <= 0 || out_dim <= 0 || n_tok <= 0 || in_dim % Q8_0_BLOCK_ELEMS != 0) return 0;
   Plan p = make_plan(in_dim, out_dim, n_tok, SIZE_MAX, true);
+  if (p.variant == Q8_0_KERNEL_SKINNY) return q8::skinny_workspace_bytes(out_dim, n_tok, p.split);
   return p.variant == Q8_0_KERNEL_MFMA ? q8::gemm_workspace_bytes(out_dim, n_tok, p.split) : 0;
 }
 

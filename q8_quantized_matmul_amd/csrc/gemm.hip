@@ -803,9 +803,13 @@ hipError_t launch_gemm(float *out, int32_t *blocksums, const void *w, int64_t in
   }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || n_split == 1) return err;
-  const int64_t n = n_tok * out_dim;
+  return launch_splitk_reduce(out, partials, n_tok * out_dim, (int)n_split, s);
+}
+
+hipError_t launch_splitk_reduce(float *out, const float *partials, int64_t n, int n_split,
+                                hipStream_t s) {
   hipLaunchKernelGGL(splitk_reduce_kernel, dim3((uint32_t)((n + 255) / 256)), dim3(256), 0, s, out,
-                     partials, n, (int)n_split);
+                     partials, n, n_split);
   return hipGetLastError();
 }
 

@@ -83,6 +83,16 @@ hipError_t launch_moe(float *out, int32_t *blocksums, const void *const *expert_
                       int32_t x_rows, int64_t n_tok, int32_t *workspace, bool fast,
                       hipStream_t s);
 
+// skinny.hip: matrix-core matmul for up to kSkinnyMaxTokens tokens, weights
+// streamed into registers, split-K through caller partials.
+constexpr int64_t kSkinnyMaxTokens = 64;
+bool skinny_supported(int64_t in_dim, int64_t n_tok);
+int skinny_auto_split(int64_t in_dim, int64_t out_dim);
+size_t skinny_workspace_bytes(int64_t out_dim, int64_t n_tok, int split);
+hipError_t launch_skinny(float *out, const void *w, int64_t in_dim, int64_t out_dim,
+                         const void *x_q, int64_t n_tok, int split, float *partials,
+                         hipStream_t s);
+
 // gemm.hip: int8 MFMA GEMM with per-block scales.
 bool gemm_supported(int64_t in_dim);
 int gemm_auto_split(int64_t in_dim, int64_t out_dim, int64_t n_tok);
@@ -90,5 +100,8 @@ size_t gemm_workspace_bytes(int64_t out_dim, int64_t n_tok, int split);
 hipError_t launch_gemm(float *out, int32_t *blocksums, const void *w, int64_t in_dim,
                        int64_t out_dim, const void *x_q, int64_t n_tok, int split,
                        float *partials, hipStream_t s);
+// out[i] = sum over s = 0..n_split-1, in order, of partials[s * n + i].
+hipError_t launch_splitk_reduce(float *out, const float *partials, int64_t n, int n_split,
+                                hipStream_t s);
 
 }  // namespace q8

@@ -158,12 +158,18 @@ def test_plan_regimes(q8):
     # Decode shapes stream weights through the matvec kernel.
     assert q8.q8_0_matmul_plan(1024, 32768, 1, 0) == (q8.KERNEL_MATVEC, 1)
     assert q8.q8_0_matmul_plan(32768, 1024, 1, 0) == (q8.KERNEL_MATVEC, 1)
-    assert q8.q8_0_matmul_plan(4096, 2048, 31, 0) == (q8.KERNEL_MATVEC, 1)
-    # From 32 tokens on the matrix-core GEMM.
-    assert q8.q8_0_matmul_plan(4096, 2048, 32, 1 << 40)[0] == q8.KERNEL_MFMA
-    # Split-K aims for 256 workgroups: 256 output tiles need none.
-    assert q8.q8_0_matmul_plan(1024, 32768, 64, 1 << 40) == (q8.KERNEL_MFMA, 1)
-    assert q8.q8_0_matmul_plan(4096, 2048, 64, 1 << 40) == (q8.KERNEL_MFMA, 16)
+    assert q8.q8_0_matmul_plan(4096, 2048, 19, 0) == (q8.KERNEL_MATVEC, 1)
+    # From 20 to 64 tokens the skinny matrix-core kernel, split for about
+    # 256 workgroups of 32 rows (at least one block pair per wave).
+    assert q8.q8_0_matmul_plan(4096, 2048, 20, 1 << 40) == (q8.KERNEL_SKINNY, 4)
+    assert q8.q8_0_matmul_plan(4096, 2048, 64, 1 << 40) == (q8.KERNEL_SKINNY, 4)
+    assert q8.q8_0_matmul_plan(4096, 2048, 64, 0) == (q8.KERNEL_SKINNY, 1)
+    assert q8.q8_0_matmul_plan(1024, 32768, 64, 1 << 40) == (q8.KERNEL_SKINNY, 1)
+    assert q8.q8_0_matmul_plan(4096, 256, 48, 1 << 40) == (q8.KERNEL_SKINNY, 16)
+    assert q8.q8_0_matmul_workspace_bytes(4096, 2048, 64) == 4 * 2048 * 64 * 4
+    # Above 64 tokens the tiled GEMM; split-K aims for 256 workgroups.
+    assert q8.q8_0_matmul_plan(4096, 2048, 65, 1 << 40)[0] == q8.KERNEL_MFMA
+    assert q8.q8_0_matmul_plan(1024, 32768, 128, 1 << 40) == (q8.KERNEL_MFMA, 1)
     assert q8.q8_0_matmul_plan(4096, 2048, 4096, 1 << 40) == (q8.KERNEL_MFMA, 1)
     v, s = q8.q8_0_matmul_plan(32768, 1024, 2048, 1 << 40)
     assert v == q8.KERNEL_MFMA and s == 8

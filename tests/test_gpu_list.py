@@ -117,11 +117,12 @@ def test_list_mixed_paths():
     _run(specs, 3, "mixed")
 
 
-@pytest.mark.parametrize("n_tok", [2, 4, 5, 15, 20, 40])
+@pytest.mark.parametrize("n_tok", [2, 4, 5, 15, 17, 40, 80])
 def test_list_token_counts(n_tok):
-    # n_tok * 16 pairs <= 64 fuses; 5 and 15 tokens pre-quantize; 20 tokens
-    # run as separate staged matvec launches; 40 leave the weight-streaming
-    # path (matrix-core GEMM, outside the list).
+    # n_tok * 16 pairs <= 64 fuses; 5 and 15 tokens pre-quantize; 17 tokens
+    # run as separate staged matvec launches; 40 and 80 leave the
+    # weight-streaming path (skinny and tiled matrix-core kernels, outside
+    # the list).
     specs = [dict(in_dim=1024, out_dim=300, mode="x+xq"),
              dict(in_dim=256, out_dim=129, mode="x+xq"),
              dict(in_dim=4096, out_dim=64, mode="xq")]

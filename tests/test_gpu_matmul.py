@@ -89,6 +89,67 @@ def test_matvec_token_counts(in_dim, n_tok):
         assert torch.equal(prod.view(torch.int32), got.view(torch.int32))
 
 
+def _run_skinny(wq, xq, wq_o, xq_o, in_dim, out_dim, n_tok, split, where):
+    q8 = _q8()
+    say(f"[matmul] {where} in={in_dim} out={out_dim} n_tok={n_tok} skinny split={split}")
+    out = torch.full((n_tok, out_dim), float("nan"), device="cuda")
+    ws = torch.empty(max(4 * split * out_dim * n_tok, 1), dtype=torch.uint8, device="cuda")
+    got, _ = q8.q8_0_matmul_debug(wq, xq, in_dim, out_dim, n_tok, variant=q8.KERNEL_SKINNY,
+                                  split_k=split, blocksums=False, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    ref, mag, _ = oracle.matmul(wq_o, xq_o, in_dim)
+    got = got.cpu().numpy()
+    assert_close(got, ref, mag, where)
+    return got, ref
+
+
+@pytest.mark.parametrize("in_dim,out_dim,n_tok,split", [
+    (4096, 2048, 64, 4), (4096, 2048, 32, 4), (2048, 4096, 33, 2), (4096, 1000, 40, 1),
+    (1024, 300, 17, 2), (64, 50, 64, 1), (192, 65, 31, 1), (128, 33, 5, 1), (4096, 64, 48, 16),
+    (1024, 32768, 64, 1), (8192, 96, 1, 3)])
+def test_skinny_shapes(in_dim, out_dim, n_tok, split):
+    # Ragged rows and token counts, one or two token tiles, waves with no
+    # block pair (192 values = 3 pairs), and split-K with uneven splits.
+    w = workloads.normal((out_dim, in_dim), 0.02, "cuda", "sk", out_dim, in_dim, "w")
+    x = workloads.normal((n_tok, in_dim), 1.0, "cuda", "sk", n_tok, in_dim, "x")
+    x[min(3, n_tok - 1), 40:50] *= 30.0  # outlier block
+    wq, xq, wq_o, xq_o = _prep(w, x)
+    _run_skinny(wq, xq, wq_o, xq_o, in_dim, out_dim, n_tok, split, "skinny")
+
+
+@pytest.mark.parametrize("only_block", [None, 0, 1, 2, 3, 6, 7])
+@pytest.mark.parametrize("n_tok", [64, 20])
+def test_skinny_exact_integer_sums(only_block, n_tok):
+    # Unit scales: every output is the exact integer sum of the block dots
+    # (below 2^24), and with one nonzero block it is that block's S_b; this
+    # pins both halves of the even (re-aligned) and odd blocks of a pair, in
+    # every wave and across two splits.
+    in_dim, out_dim = 512, 96
+    nb = in_dim // 32
+    w_b = _unit_scale_blocks(out_dim, nb, 21, only_block)
+    x_b = _unit_scale_blocks(n_tok, nb, 22, only_block)
+    wq = torch.from_numpy(w_b).cuda()
+    xq = torch.from_numpy(x_b).cuda()
+    got, ref = _run_skinny(wq, xq, w_b, x_b, in_dim, out_dim, n_tok, 2,
+                           f"skinny unit scales block={only_block}")
+    _, _, bs = oracle.matmul(w_b, x_b, in_dim, want_blocksums=True)
+    exact = bs.astype(np.int64).sum(axis=2)
+    assert np.abs(exact).max() < 2 ** 24
+    assert np.array_equal(got.astype(np.float64), exact.astype(np.float64))
+    assert np.array_equal(ref.astype(np.float64), exact.astype(np.float64))
+
+
+def test_skinny_special_scales():
+    # Subnormal weight scales, a NaN activation, a zero block.
+    in_dim, out_dim, n_tok = 512, 70, 40
+    w = workloads.normal((out_dim, in_dim), 2e-7, "cuda", "sksub", "w")
+    x = workloads.normal((n_tok, in_dim), 1.0, "cuda", "sksub", "x")
+    x[3, 17] = float("nan")
+    x[30, 64:96] = 0.0
+    wq, xq, wq_o, xq_o = _prep(w, x)
+    _run_skinny(wq, xq, wq_o, xq_o, in_dim, out_dim, n_tok, 2, "skinny special")
+
+
 @pytest.mark.parametrize("in_dim", [32, 96, 160, 3072, 4160])
 def test_generic_only_shapes(in_dim):
     q8 = _q8()
