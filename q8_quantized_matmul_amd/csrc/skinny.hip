@@ -1,12 +1,14 @@
-// skinny.hip -- Q8_0 matmul for 17..64 tokens on the matrix cores, with the
-// weights streamed once from HBM straight into MFMA registers.
+// skinny.hip -- Q8_0 matmul for up to 64 tokens on the matrix cores, with
+// the weights streamed once from HBM straight into MFMA registers (the plan
+// uses it from 20 tokens).
 //
 // The method is the same as everywhere (ds4-learning "Part 6: 代码走读",
 // trace 3: out[t][o] = sum over blocks of d_w * d_x * S_b); this kernel
 // covers the regime between the weight-streaming matvec and the LDS-tiled
-// GEMM ("Part 6: GPU 加速", section 4m: small batches get their own Q8
-// kernels).  Tokens are the MFMA's M dimension (one or two 32-token tiles),
-// output rows its N dimension (32 per wave).
+// GEMM, as the pages' backends keep dedicated kernels and a split-K path for
+// narrow batches ("Part 6: GPU 加速", sections 4c and 4s).  Tokens are the
+// MFMA's M dimension (one or two 32-token tiles), output rows its N dimension
+// (32 per wave).
 //
 //   * One v_mfma_i32_32x32x32_i8 per (token tile, block) gives the exact
 //     S_b of the 32x32 tile; one v_mfma_f32_32x32x8_f16 with only K slot 0
