@@ -49,27 +49,38 @@ __device__ __forceinline__ uint32_t quantize_block32(const float (&v)[32], uint3
 // Needs x 16-byte aligned, x_q 4-byte aligned and an even block count.  16
 // lanes per block pair, one float4 each (a wave reads 1 KB of contiguous x per
 // load).
+// A workgroup quantizes U * 16 consecutive pairs: 16 lanes per pair, U pairs
+// per lane group, all U float4 loads issued before any math so every lane
+// keeps U * 16 bytes in flight.
+template <int U>
 __global__ __launch_bounds__(256) void quantize_pair_kernel(const float *__restrict__ x,
                                                             uint8_t *__restrict__ xq,
                                                             int64_t total_pairs,
                                                             int64_t pairs_per_row,
                                                             int64_t in_dim) {
-  const int64_t gl = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int sub = (int)(gl & 15);              // 0..7 block A, 8..15 block B
-  const int64_t pair_raw = gl >> 4;
-  const bool live = pair_raw < total_pairs;    // uniform over the 16 lanes
-  const int64_t pair = live ? pair_raw : total_pairs - 1;
-  const int64_t row = pair / pairs_per_row;
-  const int64_t p = pair - row * pairs_per_row;
-  const float4 v = *reinterpret_cast<const float4 *>(x + row * in_dim + p * 64 + sub * 4);
-  const PairWords pw = quantize_pair16(v, sub);
-  if (!live) return;
-  uint32_t *dst = reinterpret_cast<uint32_t *>(xq + pair * kPairBytes);
-  dst[sub + 1] = pw.hi;
-  if (sub == 0) dst[0] = pw.lo;
+  const int sub = (int)(threadIdx.x & 15);     // 0..7 block A, 8..15 block B
+  const int64_t first = (int64_t)blockIdx.x * (16 * U) + (threadIdx.x >> 4);
+  float4 v[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int64_t pair_raw = first + 16 * u;
+    const int64_t pair = pair_raw < total_pairs ? pair_raw : total_pairs - 1;
+    const int64_t row = pair / pairs_per_row;
+    const int64_t p = pair - row * pairs_per_row;
+    v[u] = *reinterpret_cast<const float4 *>(x + row * in_dim + p * 64 + sub * 4);
+  }
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int64_t pair = first + 16 * u;
+    const PairWords pw = quantize_pair16(v[u], sub);  // every lane takes part (DPP)
+    if (pair < total_pairs) {                          // uniform over the 16 lanes
+      uint32_t *dst = reinterpret_cast<uint32_t *>(xq + pair * kPairBytes);
+      dst[sub + 1] = pw.hi;
+      if (sub == 0) dst[0] = pw.lo;
+    }
+  }
 }
 
-// One lane per block; any block count, x_q only 2-byte aligned.
 __global__ __launch_bounds__(256) void quantize_block_kernel(const float *__restrict__ x,
                                                              uint8_t *__restrict__ xq,
                                                              int64_t total_blocks,
@@ -99,9 +110,16 @@ hipError_t launch_quantize(void *x_q, const float *x, int64_t n_tok, int64_t in_
   if (fast) {
     const int64_t ppr = nb / 2;
     const int64_t total = n_tok * ppr;
-    const int64_t grid = (total * 16 + 255) / 256;
-    hipLaunchKernelGGL(quantize_pair_kernel, dim3((uint32_t)grid), dim3(256), 0, s, x,
-                       static_cast<uint8_t *>(x_q), total, ppr, in_dim);
+    // Four pairs per lane group once there are enough pairs for the chip.
+    if (total >= (int64_t)4 * 16 * 1024) {
+      const int64_t grid = (total + 63) / 64;
+      hipLaunchKernelGGL(quantize_pair_kernel<4>, dim3((uint32_t)grid), dim3(256), 0, s, x,
+                         static_cast<uint8_t *>(x_q), total, ppr, in_dim);
+    } else {
+      const int64_t grid = (total + 15) / 16;
+      hipLaunchKernelGGL(quantize_pair_kernel<1>, dim3((uint32_t)grid), dim3(256), 0, s, x,
+                         static_cast<uint8_t *>(x_q), total, ppr, in_dim);
+    }
   } else {
     const int64_t total = n_tok * nb;
     const int64_t grid = (total + 255) / 256;

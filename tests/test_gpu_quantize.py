@@ -27,7 +27,7 @@ def _check(x: torch.Tensor, where: str):
 
 
 @pytest.mark.parametrize("n_tok,in_dim", [(1, 32), (3, 96), (5, 1024), (7, 4160), (64, 4096),
-                                          (33, 2048), (2, 32768)])
+                                          (33, 2048), (2, 32768), (2000, 2112)])
 def test_quantize_random_shapes(n_tok, in_dim):
     x = workloads.normal((n_tok, in_dim), 1.0, "cuda", "test_quantize", n_tok, in_dim)
     _check(x, f"randn {n_tok}x{in_dim}")
@@ -71,6 +71,27 @@ def test_quantize_near_ties():
             x[31] = -x[5]
             rows.append(x)
     _check(torch.from_numpy(np.stack(rows)), "near ties")
+
+
+def test_quantize_near_ties_large():
+    # The near-tie blocks tiled over more than 65536 block pairs (the launch
+    # then gives each lane group four pairs), with a ragged last workgroup.
+    rows = []
+    for amax in (100.0, 3.3, 0.07, 777.7, 1e-3):
+        d = np.float32(np.float32(amax) / np.float32(127.0))
+        for start in range(-63, 63, 30):
+            x = np.zeros(32, dtype=np.float32)
+            x[0] = amax
+            for i, k in enumerate(range(start, start + 30)):
+                x[1 + i] = np.float32((k + 0.5) * np.float64(d))
+                if i % 3:
+                    x[1 + i] = np.nextafter(x[1 + i], np.float32(np.inf if i % 3 == 1 else -np.inf))
+            x[31] = -x[5]
+            rows.append(x)
+    blocks = np.stack(rows)                                # 25 blocks of 32
+    n_rows, row_blocks = 1990, 66                          # 65670 pairs, 65670 % 64 = 6
+    tiled = np.resize(blocks, (n_rows * row_blocks, 32)).reshape(n_rows, row_blocks * 32)
+    _check(torch.from_numpy(np.ascontiguousarray(tiled)), "near ties, four pairs per lane group")
 
 
 @pytest.mark.parametrize("cfg", ["tiny", "attn_q_b", "decode5", "moe", "prefill_a", "prefill_b"])
