@@ -125,7 +125,8 @@ def _routing(n_expert, n_tok, n_used, seed):
 
 @pytest.mark.parametrize("d_model,d_ff,n_expert,n_tok,n_used,clamp", [
     (256, 128, 6, 5, 3, 0.0), (256, 128, 6, 5, 3, 10.0), (512, 256, 9, 11, 4, 0.0),
-    (4096, 2048, 12, 6, 8, 10.0), (1024, 4096, 5, 3, 2, 0.0)])
+    (4096, 2048, 12, 6, 8, 10.0), (1024, 4096, 5, 3, 2, 0.0),
+    (64, 64, 1, 1, 1, 0.0), (128, 64, 3, 2, 3, 10.0), (16384, 2048, 4, 3, 2, 0.0)])
 def test_moe_ffn_small(d_model, d_ff, n_expert, n_tok, n_used, clamp):
     q8 = _q8()
     tag = f"{d_model}_{d_ff}_{n_expert}"
@@ -207,3 +208,39 @@ def test_moe_ffn_workload_sampled():
         mats_o[which] = [m if m is not None else empty for m in lst]
     say(f"[ffn] oracle on tokens {toks}")
     _check(mats_o, D, F, sel, w, x, xq, mid, mid_q, y, out, 0.0, "ffn workload", tokens=toks)
+
+
+def test_moe_ffn_graph_replay_matches_eager():
+    """The call is capturable (no host sync, no memset): replays equal the
+    eager result bit for bit, with eager work on the same buffers between."""
+    q8 = _q8()
+    d_model, d_ff, n_expert, n_tok, n_used = 512, 256, 6, 5, 3
+    mats, _ = _build(n_expert, d_model, d_ff, "graph")
+    sel, w = _routing(n_expert, n_tok, n_used, 9)
+    x = workloads.normal((n_tok, d_model), 1.0, "cuda", "ffn", "graph", "x")
+    xq = q8.q8_0_quantize_act(x)
+    tables = [q8.expert_table(mats[k]) for k in ("gate", "up", "down")]
+    sel_d, w_d = sel.cuda(), w.cuda()
+    out = torch.empty((n_tok, d_model), device="cuda")
+    ws = torch.empty(q8.q8_0_moe_ffn_workspace_bytes(n_tok, n_used, n_expert, d_model, d_ff),
+                     dtype=torch.uint8, device="cuda")
+    call = lambda: q8.q8_0_moe_ffn(*tables, n_expert, sel_d, w_d, xq, d_model, d_ff, 0.0,
+                                   out=out, workspace=ws)
+    call()
+    torch.cuda.synchronize()
+    eager = out.clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            call()
+    torch.cuda.current_stream().wait_stream(s)
+    for rep in range(3):
+        out.fill_(float("nan"))
+        ws.fill_(0x5A)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int32), eager.view(torch.int32)), f"replay {rep} differs"
+        assert q8.moe_invalid_count(ws) == 0
