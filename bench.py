@@ -140,11 +140,15 @@ def bench_attn_q_b(torch, q8, wl, steps, warmup):
     kern_us = time_kernel(torch, step, ROT)
     mv_us = time_kernel(torch, lambda i: q8.q8_0_matmul(ws[i % ROT], xq, k, n, 1, out=out), ROT)
     quant_us = time_kernel(torch, lambda i: q8.q8_0_quantize_act(x, out=xq), ROT)
+    # Measured ceiling: a plain coalesced read of the same weight copies.
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    read_us = time_kernel(torch, lambda i: q8.q8_0_probe_read(ws[i % ROT], sink), ROT)
     fused_bytes = n * row_bytes(k) + 4 * k + 4 * n       # W + fp32 x + out
     mv_bytes = n * row_bytes(k) + row_bytes(k) + 4 * n   # W + x_q + out
     return dict(sec=sec, steps=done, step_bytes=fused_bytes, kernel_bytes=fused_bytes,
                 kernel_us=kern_us, sec_separate=sec_sep, matvec_us=mv_us, matvec_bytes=mv_bytes,
-                quant_us=quant_us, plan=q8.q8_0_matmul_plan(k, n, 1, 0))
+                quant_us=quant_us, plan=q8.q8_0_matmul_plan(k, n, 1, 0),
+                read_us=read_us, read_bytes=n * row_bytes(k))
 
 
 def bench_decode5(torch, q8, wl, steps, warmup):
@@ -287,6 +291,15 @@ def bench_moe(torch, q8, wl, steps, warmup):
                 shared_bytes=mat + T * F * 4 + T * row_bytes(D), touched_experts=touched, ops=ops)
 
 
+def probe_mfma_tops(torch, q8):
+    """Measured matrix-core ceiling: independent int8 MFMA chains, no memory
+    traffic (q8_0_probe_mfma_i8), in TOPS."""
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    iters = 2000
+    us = time_kernel(torch, lambda i: q8.q8_0_probe_mfma_i8(iters, sink), 1, reps=5)
+    return q8.PROBE_MFMA_OPS_PER_ITER * iters / (us * 1e-6) / 1e12
+
+
 def bench_prefill(torch, q8, wl, name, steps, warmup):
     d = wl.prefill(name, "cuda")
     k, n, t = d["in_dim"], d["out_dim"], d["n_tok"]
@@ -378,6 +391,10 @@ def main():
                    "in_dim": 1024, "out_dim": 32768, "n_tok": 1, "kernel_plan": list(h["plan"])},
         "roofline": {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4),
+                     "measured_ceiling": {
+                         "kind": "coalesced streaming read of the same weight copies (q8_0_probe_read)",
+                         "GBs": round(h["read_bytes"] / (h["read_us"] * 1e-6) / 1e9, 1),
+                         "frac": round(ach / (h["read_bytes"] / (h["read_us"] * 1e-6) / 1e9), 4)},
                      "traffic": profiled_traffic("matvec_list_attn_q_b.md"),
                      "kernel": "matvec_list_kernel (in-launch quantize + matvec)",
                      "kernel_us": round(h["kernel_us"], 3), "bytes_per_launch": h["kernel_bytes"]},
@@ -428,6 +445,8 @@ def main():
             "routed_ffn_GBs": round(mo["ffn_bytes"] / (mo["ffn_us"] * 1e-6) / 1e9, 1),
             "frac_hbm_routed_ffn": round(mo["ffn_bytes"] / (mo["ffn_us"] * 1e-6) / 1e9
                                          / HBM_PEAK_GBS, 4)})
+        log("[bench] int8 MFMA probe")
+        mfma_tops = probe_mfma_tops(torch, q8)
         for name in ("prefill_a", "prefill_b"):
             log(f"[bench] {name}")
             pf = bench_prefill(torch, q8, wl, name, max(args.steps // 40, 10), 3)
@@ -436,6 +455,8 @@ def main():
                 "workload": name, "value": round(pf["ops"] / pf["sec"] / 1e12, 2), "unit": "TOPS",
                 "ms_per_step": round(pf["sec"] * 1e3, 4), "gemm_kernel_us": round(pf["kernel_us"], 2),
                 "gemm_TOPS": round(tops, 1), "frac_int8_mfma": round(tops / INT8_MFMA_PEAK_TOPS, 4),
+                "measured_mfma_TOPS": round(mfma_tops, 1),
+                "frac_of_measured_mfma": round(tops / mfma_tops, 4),
                 "quantize_us": round(pf["quant_us"], 2),
                 "quantize_GBs": round(pf["quant_bytes"] / (pf["quant_us"] * 1e-6) / 1e9, 1),
                 "plan": list(pf["plan"])})

@@ -249,6 +249,24 @@ int q8_0_moe_grouped_debug(float *out, int32_t *blocksums,
 int q8_0_matmul_plan(int64_t in_dim, int64_t out_dim, int64_t n_tok,
                      size_t workspace_bytes, int32_t *variant, int32_t *split_k);
 
+/* Measurement probe (the measured ceiling that the weight-streaming kernels
+ * are reported against beside the 8 TB/s peak; decode is bound by reading
+ * the weights, "Part 3: 模型架构", section 4): a plain coalesced read of
+ * `bytes` bytes at `buf`, 64 bytes in flight per lane.
+ *   buf  : device memory, 16-byte aligned; read only.
+ *   bytes: a positive multiple of 16.
+ *   sink : device uint32; written only if the loaded data hash to one fixed
+ *          value, which keeps the loads from being optimized away.
+ * Errors: bad size or alignment, null pointers -> Q8_0_EINVAL. */
+int q8_0_probe_read(const void *buf, size_t bytes, uint32_t *sink, hipStream_t stream);
+
+/* Measurement probe (the matrix-core ceiling that the int8 GEMM kernels are
+ * reported against beside the 5 POPS peak): 512 workgroups of 4 waves, each
+ * wave `iters` rounds of 4 independent v_mfma_i32_32x32x32_i8, i.e.
+ * 512 * 4 * 4 * 65536 * iters integer operations.  sink as above.
+ * Errors: iters < 1, null sink -> Q8_0_EINVAL. */
+int q8_0_probe_mfma_i8(int32_t iters, uint32_t *sink, hipStream_t stream);
+
 /* Static description of a status code. */
 const char *q8_0_strerror(int status);
 

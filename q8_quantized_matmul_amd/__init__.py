@@ -78,6 +78,8 @@ _sig = {
     "q8_0_matmul_list": ([ctypes.POINTER(MatmulItem), _i32, _i64, _vp], ctypes.c_int),
     "q8_0_moe_ffn_workspace_bytes": ([_i64, _i32, _i32, _i64, _i64], _sz),
     "q8_0_moe_ffn": ([ctypes.POINTER(MoeFfnArgs), _vp, _sz, _vp], ctypes.c_int),
+    "q8_0_probe_read": ([_vp, _sz, _vp, _vp], ctypes.c_int),
+    "q8_0_probe_mfma_i8": ([_i32, _vp, _vp], ctypes.c_int),
     "q8_0_strerror": ([ctypes.c_int], ctypes.c_char_p),
 }
 for _name, (_args, _res) in _sig.items():
@@ -283,3 +285,17 @@ def q8_0_moe_ffn(gate_table, up_table, down_table, n_expert, selected, weights, 
                              workspace.numel() * workspace.element_size(), _stream()),
            "q8_0_moe_ffn")
     return out, workspace
+
+
+PROBE_MFMA_OPS_PER_ITER = 512 * 4 * 4 * 65536  # integer ops per round of q8_0_probe_mfma_i8
+
+
+def q8_0_probe_read(buf: torch.Tensor, sink: torch.Tensor) -> None:
+    """Streaming read of the whole (contiguous, 16-byte aligned) device tensor."""
+    _check(_lib.q8_0_probe_read(_dev(buf, "buf"), buf.numel() * buf.element_size(),
+                                _dev(sink, "sink"), _stream()), "q8_0_probe_read")
+
+
+def q8_0_probe_mfma_i8(iters: int, sink: torch.Tensor) -> None:
+    _check(_lib.q8_0_probe_mfma_i8(int(iters), _dev(sink, "sink"), _stream()),
+           "q8_0_probe_mfma_i8")

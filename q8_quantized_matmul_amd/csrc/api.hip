@@ -384,6 +384,22 @@ int q8_0_matmul_list(const q8_0_matmul_item *items, int32_t n_items, int64_t n_t
   return run_list(items, n_items, n_tok, stream);
 }
 
+int q8_0_probe_read(const void *buf, size_t bytes, uint32_t *sink, hipStream_t stream) {
+  if (!buf || !sink || bytes == 0 || bytes % 16 != 0 || bytes > (size_t)INT64_MAX)
+    return Q8_0_EINVAL;
+  if (!aligned(buf, 16) || !aligned(sink, 4)) return Q8_0_EINVAL;
+  int st = check_device();
+  if (st != Q8_0_OK) return st;
+  return status_of(q8::launch_probe_read(buf, (int64_t)bytes, sink, stream));
+}
+
+int q8_0_probe_mfma_i8(int32_t iters, uint32_t *sink, hipStream_t stream) {
+  if (iters < 1 || !sink || !aligned(sink, 4)) return Q8_0_EINVAL;
+  int st = check_device();
+  if (st != Q8_0_OK) return st;
+  return status_of(q8::launch_probe_mfma(iters, sink, stream));
+}
+
 const char *q8_0_strerror(int status) {
   switch (status) {
     case Q8_0_OK: return "ok";

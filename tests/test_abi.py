@@ -27,7 +27,7 @@ def q8():
 def test_exports_every_declared_symbol(q8):
     lib = ctypes.CDLL(q8.LIB_PATH)
     declared = _declared()
-    assert len(declared) == 12
+    assert len(declared) == 14
     for name in declared:
         assert hasattr(lib, name), name
     assert set(declared) == set(q8.EXPORTED)
@@ -203,3 +203,14 @@ def test_oracle_is_not_imported_by_the_product():
             if f.endswith((".py", ".hip", ".h", ".cpp")):
                 text = open(os.path.join(root, f), encoding="utf-8").read()
                 assert "oracle" not in text.replace("oracles", ""), f
+
+
+def test_probe_validation(q8):
+    lib = q8.raw_library()
+    assert lib.q8_0_probe_read(None, 64, FAKE, None) == q8.Q8_0_EINVAL
+    assert lib.q8_0_probe_read(FAKE, 0, FAKE, None) == q8.Q8_0_EINVAL
+    assert lib.q8_0_probe_read(FAKE, 100, FAKE, None) == q8.Q8_0_EINVAL   # not a multiple of 16
+    assert lib.q8_0_probe_read(FAKE + 4, 64, FAKE, None) == q8.Q8_0_EINVAL
+    assert lib.q8_0_probe_read(FAKE, 64, None, None) == q8.Q8_0_EINVAL
+    assert lib.q8_0_probe_mfma_i8(0, FAKE, None) == q8.Q8_0_EINVAL
+    assert lib.q8_0_probe_mfma_i8(10, None, None) == q8.Q8_0_EINVAL
