@@ -1,12 +1,13 @@
 // gemm.hip -- Q8_0 x Q8_0 GEMM on gfx950 matrix cores for many tokens
-// (prefill, and any call with n_tok >= 16).
+// (prefill, and any call with more than 64 tokens; 20..64 go to the skinny
+// kernel).
 //
 // Same arithmetic as the matvec ("Part 6: 代码走读", trace 3): per output
 // (t, o) and 32-value block b, an exact int32 block dot S_b times the exact
-// fp32 scale product d_w * d_x, summed in fp32.  The pages run this on
-// matrix units only from 16 tokens up ("Part 6: GPU 加速", C3 NAX paragraph)
-// and accept a different fp32 reduction order for batched GEMMs than for
-// decode ("Part 6: GPU 加速", section 4m); this kernel is deterministic but not
+// fp32 scale product d_w * d_x, summed in fp32.  The pages move batched
+// Q8_0 matmuls onto matrix units ("Part 6: GPU 加速", C3 NAX paragraph) and
+// accept a different fp32 reduction order for batched GEMMs than for decode
+// ("Part 6: GPU 加速", section 4m); this kernel is deterministic but not
 // bitwise equal to the matvec.
 //
 // gfx950 mapping:
@@ -25,8 +26,11 @@
 //     lane; the misaligned first block of a pair is realigned in registers.
 //     The next stage's global loads are issued before the current stage's
 //     MFMAs (register prefetch).
-//   * Split-K over grid.z writes fp32 partials to caller workspace; a second
-//     kernel sums them in split order (deterministic, no atomics).
+//   * The whole-tile shapes of both prefill workloads take gemm_t4_kernel
+//     (four 32x32 tiles per wave, direct-to-LDS copies, further down); the
+//     kernels here take the rest.
+//   * Split-K writes fp32 partials to caller workspace; a second kernel sums
+//     them in split order (deterministic, no atomics).
 #include <utility>
 
 #include "launch.h"

@@ -18,10 +18,14 @@
 //     masked to zero; no repacking of the 2-byte-misaligned first block.
 //   * Rows shorter than 64 pairs share a wave (64/P rows per wave); longer
 //     rows are split into 64-pair chunks over up to 4 waves of the workgroup
-//     and reduced through LDS.  Lane partial sums are reduced with xor
-//     shuffles in a fixed order, so results are deterministic.
-//   * Each workgroup loads all of its weight rows before touching x, so every
-//     wave has RG * CPW * 272 bytes in flight per lane group.
+//     and reduced through LDS.  Lane partial sums are reduced with DPP adds
+//     in a fixed order (group_sum), so results are deterministic.
+//   * Each workgroup issues all of its weight loads before it needs x, so a
+//     lane has RG * CPW pairs (68 bytes each) in flight.  x comes from LDS:
+//     staged there by direct copies (StagedX: grouped launches and two or
+//     more tokens), or quantized there from fp32 by the workgroup itself
+//     (LdsX: the list launch); single-token launches read it per wave from
+//     global memory (GlobalX).
 #include <algorithm>
 
 #include "launch.h"
