@@ -106,7 +106,7 @@ def _run_skinny(wq, xq, wq_o, xq_o, in_dim, out_dim, n_tok, split, where):
 @pytest.mark.parametrize("in_dim,out_dim,n_tok,split", [
     (4096, 2048, 64, 4), (4096, 2048, 32, 4), (2048, 4096, 33, 2), (4096, 1000, 40, 1),
     (1024, 300, 17, 2), (64, 50, 64, 1), (192, 65, 31, 1), (128, 33, 5, 1), (4096, 64, 48, 16),
-    (1024, 32768, 64, 1), (8192, 96, 1, 3)])
+    (1024, 32768, 64, 1), (8192, 96, 1, 3), (2048, 4096, 64, 2)])
 def test_skinny_shapes(in_dim, out_dim, n_tok, split):
     # Ragged rows and token counts, one or two token tiles, waves with no
     # block pair (192 values = 3 pairs), and split-K with uneven splits.
