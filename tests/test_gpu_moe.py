@@ -130,3 +130,38 @@ def test_moe_workload_full_sampled():
     toks = np.arange(0, T, 8)
     ref, mag, _ = oracle.matmul(oracle_quantize(w_sh), oracle_quantize(x[torch.as_tensor(toks, device="cuda")]), D)
     assert_close(got.cpu().numpy()[toks], ref, mag, "shared gate")
+
+
+@pytest.mark.parametrize("n_expert,n_tok,n_used,n_bad", [
+    (256, 64, 8, 0), (5000, 300, 8, 7), (3, 700, 3, 2), (8192, 2, 1, 0), (1, 5, 2, 1)])
+def test_moe_routing_tables(n_expert, n_tok, n_used, n_bad):
+    # The routing tables are index work: compared exactly with their plain
+    # definitions (counts = histogram of the valid ids, offsets = its exclusive
+    # prefix sum, pairs = the pair ids in a stable sort by expert id).  The
+    # int32 layout of the workspace: [0] invalid-id count, counts at 16,
+    # offsets (n_expert + 1) after them, then the pair list.  Several
+    # 1024-pair chunks, experts per lane above one, duplicates and invalid ids.
+    q8 = _q8()
+    rng = np.random.default_rng(n_expert * 31 + n_tok)
+    sel = rng.integers(0, n_expert, size=(n_tok, n_used)).astype(np.int32)
+    flat = sel.reshape(-1)
+    bad_at = rng.choice(flat.size, n_bad, replace=False)
+    flat[bad_at] = np.where(np.arange(n_bad) % 2 == 0, n_expert + 3, -1)
+    out_dim, in_dim = 4, 32
+    stack = torch.zeros((n_expert, out_dim, q8.row_bytes(in_dim)), dtype=torch.uint8, device="cuda")
+    xq = torch.zeros((n_tok, q8.row_bytes(in_dim)), dtype=torch.uint8, device="cuda")
+    say(f"[moe routing] E={n_expert} T={n_tok} k={n_used} bad={n_bad}")
+    _, ws = q8.q8_0_moe_grouped(q8.expert_table(stack), n_expert, torch.from_numpy(sel).cuda(),
+                                xq, in_dim, out_dim, 0)
+    torch.cuda.synchronize()
+    got = ws.cpu().view(torch.int32).numpy()
+    valid = (flat >= 0) & (flat < n_expert)
+    counts = np.bincount(flat[valid], minlength=n_expert)
+    offsets = np.concatenate([[0], np.cumsum(counts)])
+    pairs = np.argsort(np.where(valid, flat, n_expert), kind="stable")[:int(valid.sum())]
+    c0, o0 = 16, 16 + n_expert
+    p0 = o0 + n_expert + 1
+    assert got[0] == n_bad
+    assert np.array_equal(got[c0:c0 + n_expert], counts)
+    assert np.array_equal(got[o0:o0 + n_expert + 1], offsets)
+    assert np.array_equal(got[p0:p0 + pairs.size], pairs)
