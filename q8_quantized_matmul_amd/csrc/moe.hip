@@ -13,9 +13,11 @@
 // their output rows are filled with NaN.
 //
 // One workgroup of 1024 lanes does it: LDS atomics count (integer, so the
-// result is order independent), a block scan builds offsets, and each 1024-pair
-// chunk is scattered with in-wave ranks from ballots (lanes sharing an expert
-// id are found bit by bit) and waves taking their turn in index order.
+// result is order independent), in-wave scans and the 16 wave totals build
+// the offsets, and each 1024-pair chunk is scattered with in-wave ranks from
+// ballots (lanes sharing an expert id are found bit by bit) and waves taking
+// their turn in index order.  The ids are read from memory once, in the
+// counting pass, and kept in LDS.
 #include "launch.h"
 #include "q8_device.h"
 
@@ -25,21 +27,15 @@ namespace {
 constexpr int kRouteThreads = 1024;
 constexpr int kRouteWaves = kRouteThreads / 64;
 constexpr int kHeaderInts = 16;
+constexpr int kKeyChunk = 4096;  // expert ids staged in LDS per scatter pass
 
-__device__ __forceinline__ int32_t block_exclusive_scan(int32_t v, int32_t *tmp, int32_t *total) {
-  const int tid = threadIdx.x;
-  tmp[tid] = v;
-  __syncthreads();
-  for (int off = 1; off < kRouteThreads; off <<= 1) {
-    int32_t add = tid >= off ? tmp[tid - off] : 0;
-    __syncthreads();
-    tmp[tid] += add;
-    __syncthreads();
+__device__ __forceinline__ int32_t wave_inclusive_scan(int32_t v, int lane) {
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int32_t u = __shfl_up(v, off, 64);
+    if (lane >= off) v += u;
   }
-  const int32_t incl = tmp[tid];
-  *total = tmp[kRouteThreads - 1];
-  __syncthreads();
-  return incl - v;
+  return v;
 }
 
 __global__ __launch_bounds__(kRouteThreads) void moe_route_kernel(
@@ -47,9 +43,10 @@ __global__ __launch_bounds__(kRouteThreads) void moe_route_kernel(
     int32_t *__restrict__ ws, int64_t off_counts, int64_t off_offsets, int64_t off_pairs,
     float *__restrict__ out, int64_t out_dim) {
   extern __shared__ int32_t lds[];
-  int32_t *running = lds;                          // [n_expert]
-  int32_t *scan_tmp = lds + n_expert;              // [1024]
-  int32_t *slot_base = scan_tmp + kRouteThreads;   // [16][64]
+  int32_t *running = lds;                  // [n_expert]
+  int32_t *keys = lds + n_expert;          // [kKeyChunk]
+  int32_t *wave_sum = keys + kKeyChunk;    // [kRouteWaves]
+  int32_t *slot_base = wave_sum + kRouteWaves;  // [kRouteWaves][64]
   __shared__ int32_t invalid;
 
   const int tid = threadIdx.x;
@@ -60,8 +57,10 @@ __global__ __launch_bounds__(kRouteThreads) void moe_route_kernel(
   if (tid == 0) invalid = 0;
   __syncthreads();
 
+  // Count; the first chunk of ids stays in LDS for the scatter.
   for (int64_t i = tid; i < n_pairs; i += kRouteThreads) {
     const int32_t e = selected[i];
+    if (i < kKeyChunk) keys[i] = e;
     if (e >= 0 && e < n_expert) atomicAdd(&running[e], 1);
     else atomicAdd(&invalid, 1);
   }
@@ -69,12 +68,19 @@ __global__ __launch_bounds__(kRouteThreads) void moe_route_kernel(
 
   // counts and exclusive offsets; each lane owns a contiguous run of experts.
   const int32_t per = (n_expert + kRouteThreads - 1) / kRouteThreads;
-  const int32_t e0 = tid * per;
+  const int32_t e0 = min(tid * per, n_expert);
   const int32_t e1 = min(e0 + per, n_expert);
   int32_t local = 0;
   for (int32_t e = e0; e < e1; ++e) local += running[e];
-  int32_t total = 0;
-  int32_t base = block_exclusive_scan(local, scan_tmp, &total);
+  const int32_t incl = wave_inclusive_scan(local, lane);
+  if (lane == 63) wave_sum[wave] = incl;
+  __syncthreads();
+  int32_t base = incl - local, total = 0;
+  for (int w = 0; w < kRouteWaves; ++w) {
+    const int32_t t = wave_sum[w];
+    if (w < wave) base += t;
+    total += t;
+  }
   for (int32_t e = e0; e < e1; ++e) {
     const int32_t c = running[e];
     ws[off_counts + e] = c;
@@ -88,11 +94,19 @@ __global__ __launch_bounds__(kRouteThreads) void moe_route_kernel(
   }
   __syncthreads();
 
-  // Stable scatter, 1024 pairs at a time, waves in index order.
+  // Stable scatter, 1024 pairs at a time: each wave ranks its lanes among
+  // those sharing an expert id, then the waves take slots in index order.
   const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   for (int64_t chunk = 0; chunk < n_pairs; chunk += kRouteThreads) {
+    if (chunk > 0 && chunk % kKeyChunk == 0) {
+      // Stage the next kKeyChunk ids (the barrier ending the previous chunk
+      // has retired every read of the old ones).
+      const int len = (int)min<int64_t>(kKeyChunk, n_pairs - chunk);
+      for (int j = tid; j < len; j += kRouteThreads) keys[j] = selected[chunk + j];
+      __syncthreads();
+    }
     const int64_t i = chunk + tid;
-    int32_t e = i < n_pairs ? selected[i] : -1;
+    const int32_t e = i < n_pairs ? keys[i % kKeyChunk] : -1;
     const bool valid = e >= 0 && e < n_expert;
     const uint32_t key = valid ? (uint32_t)e : (uint32_t)n_expert;
     uint64_t peers = __ballot(1);
@@ -138,7 +152,7 @@ MoeLayout moe_layout(int64_t n_tok, int32_t n_used, int32_t n_expert) {
 }
 
 size_t moe_route_lds_bytes(int32_t n_expert) {
-  return sizeof(int32_t) * ((size_t)n_expert + kRouteThreads + kRouteWaves * 64);
+  return sizeof(int32_t) * ((size_t)n_expert + kKeyChunk + kRouteWaves + kRouteWaves * 64);
 }
 
 hipError_t launch_moe_route(const int32_t *selected, int64_t n_tok, int32_t n_used,
