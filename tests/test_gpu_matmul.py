@@ -348,3 +348,43 @@ def test_empty_and_errors():
     with pytest.raises(q8.Q8Error) as e:
         q8.q8_0_matmul_debug(wq, xq, 32, 4, 1, variant=2)  # matvec needs whole pairs
     assert e.value.code == q8.Q8_0_EINVAL
+
+
+def _random_shapes(n_cases, seed):
+    """Seeded shapes around the plan's regime edges (1-2 tokens, 15-21, 60-70,
+    above 100), in_dim any multiple of 32 up to 8192, ragged out_dim; the
+    oracle's work per case is bounded."""
+    rng = np.random.default_rng(seed)
+    tok_pool = [1, 2, 3, 15, 16, 17, 19, 20, 21, 33, 63, 64, 65, 66, 70, 97, 128, 129, 160]
+    cases = []
+    while len(cases) < n_cases:
+        kind = rng.integers(0, 3)
+        if kind == 0:
+            in_dim = 32 * int(rng.integers(1, 257))
+        elif kind == 1:
+            in_dim = 64 * 2 ** int(rng.integers(0, 8))
+        else:
+            in_dim = 4096 * int(rng.integers(1, 3))
+        out_dim = int(rng.integers(1, 2500))
+        n_tok = int(rng.choice(tok_pool))
+        if in_dim * out_dim * n_tok <= 1.5e8:
+            cases.append((in_dim, out_dim, n_tok))
+    return cases
+
+
+@pytest.mark.parametrize("in_dim,out_dim,n_tok", _random_shapes(36, 2024))
+def test_auto_plan_random_shapes(in_dim, out_dim, n_tok):
+    # Whatever kernel and split the plan picks for the shape (with the
+    # workspace it asks for) matches the oracle; the output starts poisoned.
+    q8 = _q8()
+    w = workloads.normal((out_dim, in_dim), 0.02, "cuda", "rand", in_dim, out_dim, "w")
+    x = workloads.normal((n_tok, in_dim), 1.0, "cuda", "rand", in_dim, n_tok, "x")
+    wq, xq, wq_o, xq_o = _prep(w, x)
+    ws = q8.matmul_workspace(in_dim, out_dim, n_tok)
+    plan = q8.q8_0_matmul_plan(in_dim, out_dim, n_tok, ws.numel())
+    say(f"[matmul random] in={in_dim} out={out_dim} n_tok={n_tok} plan={plan}")
+    out = torch.full((n_tok, out_dim), float("nan"), device="cuda")
+    got = q8.q8_0_matmul(wq, xq, in_dim, out_dim, n_tok, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    ref, mag, _ = oracle.matmul(wq_o, xq_o, in_dim)
+    assert_close(got.cpu().numpy(), ref, mag, f"random {in_dim}x{out_dim}x{n_tok} plan {plan}")
