@@ -191,3 +191,34 @@ def test_list_graph_replay_matches_eager():
         torch.cuda.synchronize()
         for o, e in zip(outs, eager):
             assert torch.equal(o.view(torch.int32), e.view(torch.int32)), f"replay {rep} differs"
+
+
+def _random_calls(n_calls, seed):
+    """Seeded list calls: 1-16 items of mixed in_dim (any multiple of 32 up to
+    8192, and the 16384/32768 rows), ragged out_dim, every x mode the call
+    accepts for the item; the oracle's work per call is bounded."""
+    rng = np.random.default_rng(seed)
+    calls = []
+    while len(calls) < n_calls:
+        n_tok = int(rng.choice([1, 1, 2, 4, 15, 16, 17, 40]))
+        specs, work = [], 0
+        for _ in range(int(rng.integers(1, 17))):
+            r = rng.integers(0, 4)
+            k = (32 * int(rng.integers(1, 257)) if r == 0 else
+                 64 * 2 ** int(rng.integers(0, 8)) if r == 1 else
+                 1024 * int(rng.integers(1, 9)) if r == 2 else int(rng.choice([16384, 32768])))
+            n = int(rng.integers(1, 1500))
+            # x without x_q only where the call quantizes inside its launch.
+            fused = 64 <= k <= 4096 and k & (k - 1) == 0 and n_tok * k <= 4096
+            modes = ["x", "x+xq", "xq"] if fused else ["x+xq", "xq"]
+            specs.append(dict(in_dim=k, out_dim=n, mode=str(rng.choice(modes))))
+            work += k * n * n_tok
+        if work <= 2e8:
+            calls.append((n_tok, specs))
+    return calls
+
+
+@pytest.mark.parametrize("case", range(12))
+def test_list_random_calls(case):
+    n_tok, specs = _random_calls(12, 77)[case]
+    _run(specs, n_tok, f"random{case}")
