@@ -165,3 +165,37 @@ def test_moe_routing_tables(n_expert, n_tok, n_used, n_bad):
     assert np.array_equal(got[c0:c0 + n_expert], counts)
     assert np.array_equal(got[o0:o0 + n_expert + 1], offsets)
     assert np.array_equal(got[p0:p0 + pairs.size], pairs)
+
+
+def _random_moe(n_cases, seed):
+    """Seeded grouped calls: any in_dim multiple of 32 up to 4096 (both the
+    weight-streaming and the generic grouped kernels), 1-40 experts, 1-150
+    tokens, either x layout; the oracle's work per case is bounded."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    while len(cases) < n_cases:
+        in_dim = (32 * int(rng.integers(1, 129)) if rng.integers(0, 2) else
+                  64 * 2 ** int(rng.integers(0, 7)))
+        out_dim = int(rng.integers(1, 300))
+        n_expert = int(rng.integers(1, 41))
+        n_used = int(rng.integers(1, min(8, n_expert) + 1))
+        n_tok = int(rng.choice([1, 2, 7, 16, 17, 40, 150]))
+        if in_dim * out_dim * n_tok * n_used <= 6e7:
+            cases.append((in_dim, out_dim, n_expert, n_tok, n_used, int(rng.integers(0, 2))))
+    return cases
+
+
+@pytest.mark.parametrize("in_dim,out_dim,n_expert,n_tok,n_used,x_rows", _random_moe(12, 31))
+def test_moe_random_shapes(in_dim, out_dim, n_expert, n_tok, n_used, x_rows):
+    q8 = _q8()
+    wq, sel, xq, wq_o, xq_o = _small_case(in_dim, out_dim, n_expert, n_tok, n_used,
+                                          in_dim * 7 + n_tok, x_rows)
+    say(f"[moe random] in={in_dim} out={out_dim} E={n_expert} T={n_tok} k={n_used} x_rows={x_rows}")
+    out = torch.full((n_tok, n_used, out_dim), float("nan"), device="cuda")
+    got, ws = q8.q8_0_moe_grouped(q8.expert_table(wq), n_expert, sel.cuda(), xq, in_dim, out_dim,
+                                  x_rows, out=out)
+    torch.cuda.synchronize()
+    assert q8.moe_invalid_count(ws) == 0
+    ref, mag, bad = oracle.moe_grouped(wq_o, sel.numpy(), xq_o, in_dim, out_dim, x_rows)
+    assert bad == 0
+    assert_close(got.cpu().numpy(), ref, mag, "moe random")
