@@ -143,6 +143,38 @@ def test_moe_ffn_small(d_model, d_ff, n_expert, n_tok, n_used, clamp):
     assert torch.equal(y.view(torch.int32), y2.view(torch.int32))
 
 
+def _random_ffn(n_cases, seed):
+    """Seeded FFN calls over the widths the call accepts (64 ... 4096 values a
+    row, and 8192/16384 for d_model), 1-20 experts, 1-40 tokens, with and
+    without the clamp; the oracle's work per case is bounded."""
+    rng = np.random.default_rng(seed)
+    widths = [64 * 2 ** i for i in range(7)]
+    cases = []
+    while len(cases) < n_cases:
+        d_model = int(rng.choice(widths + [8192, 16384]))
+        d_ff = int(rng.choice(widths + [8192]))
+        n_expert = int(rng.integers(1, 21))
+        n_used = int(rng.integers(1, min(8, n_expert) + 1))
+        n_tok = int(rng.choice([1, 2, 5, 16, 17, 40]))
+        clamp = float(rng.choice([0.0, 10.0]))
+        if 3 * n_tok * n_used * d_model * d_ff <= 1.2e8 and n_expert * d_model * d_ff <= 2e8:
+            cases.append((d_model, d_ff, n_expert, n_tok, n_used, clamp))
+    return cases
+
+
+@pytest.mark.parametrize("d_model,d_ff,n_expert,n_tok,n_used,clamp", _random_ffn(8, 11))
+def test_moe_ffn_random_shapes(d_model, d_ff, n_expert, n_tok, n_used, clamp):
+    q8 = _q8()
+    tag = f"r{d_model}_{d_ff}_{n_expert}"
+    mats, mats_o = _build(n_expert, d_model, d_ff, tag)
+    sel, w = _routing(n_expert, n_tok, n_used, d_ff + n_tok)
+    x = workloads.normal((n_tok, d_model), 1.0, "cuda", "ffn", tag, "x")
+    say(f"[ffn random] d_model={d_model} d_ff={d_ff} E={n_expert} T={n_tok} k={n_used} clamp={clamp}")
+    xq, mid, mid_q, y, out, ws = _run(mats, n_expert, d_model, d_ff, sel, w, x, clamp)
+    assert q8.moe_invalid_count(ws) == 0
+    _check(mats_o, d_model, d_ff, sel, w, x, xq, mid, mid_q, y, out, clamp, "ffn random")
+
+
 def test_moe_ffn_clamp_is_active():
     # Large activations push gate and up past the limit: the clamped and
     # unclamped results differ, and each matches its own oracle.
