@@ -13,10 +13,10 @@
 namespace {
 
 // Regimes by token count (measured on 4096->2048, 2048->4096, 4096->1024 and
-// 1024->32768): the weight-streaming matvec below 20 tokens, the skinny
-// matrix-core kernel (weights streamed into MFMA registers) from 20 to 64,
+// 1024->32768): the weight-streaming matvec below 16 tokens, the skinny
+// matrix-core kernel (weight and token rows staged in LDS) from 16 to 64,
 // the LDS-tiled GEMM above.
-constexpr int64_t kSkinnyMinTokens = 20;
+constexpr int64_t kSkinnyMinTokens = 16;
 // The shared list launch reads each token's x row per wave from global
 // memory; from 16 tokens an item runs as its own (LDS-staged) matvec launch.
 constexpr int64_t kListMaxTokens = 15;

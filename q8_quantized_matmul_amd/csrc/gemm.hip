@@ -509,69 +509,6 @@ constexpr int PERIOD = 17;                  // 17 * 64 dwords = 32 rows
 static_assert(PERIOD * 64 == 32 * RD, "copy pattern period");
 }  // namespace t4
 
-// LDS words of one operand of block B of a stage: a 24-byte (16 for B = 3)
-// 8-byte-aligned window holding the 16 quant bytes of half h, and for B = 3
-// the block's scale, which lies before that window.
-struct T4Raw {
-  uint32_t w[6];
-  uint32_t sc;
-};
-
-template <int B>
-__device__ __forceinline__ void t4_read(const uint8_t *row, int h, T4Raw &r) {
-  constexpr int M = (2 * B + 2) % 8;  // quant start modulo 8 (rows are 8-aligned)
-  typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-  const u32x2 *q = reinterpret_cast<const u32x2 *>(row + B * kBlockBytes + 2 + 16 * h - M);
-  const u32x2 a = q[0], b = q[1];
-  r.w[0] = a.x;
-  r.w[1] = a.y;
-  r.w[2] = b.x;
-  r.w[3] = b.y;
-  if constexpr (M != 0) {
-    const u32x2 c = q[2];
-    r.w[4] = c.x;
-    r.w[5] = c.y;
-  } else {
-    r.sc = *reinterpret_cast<const uint16_t *>(row + B * kBlockBytes);
-  }
-}
-
-// The 16 quant bytes realigned for the MFMA, and the scale bits for half 0
-// (zero for half 1, which feeds the unused K slots of the scale MFMA).
-template <int B>
-__device__ __forceinline__ i32x4 t4_prep(const T4Raw &r, int h, uint32_t &scale) {
-  constexpr int M = (2 * B + 2) % 8;
-  const uint32_t *w = r.w;
-  if constexpr (M == 0) {
-    scale = h ? 0u : r.sc;
-    return i32x4{(int)w[0], (int)w[1], (int)w[2], (int)w[3]};
-  } else if constexpr (M == 4) {
-    scale = h ? 0u : (w[0] >> 16);
-    return i32x4{(int)w[1], (int)w[2], (int)w[3], (int)w[4]};
-  } else {
-    constexpr int K = M == 2 ? 0 : 1;
-    scale = h ? 0u : (M == 2 ? (w[0] & 0xFFFFu) : (w[1] & 0xFFFFu));
-    return i32x4{(int)__builtin_amdgcn_alignbyte(w[K + 1], w[K], 2),
-                 (int)__builtin_amdgcn_alignbyte(w[K + 2], w[K + 1], 2),
-                 (int)__builtin_amdgcn_alignbyte(w[K + 3], w[K + 2], 2),
-                 (int)__builtin_amdgcn_alignbyte(w[K + 4], w[K + 3], 2)};
-  }
-}
-
-// Direct global->LDS dword copy through a buffer resource: a 32-bit lane
-// offset and a scalar offset, so the copy needs no 64-bit address per lane.
-typedef int32_t rsrc_t __attribute__((ext_vector_type(4)));
-__device__ void buffer_load_lds_raw(rsrc_t rsrc, __attribute__((address_space(3))) uint32_t *lds,
-                                    int size, int voffset, int soffset, int offset,
-                                    int aux) __asm("llvm.amdgcn.raw.buffer.load.lds");
-
-// Raw buffer resource over [base, base + bytes): stride 0, 32-bit dword format.
-__device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t bytes) {
-  const uint64_t b = reinterpret_cast<uint64_t>(base);
-  return rsrc_t{(int32_t)(uint32_t)b, (int32_t)(uint32_t)(b >> 32) & 0xFFFF, (int32_t)bytes,
-                0x00020000};
-}
-
 __global__ __launch_bounds__(256, 2) void gemm_t4_kernel(const GemmArgs a) {
   using namespace t4;
   __shared__ __attribute__((aligned(16))) uint8_t ring[2 * STAGE];
@@ -722,8 +659,17 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(float *__restrict__ 
                                                             int64_t n, int n_split) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i >= n) return;
-  float v = part[i];
-  for (int s = 1; s < n_split; ++s) v += part[(int64_t)s * n + i];
+  // Partials 0, 1, ... summed in that order; eight loads are issued before
+  // their adds (past the last split they re-read the last one, unused).
+  float v = 0.0f;
+  for (int s0 = 0; s0 < n_split; s0 += 8) {
+    float p[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) p[k] = part[(int64_t)min(s0 + k, n_split - 1) * n + i];
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+      if (s0 + k < n_split) v = s0 + k == 0 ? p[k] : v + p[k];
+  }
   out[i] = v;
 }
 

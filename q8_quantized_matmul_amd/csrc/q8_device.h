@@ -274,4 +274,68 @@ __device__ __forceinline__ void quantize_pair4(const float4 (&v)[4], int j, uint
   }
 }
 
+// Staged rows in LDS (8-byte-aligned rows of 4-block, 136-byte slices).
+// LDS words of one operand of block B of a slice: a 24-byte (16 for B = 3)
+// 8-byte-aligned window holding the 16 quant bytes of half h, and for B = 3
+// the block's scale, which lies before that window.
+struct T4Raw {
+  uint32_t w[6];
+  uint32_t sc;
+};
+
+template <int B>
+__device__ __forceinline__ void t4_read(const uint8_t *row, int h, T4Raw &r) {
+  constexpr int M = (2 * B + 2) % 8;  // quant start modulo 8 (rows are 8-aligned)
+  typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+  const u32x2 *q = reinterpret_cast<const u32x2 *>(row + B * kBlockBytes + 2 + 16 * h - M);
+  const u32x2 a = q[0], b = q[1];
+  r.w[0] = a.x;
+  r.w[1] = a.y;
+  r.w[2] = b.x;
+  r.w[3] = b.y;
+  if constexpr (M != 0) {
+    const u32x2 c = q[2];
+    r.w[4] = c.x;
+    r.w[5] = c.y;
+  } else {
+    r.sc = *reinterpret_cast<const uint16_t *>(row + B * kBlockBytes);
+  }
+}
+
+// The 16 quant bytes realigned for the MFMA, and the scale bits for half 0
+// (zero for half 1, which feeds the unused K slots of the scale MFMA).
+template <int B>
+__device__ __forceinline__ i32x4 t4_prep(const T4Raw &r, int h, uint32_t &scale) {
+  constexpr int M = (2 * B + 2) % 8;
+  const uint32_t *w = r.w;
+  if constexpr (M == 0) {
+    scale = h ? 0u : r.sc;
+    return i32x4{(int)w[0], (int)w[1], (int)w[2], (int)w[3]};
+  } else if constexpr (M == 4) {
+    scale = h ? 0u : (w[0] >> 16);
+    return i32x4{(int)w[1], (int)w[2], (int)w[3], (int)w[4]};
+  } else {
+    constexpr int K = M == 2 ? 0 : 1;
+    scale = h ? 0u : (M == 2 ? (w[0] & 0xFFFFu) : (w[1] & 0xFFFFu));
+    return i32x4{(int)__builtin_amdgcn_alignbyte(w[K + 1], w[K], 2),
+                 (int)__builtin_amdgcn_alignbyte(w[K + 2], w[K + 1], 2),
+                 (int)__builtin_amdgcn_alignbyte(w[K + 3], w[K + 2], 2),
+                 (int)__builtin_amdgcn_alignbyte(w[K + 4], w[K + 3], 2)};
+  }
+}
+
+// Direct global->LDS dword copy through a buffer resource: a 32-bit lane
+// offset and a scalar offset, so the copy needs no 64-bit address per lane.
+typedef int32_t rsrc_t __attribute__((ext_vector_type(4)));
+__device__ void buffer_load_lds_raw(rsrc_t rsrc, __attribute__((address_space(3))) uint32_t *lds,
+                                    int size, int voffset, int soffset, int offset,
+                                    int aux) __asm("llvm.amdgcn.raw.buffer.load.lds");
+
+// Raw buffer resource over [base, base + bytes): stride 0, 32-bit dword format.
+__device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+  const uint64_t b = reinterpret_cast<uint64_t>(base);
+  return rsrc_t{(int32_t)(uint32_t)b, (int32_t)(uint32_t)(b >> 32) & 0xFFFF, (int32_t)bytes,
+                0x00020000};
+}
+
 }  // namespace q8

@@ -1,28 +1,27 @@
-// skinny.hip -- Q8_0 matmul for up to 64 tokens on the matrix cores, with
-// the weights streamed once from HBM straight into MFMA registers (the plan
-// uses it from 20 tokens).
+// skinny.hip -- Q8_0 matmul for up to 64 tokens on the matrix cores (the
+// plan uses it from 16 tokens), a 32-row output tile per workgroup.
 //
 // The method is the same as everywhere (ds4-learning "Part 6: 代码走读",
 // trace 3: out[t][o] = sum over blocks of d_w * d_x * S_b); this kernel
 // covers the regime between the weight-streaming matvec and the LDS-tiled
 // GEMM, as the pages' backends keep dedicated kernels and a split-K path for
 // narrow batches ("Part 6: GPU 加速", sections 4c and 4s).  Tokens are the
-// MFMA's M dimension (one or two 32-token tiles), output rows its N dimension
-// (32 per wave).
+// MFMA's M dimension (one or two 32-token tiles), output rows its N dimension.
 //
-//   * One v_mfma_i32_32x32x32_i8 per (token tile, block) gives the exact
-//     S_b of the 32x32 tile; one v_mfma_f32_32x32x8_f16 with only K slot 0
-//     populated gives the matching d_w * d_x outer product, exactly; the
-//     epilogue is acc += float(S_b) * scale.
-//   * A lane reads the block pair (68 bytes) of its row: the 20 bytes around
-//     its half of block 2p (re-aligned by 2 bytes), its half of block 2p + 1,
-//     and the dword holding block 2p + 1's scale.  Token rows are read the
-//     same way from x_q (L2-resident).  Everything is dword aligned.
-//   * The 4 waves of a workgroup take interleaved block pairs of the
-//     workgroup's K range and are summed through LDS in wave order; K ranges
-//     of different workgroups (split-K) go to partials that the ordered
-//     reduce kernel sums.  Every sum has a fixed order: results are
-//     deterministic.
+//   * The workgroup's K range goes through LDS in stages of 4 block pairs
+//     (272 bytes of every token and weight row), double-buffered, filled by
+//     direct global->LDS copies in which consecutive lanes read consecutive
+//     bytes of a row (16-byte copies where rows are whole 16-byte chunks,
+//     dword copies otherwise).  Reading the MFMA operand layout straight from
+//     memory instead (each lane its own row) left the kernel bound by
+//     address processing, 1.2-2x slower depending on the split.
+//   * Wave w takes pair w of each stage.  One v_mfma_i32_32x32x32_i8 per
+//     (token tile, block) gives the exact S_b of the 32x32 tile; one
+//     v_mfma_f32_32x32x8_f16 with only K slot 0 populated gives the matching
+//     d_w * d_x outer product, exactly; the epilogue is acc += float(S_b) * scale.
+//   * The 4 waves are summed through LDS in wave order; K ranges of different
+//     workgroups (split-K) go to partials that the ordered reduce kernel sums.
+//     Every sum has a fixed order: results are deterministic.
 #include <algorithm>
 
 #include "launch.h"
@@ -30,8 +29,6 @@
 
 namespace q8 {
 namespace {
-
-typedef uint32_t u32x4_a4s __attribute__((ext_vector_type(4), aligned(4)));
 
 struct SkinnyArgs {
   float *out;            // [n_tok][out_dim], or partials [n_split][n_tok][out_dim]
@@ -44,67 +41,161 @@ struct SkinnyArgs {
   int32_t pairs_per_split;
 };
 
-// The 10 dwords one lane needs of a block pair at p (dword aligned): F = the
-// 5 dwords holding its half of block 2p (2-byte offset), G = its half of
-// block 2p + 1, d8 = the dword holding block 2p + 1's scale.
-struct PairPart {
-  uint32_t F[5];
-  uint32_t G[4];
-  uint32_t d8;
+// A stage holds kStagePairs block pairs (one per wave) of every row of the
+// workgroup: 32 * MT token rows, then 32 weight rows, 272 bytes each.
+constexpr int kStagePairs = 4;
+constexpr int kStageRowBytes = kStagePairs * kPairBytes;  // 272
+constexpr int kStageRowDwords = kStageRowBytes / 4;       // 68
+constexpr int kCopyPeriod = 17;                           // 17 copies of 64 dwords = 16 rows
+static_assert(kCopyPeriod * 64 == 16 * kStageRowDwords, "copy pattern period");
+
+template <int MT>
+struct SkinnyStage {
+  static constexpr int XROWS = 32 * MT;
+  static constexpr int ROWS = XROWS + 32;
+  static constexpr int BYTES = ROWS * kStageRowBytes;
 };
 
-__device__ __forceinline__ void load_part(const uint8_t *pair, int h, PairPart &r) {
-  const u32x4_a4s f = *reinterpret_cast<const u32x4_a4s *>(pair + 16 * h);
-  const u32x4_a4s g = *reinterpret_cast<const u32x4_a4s *>(pair + 36 + 16 * h);
-  r.F[0] = f.x;
-  r.F[1] = f.y;
-  r.F[2] = f.z;
-  r.F[3] = f.w;
-  r.F[4] = *reinterpret_cast<const uint32_t *>(pair + 16 * h + 16);
-  r.G[0] = g.x;
-  r.G[1] = g.y;
-  r.G[2] = g.z;
-  r.G[3] = g.w;
-  r.d8 = *reinterpret_cast<const uint32_t *>(pair + 32);
+// One block of the wave's pair: operands from the staged rows, then per
+// token tile one int8 MFMA (S_b) and one scale MFMA (d_x * d_w), added as
+// acc += float(S_b) * scale.
+template <int B, int MT>
+__device__ __forceinline__ void skinny_block(const uint8_t *const (&xrow)[MT], const uint8_t *wrow,
+                                             int h, float (&acc)[MT][16]) {
+  typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+  const i32x16 izero = {};
+  const f32x16 fzero = {};
+  T4Raw rw;
+  t4_read<B>(wrow, h, rw);
+  uint32_t sw;
+  const i32x4 Bop = t4_prep<B>(rw, h, sw);
+  const f16x4 SB = __builtin_bit_cast(f16x4, u32x2{sw, 0u});
+#pragma unroll
+  for (int m = 0; m < MT; ++m) {
+    T4Raw rx;
+    t4_read<B>(xrow[m], h, rx);
+    uint32_t sx;
+    const i32x4 Aop = t4_prep<B>(rx, h, sx);
+    const f16x4 SA = __builtin_bit_cast(f16x4, u32x2{sx, 0u});
+    const i32x16 S = __builtin_amdgcn_mfma_i32_32x32x32_i8(Aop, Bop, izero, 0, 0, 0);
+    const f32x16 C = __builtin_amdgcn_mfma_f32_32x32x8f16(SA, SB, fzero, 0, 0, 0);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[m][r] = fmaf((float)S[r], C[r], acc[m][r]);
+  }
 }
 
-// MFMA operand (16 quant bytes) of block 2p + blk and its scale bits (only
-// for half 0 of a live slot; half 1 feeds the zero K slots of the scale
-// MFMA, and a zero scale on both sides makes a slot add exactly nothing).
-__device__ __forceinline__ i32x4 part_operand(const PairPart &r, int blk, bool keep, uint32_t &sc) {
-  if (blk == 0) {
-    sc = keep ? (r.F[0] & 0xFFFFu) : 0u;
-    return i32x4{(int)__builtin_amdgcn_alignbyte(r.F[1], r.F[0], 2),
-                 (int)__builtin_amdgcn_alignbyte(r.F[2], r.F[1], 2),
-                 (int)__builtin_amdgcn_alignbyte(r.F[3], r.F[2], 2),
-                 (int)__builtin_amdgcn_alignbyte(r.F[4], r.F[3], 2)};
+// Stage copies, dword granularity (any in_dim % 64 == 0): waves 0 .. MT-1
+// move token rows 32 w + r, waves 2 and 3 weight rows o_tile + 16 (w - 2) + r
+// (stage rows XROWS + 16 (w - 2) + r).  Lane l of copy k moves flat dword
+// 64 k + l of the wave's rows, through a buffer resource over them: rows past
+// the matrix, and bytes past the last row, lie outside its range and are not
+// read (what lands in LDS for them feeds only outputs that are not stored).
+template <int MT>
+struct DwordCopies {
+  static constexpr int XROWS = 32 * MT;
+  rsrc_t rsrc;
+  uint32_t off[kCopyPeriod];
+  int grp_rows = 0, first = 0, rows16, p_begin;
+
+  __device__ __forceinline__ DwordCopies(const SkinnyArgs &a, int wave, int lane, int64_t o_tile,
+                                         int pb)
+      : p_begin(pb) {
+    const uint8_t *gbase = a.w;
+    int64_t valid = 0;
+    if (wave < MT) {
+      grp_rows = 32;
+      first = 32 * wave;
+      gbase = a.x_q + (int64_t)first * a.row_bytes;
+      valid = a.n_tok - first;
+    } else if (wave >= 2) {
+      grp_rows = 16;
+      first = XROWS + 16 * (wave - 2);
+      const int64_t o0 = o_tile + 16 * (wave - 2);
+      gbase = a.w + o0 * a.row_bytes;
+      valid = a.out_dim - o0;
+    }
+    valid = valid < 0 ? 0 : (valid > grp_rows ? grp_rows : valid);
+    rsrc = make_rsrc(gbase, (uint32_t)(valid * a.row_bytes));
+#pragma unroll
+    for (int k = 0; k < kCopyPeriod; ++k) {
+      const int f = 64 * k + lane;
+      const int r = f / kStageRowDwords;
+      off[k] = (uint32_t)(r * (int)a.row_bytes + 4 * (f - r * kStageRowDwords));
+    }
+    rows16 = (int)(16 * a.row_bytes);
   }
-  sc = keep ? (r.d8 >> 16) : 0u;
-  return i32x4{(int)r.G[0], (int)r.G[1], (int)r.G[2], (int)r.G[3]};
-}
+
+  __device__ __forceinline__ void issue(uint8_t *stage, int s) const {
+    if (grp_rows == 0) return;
+    const uint32_t lds = (uint32_t)reinterpret_cast<uintptr_t>(stage + first * kStageRowBytes);
+    const int sb = (p_begin + s * kStagePairs) * kPairBytes;
+#pragma unroll
+    for (int k = 0; k < 2 * kCopyPeriod; ++k) {
+      if (k >= kCopyPeriod && grp_rows == 16) break;
+      buffer_load_lds_raw(rsrc,
+                          reinterpret_cast<__attribute__((address_space(3))) uint32_t *>(
+                              (uintptr_t)(lds + 256 * k)),
+                          4, (int)off[k % kCopyPeriod], sb + (k / kCopyPeriod) * rows16, 0, 0);
+    }
+  }
+};
+
+// Stage copies, 16-byte granularity (in_dim % 256 == 0, so every row and
+// every stage is whole 16-byte chunks, and 16-byte-aligned operands): the
+// stage's ROWS * 17 chunks, x rows then weight rows, go out as 64-chunk wave
+// copies, copy i taken by wave i % 4.  Rows past the matrix re-read its last
+// row (their outputs are not stored).
+template <int MT>
+struct ChunkCopies {
+  static constexpr int XROWS = 32 * MT;
+  static constexpr int CHUNKS = (XROWS + 32) * (kStageRowBytes / 16);
+  static constexpr int INSTS = (CHUNKS + 63) / 64;
+  static constexpr int PER_WAVE = (INSTS + 3) / 4;
+  const uint8_t *src[PER_WAVE];
+  int wave, lane, p_begin;
+
+  __device__ __forceinline__ ChunkCopies(const SkinnyArgs &a, int w, int l, int64_t o_tile, int pb)
+      : wave(w), lane(l), p_begin(pb) {
+#pragma unroll
+    for (int j = 0; j < PER_WAVE; ++j) {
+      const int c = min(64 * (wave + 4 * j) + lane, CHUNKS - 1);
+      const int row = c / (kStageRowBytes / 16);
+      const int part = c - row * (kStageRowBytes / 16);
+      const int64_t g = row < XROWS ? min<int64_t>(row, a.n_tok - 1)
+                                    : min<int64_t>(o_tile + row - XROWS, a.out_dim - 1);
+      src[j] = (row < XROWS ? a.x_q : a.w) + g * a.row_bytes + 16 * part;
+    }
+  }
+
+  __device__ __forceinline__ void issue(uint8_t *stage, int s) const {
+    const int64_t sb = (int64_t)(p_begin + s * kStagePairs) * kPairBytes;
+#pragma unroll
+    for (int j = 0; j < PER_WAVE; ++j) {
+      const int inst = wave + 4 * j;
+      if (inst < INSTS && 64 * inst + lane < CHUNKS)
+        __builtin_amdgcn_global_load_lds(src[j] + sb, stage + 1024 * inst, 16, 0, 0);
+    }
+  }
+};
 
 // MT token tiles of 32.  Grid: x = 32-row output tiles, y = K splits.
-template <int MT>
+template <int MT, class COPY>
 __global__ __launch_bounds__(256) void skinny_kernel(const SkinnyArgs a) {
-  __shared__ float red[4][MT][16][64];
+  using St = SkinnyStage<MT>;
+  __shared__ __attribute__((aligned(16))) uint8_t ring[2 * St::BYTES];
+  static_assert(4 * MT * 16 * 64 * sizeof(float) <= sizeof(ring), "reduction fits the ring");
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int n = lane & 31;
+  const int lrow = lane & 31;
   const int h = lane >> 5;
-  const int64_t o = (int64_t)blockIdx.x * 32 + n;
-  const int64_t lo = o < a.out_dim ? o : a.out_dim - 1;  // rows past the end re-read the last
-  const uint8_t *wrow = a.w + lo * a.row_bytes;
-  const uint8_t *xrow[MT];
-#pragma unroll
-  for (int m = 0; m < MT; ++m) {
-    const int64_t t = 32 * m + n;
-    xrow[m] = a.x_q + (t < a.n_tok ? t : a.n_tok - 1) * a.row_bytes;
-  }
+  const int64_t o_tile = (int64_t)blockIdx.x * 32;
   const int p_begin = blockIdx.y * a.pairs_per_split;
   const int p_end = min(p_begin + a.pairs_per_split, a.n_pairs);
-  // This wave's pairs: p_begin + wave, + 4, ... (count uniform per wave).
-  const int n_mine = p_begin + wave < p_end ? (p_end - p_begin - wave + 3) / 4 : 0;
+  const int nstages = (p_end - p_begin + kStagePairs - 1) / kStagePairs;
+
+  COPY copies(a, wave, lane, o_tile, p_begin);
+  auto issue = [&](int st, int buf) { copies.issue(ring + buf * St::BYTES, st); };
 
   float acc[MT][16];
 #pragma unroll
@@ -112,53 +203,38 @@ __global__ __launch_bounds__(256) void skinny_kernel(const SkinnyArgs a) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[m][r] = 0.0f;
 
-  const i32x16 izero = {};
-  const f32x16 fzero = {};
-  typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-
-  // The wave's pairs go in batches of NB: all loads of a batch are issued
-  // before its math, so one memory latency covers NB pairs.  Slots past the
-  // wave's last pair re-load that pair (same addresses) and run with zero
-  // scales, so every batch issues the same loads and the same math (a
-  // conditional use would let the compiler sink the loads into it).
-  constexpr int NB = 4;
-  for (int i0 = 0; i0 < n_mine; i0 += NB) {
-    PairPart wp[NB], xp[NB][MT];
+  issue(0, 0);
+  for (int s = 0; s < nstages; ++s) {
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's copies of stage s have landed
+    __syncthreads();                // ... and every wave's; buffer (s+1)&1 is free
+    if (s + 1 < nstages) issue(s + 1, (s + 1) & 1);
+    // Wave w takes pair w of the stage (blocks 2w, 2w+1), which starts 68 w
+    // bytes into each staged row: in the 136-byte slice w / 2, at block 0 or 2.
+    if (p_begin + s * kStagePairs + wave < p_end) {
+      const uint8_t *st = ring + (s & 1) * St::BYTES + 136 * (wave >> 1);
+      const uint8_t *xrow[MT];
 #pragma unroll
-    for (int j = 0; j < NB; ++j) {
-      const int p = p_begin + wave + 4 * min(i0 + j, n_mine - 1);
-      load_part(wrow + (int64_t)p * 68, h, wp[j]);
-#pragma unroll
-      for (int m = 0; m < MT; ++m) load_part(xrow[m] + (int64_t)p * 68, h, xp[j][m]);
-    }
-#pragma unroll
-    for (int j = 0; j < NB; ++j) {
-      const bool keep = h == 0 && i0 + j < n_mine;
-#pragma unroll
-      for (int blk = 0; blk < 2; ++blk) {
-        uint32_t sw;
-        const i32x4 B = part_operand(wp[j], blk, keep, sw);
-        const f16x4 SB = __builtin_bit_cast(f16x4, u32x2{sw, 0u});
-#pragma unroll
-        for (int m = 0; m < MT; ++m) {
-          uint32_t sx;
-          const i32x4 A = part_operand(xp[j][m], blk, keep, sx);
-          const f16x4 SA = __builtin_bit_cast(f16x4, u32x2{sx, 0u});
-          const i32x16 S = __builtin_amdgcn_mfma_i32_32x32x32_i8(A, B, izero, 0, 0, 0);
-          const f32x16 C = __builtin_amdgcn_mfma_f32_32x32x8f16(SA, SB, fzero, 0, 0, 0);
-#pragma unroll
-          for (int r = 0; r < 16; ++r) acc[m][r] = fmaf((float)S[r], C[r], acc[m][r]);
-        }
+      for (int m = 0; m < MT; ++m) xrow[m] = st + (32 * m + lrow) * kStageRowBytes;
+      const uint8_t *wrow = st + (St::XROWS + lrow) * kStageRowBytes;
+      if (wave & 1) {
+        skinny_block<2, MT>(xrow, wrow, h, acc);
+        skinny_block<3, MT>(xrow, wrow, h, acc);
+      } else {
+        skinny_block<0, MT>(xrow, wrow, h, acc);
+        skinny_block<1, MT>(xrow, wrow, h, acc);
       }
     }
   }
 
   // Sum the four waves in wave order; wave w finishes values r = 4w .. 4w+3.
+  __syncthreads();  // every wave is done with the ring
+  float(*red)[MT][16][64] = reinterpret_cast<float(*)[MT][16][64]>(ring);
 #pragma unroll
   for (int m = 0; m < MT; ++m)
 #pragma unroll
     for (int r = 0; r < 16; ++r) red[wave][m][r][lane] = acc[m][r];
   __syncthreads();
+  const int64_t o = o_tile + lrow;
   float *dst = a.out + (int64_t)blockIdx.y * a.n_tok * a.out_dim;
 #pragma unroll
   for (int m = 0; m < MT; ++m) {
@@ -167,7 +243,7 @@ __global__ __launch_bounds__(256) void skinny_kernel(const SkinnyArgs a) {
       const int r = 4 * wave + k;
       const float v = ((red[0][m][r][lane] + red[1][m][r][lane]) + red[2][m][r][lane]) +
                       red[3][m][r][lane];
-      // Element r of a lane: token 32 m + 8 (r / 4) + 4 h + r % 4, column n.
+      // Element r of a lane: token 32 m + 8 (r / 4) + 4 h + r % 4, column lrow.
       const int64_t t = 32 * m + 8 * (r >> 2) + 4 * h + (r & 3);
       if (t < a.n_tok && o < a.out_dim) dst[t * a.out_dim + o] = v;
     }
@@ -177,7 +253,8 @@ __global__ __launch_bounds__(256) void skinny_kernel(const SkinnyArgs a) {
 }  // namespace
 
 bool skinny_supported(int64_t in_dim, int64_t n_tok) {
-  return in_dim > 0 && in_dim % 64 == 0 && n_tok >= 1 && n_tok <= kSkinnyMaxTokens;
+  return in_dim > 0 && in_dim % 64 == 0 && (in_dim / 32) * kBlockBytes <= (1 << 24) && n_tok >= 1 &&
+         n_tok <= kSkinnyMaxTokens;
 }
 
 // Splits: enough workgroups for the chip (about 256), at least one pair per
@@ -200,7 +277,8 @@ hipError_t launch_skinny(float *out, const void *w, int64_t in_dim, int64_t out_
                          hipStream_t s) {
   SkinnyArgs a{};
   a.n_pairs = (int32_t)(in_dim / 64);
-  const int pps = (a.n_pairs + split - 1) / split;
+  // Splits are whole stages (the last one may be short).
+  const int pps = (((a.n_pairs + split - 1) / split + kStagePairs - 1) / kStagePairs) * kStagePairs;
   const int n_split = (a.n_pairs + pps - 1) / pps;
   a.out = n_split > 1 ? partials : out;
   a.w = static_cast<const uint8_t *>(w);
@@ -210,8 +288,16 @@ hipError_t launch_skinny(float *out, const void *w, int64_t in_dim, int64_t out_
   a.row_bytes = (in_dim / 32) * 34;
   a.pairs_per_split = pps;
   const dim3 grid((uint32_t)((out_dim + 31) / 32), (uint32_t)n_split);
-  if (n_tok > 32) hipLaunchKernelGGL(skinny_kernel<2>, grid, dim3(256), 0, s, a);
-  else hipLaunchKernelGGL(skinny_kernel<1>, grid, dim3(256), 0, s, a);
+  // 16-byte copies need whole 16-byte chunks: rows of 8k blocks, 16-aligned bases.
+  const bool wide = in_dim % 256 == 0 && (reinterpret_cast<uintptr_t>(w) & 15) == 0 &&
+                    (reinterpret_cast<uintptr_t>(x_q) & 15) == 0;
+  if (n_tok > 32) {
+    if (wide) hipLaunchKernelGGL((skinny_kernel<2, ChunkCopies<2>>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((skinny_kernel<2, DwordCopies<2>>), grid, dim3(256), 0, s, a);
+  } else {
+    if (wide) hipLaunchKernelGGL((skinny_kernel<1, ChunkCopies<1>>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((skinny_kernel<1, DwordCopies<1>>), grid, dim3(256), 0, s, a);
+  }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || n_split == 1) return err;
   return launch_splitk_reduce(out, partials, n_tok * out_dim, n_split, s);

@@ -158,10 +158,10 @@ def test_plan_regimes(q8):
     # Decode shapes stream weights through the matvec kernel.
     assert q8.q8_0_matmul_plan(1024, 32768, 1, 0) == (q8.KERNEL_MATVEC, 1)
     assert q8.q8_0_matmul_plan(32768, 1024, 1, 0) == (q8.KERNEL_MATVEC, 1)
-    assert q8.q8_0_matmul_plan(4096, 2048, 19, 0) == (q8.KERNEL_MATVEC, 1)
-    # From 20 to 64 tokens the skinny matrix-core kernel, split for about
+    assert q8.q8_0_matmul_plan(4096, 2048, 15, 0) == (q8.KERNEL_MATVEC, 1)
+    # From 16 to 64 tokens the skinny matrix-core kernel, split for about
     # 256 workgroups of 32 rows (at least one block pair per wave).
-    assert q8.q8_0_matmul_plan(4096, 2048, 20, 1 << 40) == (q8.KERNEL_SKINNY, 4)
+    assert q8.q8_0_matmul_plan(4096, 2048, 16, 1 << 40) == (q8.KERNEL_SKINNY, 4)
     assert q8.q8_0_matmul_plan(4096, 2048, 64, 1 << 40) == (q8.KERNEL_SKINNY, 4)
     assert q8.q8_0_matmul_plan(4096, 2048, 64, 0) == (q8.KERNEL_SKINNY, 1)
     assert q8.q8_0_matmul_plan(1024, 32768, 64, 1 << 40) == (q8.KERNEL_SKINNY, 1)
