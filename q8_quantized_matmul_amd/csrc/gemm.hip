@@ -486,12 +486,16 @@ __global__ __launch_bounds__(512, 1) void gemm_lds_kernel(const GemmArgs a) {
 // one tile (int32 -> fp32 convert + fma, the vector-ALU bound of this
 // method) overlaps the matrix-core work of the next, and two workgroups per
 // CU give each SIMD two such waves.  That fits LDS only with 4-block stages:
-// (128 token rows + 128 weight rows) x 136 bytes = 34 KB per stage, two
-// stages per workgroup.  136-byte row slices are not 16-byte multiples, so
-// the stage is filled by dword direct-to-LDS loads; lane l of copy
-// instruction k moves flat dword 64k + l of its wave's 64-row region, a
-// pattern that repeats every 17 instructions (32 rows), so 17 per-lane
-// offsets and a per-instruction scalar base address every copy.
+// a row's 4 blocks are 136 bytes, kept at a 144-byte LDS pitch so a stage
+// row is nine whole 16-byte chunks; (128 token rows + 128 weight rows) x 144
+// bytes = 36 KB per stage, two stages per workgroup.  The stage is filled by
+// 16-byte direct-to-LDS loads: lane l of copy instruction k moves chunk
+// 64k + l of its wave's 64-row region, i.e. row (64k + l) / 9, chunk
+// (64k + l) % 9, so nine instructions with nine per-lane offsets cover the
+// wave's rows.  Chunks 0..7 are slice bytes 0..127; chunk 8 is slice bytes
+// 120..135 (it overlaps chunk 7, so no copy reads outside the slice), which
+// puts slice bytes 128..135 at LDS offset 136..143: the upper half of the
+// fourth block's quants is read from 8 bytes further on.
 //
 // The MFMA's A operand is the token tile and B the weight tile, so a lane's
 // column of the result is an output column and the stores coalesce.  Only
@@ -501,12 +505,12 @@ namespace t4 {
 constexpr int BO = 128;                     // output rows per workgroup
 constexpr int BT = 128;                     // tokens per workgroup
 constexpr int KB = 4;                       // blocks per stage
-constexpr int RB = KB * kBlockBytes;        // 136 bytes per row per stage
-constexpr int RD = RB / 4;                  // 34 dwords
-constexpr int STAGE = (BO + BT) * RB;       // 34816 bytes
+constexpr int RB = 144;                     // LDS pitch of a row's 4-block slice (136 bytes used)
+constexpr int CH = RB / 16;                 // 9 chunks of 16 bytes per row
+constexpr int STAGE = (BO + BT) * RB;       // 36864 bytes
 constexpr int WAVE_BYTES = 64 * RB;         // each wave copies 64 rows
-constexpr int PERIOD = 17;                  // 17 * 64 dwords = 32 rows
-static_assert(PERIOD * 64 == 32 * RD, "copy pattern period");
+constexpr int NCOPY = 64 * CH / 64;         // 9 copy instructions per wave and stage
+static_assert(KB * kBlockBytes <= RB && RB % 16 == 0, "stage row pitch");
 }  // namespace t4
 
 __global__ __launch_bounds__(256, 2) void gemm_t4_kernel(const GemmArgs a) {
@@ -527,29 +531,29 @@ __global__ __launch_bounds__(256, 2) void gemm_t4_kernel(const GemmArgs a) {
   // Copies: waves 0, 1 move token rows t_tile + 64 w + r, waves 2, 3 weight
   // rows o_tile + 64 (w - 2) + r, into stage rows 64 w + r.  The base is
   // uniform per wave; each lane adds its 32-bit offset.
-  uint32_t off[PERIOD];
+  uint32_t off[NCOPY];
 #pragma unroll
-  for (int k = 0; k < PERIOD; ++k) {
+  for (int k = 0; k < NCOPY; ++k) {
     const int f = 64 * k + lane;
-    const int r = f / RD;
-    off[k] = (uint32_t)(r * (int)a.row_bytes + 4 * (f - r * RD));
+    const int r = f / CH;
+    const int j = f - r * CH;
+    off[k] = (uint32_t)(r * (int)a.row_bytes + (j < CH - 1 ? 16 * j : KB * kBlockBytes - 16));
   }
   // The wave's 64 rows as one buffer (64 * row_bytes <= 2^30: the launcher
-  // takes this kernel only for rows of at most 2^24 bytes); the row-group
-  // and stage offsets go in the scalar offset.
+  // takes this kernel only for rows of at most 2^24 bytes); the stage offset
+  // goes in the scalar offset.
   const uint8_t *copy_base = wave < 2 ? a.x_q + (t_tile + 64 * wave) * a.row_bytes
                                       : a.w + (o_tile + 64 * (wave - 2)) * a.row_bytes;
   const rsrc_t rsrc = make_rsrc(copy_base, (uint32_t)(64 * a.row_bytes));
-  const int half_rows = (int)(32 * a.row_bytes);
   auto issue = [&](int64_t b0, int buf) {
     const uint32_t lds = (uint32_t)reinterpret_cast<uintptr_t>(ring + buf * STAGE + wave * WAVE_BYTES);
     const int sb = (int)(b0 * kBlockBytes);
 #pragma unroll
-    for (int k = 0; k < 2 * PERIOD; ++k) {
+    for (int k = 0; k < NCOPY; ++k) {
       buffer_load_lds_raw(rsrc,
                           reinterpret_cast<__attribute__((address_space(3))) uint32_t *>(
-                              (uintptr_t)(lds + 256 * k)),
-                          4, (int)off[k % PERIOD], sb + (k / PERIOD) * half_rows, 0, 0);
+                              (uintptr_t)(lds + 1024 * k)),
+                          16, (int)off[k], sb, 0, 0);
     }
   };
 
@@ -591,13 +595,12 @@ __global__ __launch_bounds__(256, 2) void gemm_t4_kernel(const GemmArgs a) {
     const uint8_t *arow1 = arow0 + 32 * RB;
     const uint8_t *brow0 = st + (BT + 64 * wo + lrow) * RB;    // weight rows
     const uint8_t *brow1 = brow0 + 32 * RB;
-    const int64_t b0 = b_begin + (int64_t)s * KB;
 
     T4Raw ra0, ra1, rb0, rb1;
-    t4_read<0>(arow0, h, ra0);
-    t4_read<0>(arow1, h, ra1);
-    t4_read<0>(brow0, h, rb0);
-    t4_read<0>(brow1, h, rb1);
+    t4_read<0, true>(arow0, h, ra0);
+    t4_read<0, true>(arow1, h, ra1);
+    t4_read<0, true>(brow0, h, rb0);
+    t4_read<0, true>(brow1, h, rb1);
     [&]<int... B>(std::integer_sequence<int, B...>) {
       (([&] {
          uint32_t sa0, sa1, sb0, sb1;
@@ -607,10 +610,10 @@ __global__ __launch_bounds__(256, 2) void gemm_t4_kernel(const GemmArgs a) {
          const i32x4 B1 = t4_prep<B>(rb1, h, sb1);
          __builtin_amdgcn_sched_barrier(0);
          if constexpr (B + 1 < KB) {
-           t4_read<B + 1>(arow0, h, ra0);
-           t4_read<B + 1>(arow1, h, ra1);
-           t4_read<B + 1>(brow0, h, rb0);
-           t4_read<B + 1>(brow1, h, rb1);
+           t4_read<B + 1, true>(arow0, h, ra0);
+           t4_read<B + 1, true>(arow1, h, ra1);
+           t4_read<B + 1, true>(brow0, h, rb0);
+           t4_read<B + 1, true>(brow1, h, rb1);
          }
          __builtin_amdgcn_sched_barrier(0);
          const f16x4 SA[2] = {__builtin_bit_cast(f16x4, u32x2{sa0, 0u}),

@@ -277,17 +277,20 @@ __device__ __forceinline__ void quantize_pair4(const float4 (&v)[4], int j, uint
 // Staged rows in LDS (8-byte-aligned rows of 4-block, 136-byte slices).
 // LDS words of one operand of block B of a slice: a 24-byte (16 for B = 3)
 // 8-byte-aligned window holding the 16 quant bytes of half h, and for B = 3
-// the block's scale, which lies before that window.
+// the block's scale, which lies before that window.  With SPLIT_TAIL the
+// slice's bytes 128..135 sit 8 bytes further on (at 136..143; the GEMM's
+// 144-byte pitch), which moves block 3's upper half.
 struct T4Raw {
   uint32_t w[6];
   uint32_t sc;
 };
 
-template <int B>
+template <int B, bool SPLIT_TAIL = false>
 __device__ __forceinline__ void t4_read(const uint8_t *row, int h, T4Raw &r) {
   constexpr int M = (2 * B + 2) % 8;  // quant start modulo 8 (rows are 8-aligned)
   typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-  const u32x2 *q = reinterpret_cast<const u32x2 *>(row + B * kBlockBytes + 2 + 16 * h - M);
+  const u32x2 *q = reinterpret_cast<const u32x2 *>(row + B * kBlockBytes + 2 + 16 * h - M +
+                                                   (SPLIT_TAIL && B == 3 ? 8 * h : 0));
   const u32x2 a = q[0], b = q[1];
   r.w[0] = a.x;
   r.w[1] = a.y;
