@@ -483,9 +483,9 @@ __global__ __launch_bounds__(512, 1) void gemm_lds_kernel(const GemmArgs a) {
 // ---- Four-tile kernel: 128 x 128 workgroup tiles, 4 waves of 64 x 64.
 //
 // Each wave owns four independent 32x32 MFMA tiles, so the scale epilogue of
-// one tile (int32 -> fp32 convert + fma, the vector-ALU bound of this
-// method) overlaps the matrix-core work of the next, and two workgroups per
-// CU give each SIMD two such waves.  That fits LDS only with 4-block stages:
+// one tile (one fma per output and block; the int32 -> fp32 conversion runs
+// on the matrix core, see below) overlaps the matrix-core work of the next,
+// and two workgroups per CU give each SIMD two such waves.  That fits LDS only with 4-block stages:
 // a row's 4 blocks are 136 bytes, kept at a 144-byte LDS pitch so a stage
 // row is nine whole 16-byte chunks; (128 token rows + 128 weight rows) x 144
 // bytes = 36 KB per stage, two stages per workgroup.  The stage is filled by
@@ -561,7 +561,6 @@ __global__ __launch_bounds__(256, 2) void gemm_t4_kernel(const GemmArgs a) {
   const int wo = wave >> 1;  // outputs [64 wo, 64 wo + 64)
   const int lrow = lane & 31;
   const int h = lane >> 5;
-  const i32x16 izero = {};
   const f32x16 fzero = {};
   f32x16 acc[4];
 #pragma unroll
@@ -570,19 +569,31 @@ __global__ __launch_bounds__(256, 2) void gemm_t4_kernel(const GemmArgs a) {
     for (int r = 0; r < 16; ++r) acc[q][r] = 0.0f;
 
   typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-  // MFMA results of one tile.  Tile q of a block goes to slot q & 1 and its
-  // epilogue runs after the next tile's MFMAs are issued, from that slot; with
-  // four tiles per block the previous tile is always in the other slot.
+  // int32 -> fp32 on the matrix core.  The int8 MFMA accumulates onto
+  // 0x4B400000 (the bits of 1.5 * 2^23), so for |S_b| < 2^22 its result, read
+  // as fp32, is exactly 1.5 * 2^23 + S_b; a second f16 MFMA adds the constant
+  // product (-3072) * 4096 = -1.5 * 2^23 (K-slot 0, exact in f16 and fp32) to
+  // it, which leaves exactly float(S_b).  The vector ALU is then left with one
+  // fma per output and block instead of a convert and an fma.
+  const i32x16 ibias = {0x4B400000, 0x4B400000, 0x4B400000, 0x4B400000, 0x4B400000, 0x4B400000,
+                        0x4B400000, 0x4B400000, 0x4B400000, 0x4B400000, 0x4B400000, 0x4B400000,
+                        0x4B400000, 0x4B400000, 0x4B400000, 0x4B400000};
+  const f16x4 unbias_a = h ? f16x4{0, 0, 0, 0} : f16x4{(_Float16)-3072.0f, 0, 0, 0};
+  const f16x4 unbias_b = h ? f16x4{0, 0, 0, 0} : f16x4{(_Float16)4096.0f, 0, 0, 0};
+  // MFMA results of one tile: exact float(S_b) and the scale product.  Tile q
+  // of a block goes to slot q & 1 and its epilogue runs after the next tile's
+  // MFMAs are issued, from that slot; with four tiles per block the previous
+  // tile is always in the other slot.
   struct TileOut {
-    i32x16 S;
+    f32x16 S;
     f32x16 C;
   };
   TileOut slot[2];
-  slot[1].S = izero;  // the tile "before" the first: adds exactly 0
+  slot[1].S = fzero;  // the tile "before" the first: adds exactly 0
   slot[1].C = fzero;
   auto epilogue = [&]<int Q>(const TileOut &o) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) acc[Q][r] = fmaf((float)o.S[r], o.C[r], acc[Q][r]);
+    for (int r = 0; r < 16; ++r) acc[Q][r] = fmaf(o.S[r], o.C[r], acc[Q][r]);
   };
 
   issue(b_begin, 0);
@@ -626,14 +637,18 @@ __global__ __launch_bounds__(256, 2) void gemm_t4_kernel(const GemmArgs a) {
            (([&] {
               TileOut &cur = slot[Q & 1];
               const TileOut &prev = slot[(Q + 1) & 1];
-              cur.S = __builtin_amdgcn_mfma_i32_32x32x32_i8(AA[Q >> 1], BB[Q & 1], izero, 0, 0, 0);
+              const i32x16 biased =
+                  __builtin_amdgcn_mfma_i32_32x32x32_i8(AA[Q >> 1], BB[Q & 1], ibias, 0, 0, 0);
               cur.C = __builtin_amdgcn_mfma_f32_32x32x8f16(SA[Q >> 1], SB[Q & 1], fzero, 0, 0, 0);
+              cur.S = __builtin_amdgcn_mfma_f32_32x32x8f16(unbias_a, unbias_b,
+                                                          __builtin_bit_cast(f32x16, biased), 0, 0, 0);
               epilogue.template operator()<(Q + 3) & 3>(prev);
-#pragma unroll
-              for (int g = 0; g < 2; ++g) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // 1 MFMA
-                __builtin_amdgcn_sched_group_barrier(0x002, 16, 0);  // 16 VALU
-              }
+              // 3 MFMAs, the 16 fmas of the previous tile between them.
+              __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+              __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+              __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+              __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+              __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
               __builtin_amdgcn_sched_barrier(0);
             }()), ...);
          }(std::make_integer_sequence<int, 4>{});
