@@ -249,6 +249,39 @@ def test_mfma_whole_tiles_exact_integer_sums(only_block, split, out_dim):
     assert np.array_equal(ref.astype(np.float64), exact.astype(np.float64))
 
 
+def test_mfma_whole_tiles_extreme_block_sums():
+    # Block sums at the ends of their range, |S_b| = 32 * 127 * 127 = 516128,
+    # of both signs, next to sums of 0 and +-1: the four-tile kernel turns
+    # each block's int32 sum into fp32 on the matrix core (a biased
+    # accumulator and an exact unbias), which must stay exact across the
+    # whole range.  Unit scales keep every output an exact integer < 2^24.
+    in_dim, out_dim, n_tok = 512, 128, 128
+    nb = in_dim // 32
+    rng = np.random.default_rng(21)
+    qw = np.full((out_dim, nb, 32), 127, dtype=np.int64)
+    qw[::3] = -127                                   # rows of -127 as well
+    sign = rng.choice([-1, 1], size=(n_tok, nb, 1))
+    qx = np.broadcast_to(127 * sign, (n_tok, nb, 32)).copy()
+    qx[::5, :, :] = 0                                # S_b = 0
+    qx[1::5, :, :] = 0
+    qx[1::5, :, 0] = 1                               # S_b = +-127
+    qx[2::5, :, 1:] = 0
+    qx[2::5, :, 0] = -1                              # S_b = -+127
+
+    def blocks(q):
+        b = np.zeros(q.shape[:2] + (34,), dtype=np.uint8)
+        b[:, :, 1] = 0x3C                            # binary16 1.0
+        b[:, :, 2:] = q.astype(np.int8).view(np.uint8)
+        return b.reshape(q.shape[0], -1)
+
+    w_b, x_b = blocks(qw), blocks(qx)
+    got, ref = _run_outputs(torch.from_numpy(w_b).cuda(), torch.from_numpy(x_b).cuda(),
+                            w_b, x_b, in_dim, out_dim, n_tok, 1, "mfma4 extreme sums")
+    exact = np.einsum("tbk,obk->to", qx, qw)
+    assert np.abs(exact).max() < 2 ** 24
+    assert np.array_equal(got.astype(np.float64), exact.astype(np.float64))
+
+
 def test_subnormal_and_nan_scales():
     # Tiny weights give binary16-subnormal scales; a NaN-marked x block must
     # poison exactly the outputs of its token on every path.
