@@ -140,7 +140,7 @@ def bench_attn_q_b(torch, q8, wl, steps, warmup):
     kern_us = time_kernel(torch, step, ROT)
     mv_us = time_kernel(torch, lambda i: q8.q8_0_matmul(ws[i % ROT], xq, k, n, 1, out=out), ROT)
     quant_us = time_kernel(torch, lambda i: q8.q8_0_quantize_act(x, out=xq), ROT)
-    # Measured ceiling: a plain coalesced read of the same weight copies.
+    # Measured ceiling: a coalesced non-temporal streaming read of the same weight copies.
     sink = torch.zeros(1, dtype=torch.int32, device="cuda")
     read_us = time_kernel(torch, lambda i: q8.q8_0_probe_read(ws[i % ROT], sink), ROT)
     fused_bytes = n * row_bytes(k) + 4 * k + 4 * n       # W + fp32 x + out
@@ -392,7 +392,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4),
                      "measured_ceiling": {
-                         "kind": "coalesced streaming read of the same weight copies (q8_0_probe_read)",
+                         "kind": "coalesced non-temporal streaming read of the same weight copies (q8_0_probe_read)",
                          "GBs": round(h["read_bytes"] / (h["read_us"] * 1e-6) / 1e9, 1),
                          "frac": round(ach / (h["read_bytes"] / (h["read_us"] * 1e-6) / 1e9), 4)},
                      "traffic": profiled_traffic("matvec_list_attn_q_b.md"),
