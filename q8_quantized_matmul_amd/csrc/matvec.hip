@@ -219,16 +219,31 @@ struct LdsX {
   }
 };
 
+// Coalesced weight staging (COAL bodies): a wave's 64 pairs are 4352 bytes =
+// 1088 dwords; at most two such regions per wave, four waves.
+constexpr int kCoalDwords = 64 * kPairDwords;
+constexpr int kCoalRegions = 2;
+constexpr int kCoalLdsDwords = 4 * kCoalRegions * kCoalDwords;
+// Bodies that stage their weights this way: at most two regions per wave, and
+// rows of at least four pairs, so that the matrix ends on a 16-byte boundary
+// of every region (a 16-byte load is then wholly inside or wholly past it).
+constexpr bool coal_body(int lpr, int rg, int cpw) { return rg * cpw <= kCoalRegions && lpr >= 4; }
+
 // One workgroup tile of the matvec: TILE_ROWS weight rows against n_items x
 // rows.  `tile` is the tile index within the matrix; `w` and `items` the
 // (possibly per-expert) weights and item list.
 // PAIR: two weight matrices of the same shape (w and w2, the gate and up
 // projections) against the same x rows; the stored output is their SwiGLU.
+//
+// COAL: the weight rows come in through whole coalesced 16-byte non-temporal
+// loads, passed through a per-wave LDS region from which each lane reads its
+// pair, instead of per-lane 68-byte pair loads (wst: kCoalDwords dwords per
+// region, (RG * CPW) regions per wave).
 template <int LPR, int WPR, int CPW, int RG, bool GROUPED, bool STORE_S, class XS,
-          bool PAIR = false>
+          bool PAIR = false, bool COAL = false>
 __device__ __forceinline__ void matvec_body(const MatvecArgs &a, int64_t tile, const uint8_t *w,
                                             const int32_t *items, int64_t n_items, XS &xs,
-                                            const uint8_t *w2 = nullptr) {
+                                            const uint8_t *w2 = nullptr, uint32_t *wst = nullptr) {
   constexpr int RPW = 64 / LPR;                   // rows per wave row-group
   constexpr int ROWS_PER_SLOT = RG * RPW;
   constexpr int TILE_ROWS = (4 / WPR) * ROWS_PER_SLOT;
@@ -251,17 +266,72 @@ __device__ __forceinline__ void matvec_body(const MatvecArgs &a, int64_t tile, c
   // can leave the weight loads in flight.
   xs.prefetch();
   uint32_t wr[NM][RG][CPW][kPairDwords];
+  if constexpr (COAL) {
+    static_assert(!PAIR && coal_body(LPR, RG, CPW), "coalesced weight staging");
+    // A wave's 64 pairs of one (row group, chunk) are 4352 contiguous bytes:
+    // RPW whole rows, or one 64-pair chunk of a row.  Lane l loads 16-byte
+    // chunks l, l + 64, l + 128, l + 192 and then dword 1024 + l, so every
+    // lane issues the same five loads.  Loads of a region that reaches past
+    // the last row are clamped to the matrix's last bytes: what they bring
+    // feeds only outputs that are not stored, and nothing is read outside the
+    // matrix.  The loads go to registers (not direct to LDS) and nothing
+    // branches between them and the earlier x loads, so waiting for x does
+    // not wait for the weights.
+    const int wave_u = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const int64_t rb0 = tile * TILE_ROWS + (wave_u / WPR) * ROWS_PER_SLOT;
+    uint32_t *mine = wst + wave_u * (kCoalRegions * kCoalDwords);
+    const uint8_t *wend = w + a.out_dim * a.row_bytes;
+    u32x4_a4 ch[RG][CPW][4];
+    uint32_t tail[RG][CPW];
 #pragma unroll
-  for (int g = 0; g < RG; ++g) {
-    const int64_t row = row0 + g * RPW;
-    const int64_t lrow = row < a.out_dim ? row : a.out_dim - 1;
+    for (int g = 0; g < RG; ++g) {
 #pragma unroll
-    for (int c = 0; c < CPW; ++c) {
-      load_pair(w + lrow * a.row_bytes + pair_of[c] * kPairBytes, wr[0][g][c]);
-      if constexpr (PAIR) load_pair(w2 + lrow * a.row_bytes + pair_of[c] * kPairBytes, wr[NM - 1][g][c]);
+      for (int c = 0; c < CPW; ++c) {
+        const int64_t chunk0 = LPR < 64 ? 0 : (int64_t)(c * WPR + (wave_u % WPR)) * 64;
+        const uint8_t *src = w + (rb0 + g * RPW) * a.row_bytes + chunk0 * kPairBytes;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const uint8_t *p = src + 16 * (64 * k + lane);
+          ch[g][c][k] = __builtin_nontemporal_load(
+              reinterpret_cast<const u32x4_a4 *>(p < wend - 16 ? p : wend - 16));
+        }
+        const uint8_t *p = src + 4096 + 4 * lane;
+        tail[g][c] = __builtin_nontemporal_load(
+            reinterpret_cast<const uint32_t *>(p < wend - 4 ? p : wend - 4));
+      }
     }
+    xs.publish();
+    // Through this wave's LDS regions: write the region back in byte order,
+    // then lane l reads its pair at byte 68 l.  LDS operations of one wave
+    // run in order, so no barrier is needed.
+#pragma unroll
+    for (int g = 0; g < RG; ++g) {
+#pragma unroll
+      for (int c = 0; c < CPW; ++c) {
+        uint32_t *reg = mine + (g * CPW + c) * kCoalDwords;
+        u32x4_a4 *dst = reinterpret_cast<u32x4_a4 *>(reg);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) dst[64 * k + lane] = ch[g][c][k];
+        reg[1024 + lane] = tail[g][c];
+        __builtin_amdgcn_wave_barrier();
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+#pragma unroll
+        for (int i = 0; i < kPairDwords; ++i) wr[0][g][c][i] = reg[kPairDwords * lane + i];
+      }
+    }
+  } else {
+#pragma unroll
+    for (int g = 0; g < RG; ++g) {
+      const int64_t row = row0 + g * RPW;
+      const int64_t lrow = row < a.out_dim ? row : a.out_dim - 1;
+#pragma unroll
+      for (int c = 0; c < CPW; ++c) {
+        load_pair(w + lrow * a.row_bytes + pair_of[c] * kPairBytes, wr[0][g][c]);
+        if constexpr (PAIR) load_pair(w2 + lrow * a.row_bytes + pair_of[c] * kPairBytes, wr[NM - 1][g][c]);
+      }
+    }
+    xs.publish();
   }
-  xs.publish();
 
   for (int64_t it = 0; it < n_items; ++it) {
     xs.advance(it);
@@ -363,6 +433,11 @@ __global__ __launch_bounds__(256) void matvec_kernel(const MatvecArgs a) {
     __shared__ __attribute__((aligned(16))) uint32_t xbuf[2 * SX::BUF];
     SX xs{xbuf, a.x_q, a.row_bytes, items, n_items, (uint32_t)a.n_used, a.x_rows};
     matvec_body<LPR, WPR, CPW, RG, GROUPED, STORE_S>(a, blockIdx.x, w, items, n_items, xs);
+  } else if constexpr (!GROUPED && coal_body(LPR, RG, CPW)) {
+    __shared__ __attribute__((aligned(16))) uint32_t wst[kCoalLdsDwords];
+    GlobalX xs{a.x_q, a.row_bytes};
+    matvec_body<LPR, WPR, CPW, RG, GROUPED, STORE_S, GlobalX, false, true>(a, blockIdx.x, w, items,
+                                                                          n_items, xs, nullptr, wst);
   } else {
     GlobalX xs{a.x_q, a.row_bytes};
     matvec_body<LPR, WPR, CPW, RG, GROUPED, STORE_S>(a, blockIdx.x, w, items, n_items, xs);
@@ -548,8 +623,13 @@ struct ListArgs {
 };
 
 template <int LPR, int WPR, int CPW, int RG, class XS>
-__device__ __forceinline__ void list_tile(const MatvecArgs &m, int64_t tile, XS &xs) {
-  matvec_body<LPR, WPR, CPW, RG, false, false>(m, tile, m.w, nullptr, m.n_items, xs);
+__device__ __forceinline__ void list_tile(const MatvecArgs &m, int64_t tile, XS &xs,
+                                          uint32_t *wst) {
+  if constexpr (coal_body(LPR, RG, CPW))
+    matvec_body<LPR, WPR, CPW, RG, false, false, XS, false, true>(m, tile, m.w, nullptr,
+                                                                  m.n_items, xs, nullptr, wst);
+  else
+    matvec_body<LPR, WPR, CPW, RG, false, false>(m, tile, m.w, nullptr, m.n_items, xs);
 }
 
 // Row shapes with one 64-pair chunk per wave, and in_dim 32768 (two chunks on
@@ -558,35 +638,36 @@ __device__ __forceinline__ void list_tile(const MatvecArgs &m, int64_t tile, XS 
 // (decode5: 19.9 -> 18.4 us) and leave the list kernel at four waves per
 // SIMD, which the single-chunk shapes do not miss.
 template <int LPR, int WPR, int CPW, class XS>
-__device__ __forceinline__ void list_tile_rg(int rg, const MatvecArgs &m, int64_t tile, XS &xs) {
+__device__ __forceinline__ void list_tile_rg(int rg, const MatvecArgs &m, int64_t tile, XS &xs,
+                                             uint32_t *wst) {
   if constexpr (CPW == 1 || (CPW == 2 && WPR == 4)) {
     if (rg == 2) {
-      list_tile<LPR, WPR, CPW, 2>(m, tile, xs);
+      list_tile<LPR, WPR, CPW, 2>(m, tile, xs, wst);
       return;
     }
   }
-  list_tile<LPR, WPR, CPW, 1>(m, tile, xs);
+  list_tile<LPR, WPR, CPW, 1>(m, tile, xs, wst);
 }
 
 template <bool FUSED, class XS>
 __device__ __forceinline__ void list_dispatch(int code, int rg, const MatvecArgs &m, int64_t tile,
-                                              XS &xs) {
+                                              XS &xs, uint32_t *wst) {
   switch (code) {
-    case 0: list_tile_rg<1, 1, 1>(rg, m, tile, xs); break;
-    case 1: list_tile_rg<2, 1, 1>(rg, m, tile, xs); break;
-    case 2: list_tile_rg<4, 1, 1>(rg, m, tile, xs); break;
-    case 3: list_tile_rg<8, 1, 1>(rg, m, tile, xs); break;
-    case 4: list_tile_rg<16, 1, 1>(rg, m, tile, xs); break;
-    case 5: list_tile_rg<32, 1, 1>(rg, m, tile, xs); break;
-    case 6: list_tile_rg<64, 1, 1>(rg, m, tile, xs); break;
+    case 0: list_tile_rg<1, 1, 1>(rg, m, tile, xs, wst); break;
+    case 1: list_tile_rg<2, 1, 1>(rg, m, tile, xs, wst); break;
+    case 2: list_tile_rg<4, 1, 1>(rg, m, tile, xs, wst); break;
+    case 3: list_tile_rg<8, 1, 1>(rg, m, tile, xs, wst); break;
+    case 4: list_tile_rg<16, 1, 1>(rg, m, tile, xs, wst); break;
+    case 5: list_tile_rg<32, 1, 1>(rg, m, tile, xs, wst); break;
+    case 6: list_tile_rg<64, 1, 1>(rg, m, tile, xs, wst); break;
     default: break;
   }
   if constexpr (!FUSED) {
     switch (code) {
-      case 7: list_tile_rg<64, 2, 1>(rg, m, tile, xs); break;
-      case 8: list_tile_rg<64, 2, 2>(rg, m, tile, xs); break;
-      case 9: list_tile_rg<64, 4, 1>(rg, m, tile, xs); break;
-      case 10: list_tile_rg<64, 4, 2>(rg, m, tile, xs); break;
+      case 7: list_tile_rg<64, 2, 1>(rg, m, tile, xs, wst); break;
+      case 8: list_tile_rg<64, 2, 2>(rg, m, tile, xs, wst); break;
+      case 9: list_tile_rg<64, 4, 1>(rg, m, tile, xs, wst); break;
+      case 10: list_tile_rg<64, 4, 2>(rg, m, tile, xs, wst); break;
       default: break;
     }
   }
@@ -594,6 +675,7 @@ __device__ __forceinline__ void list_dispatch(int code, int rg, const MatvecArgs
 
 __global__ __launch_bounds__(256) void matvec_list_kernel(const ListArgs a) {
   __shared__ uint32_t xbuf[kFusePairs * kPairDwords];
+  __shared__ __attribute__((aligned(16))) uint32_t wst[kCoalLdsDwords];
   int i = 0;
   for (int j = 1; j < a.n_items; ++j)
     if ((int)blockIdx.x >= a.item[j].first_tile) i = j;
@@ -615,10 +697,10 @@ __global__ __launch_bounds__(256) void matvec_list_kernel(const ListArgs a) {
     xs.log2_ppr = __builtin_ctzll((uint64_t)(it.nb / 2));
     xs.n_pairs = a.n_tok << xs.log2_ppr;
     xs.in_dim = it.nb * kBlockElems;
-    list_dispatch<true>(it.shape, it.rg, m, tile, xs);
+    list_dispatch<true>(it.shape, it.rg, m, tile, xs, wst);
   } else {
     GlobalX xs{it.x_q, m.row_bytes};
-    list_dispatch<false>(it.shape, it.rg, m, tile, xs);
+    list_dispatch<false>(it.shape, it.rg, m, tile, xs, wst);
   }
 }
 
