@@ -632,15 +632,13 @@ __device__ __forceinline__ void list_tile(const MatvecArgs &m, int64_t tile, XS 
     matvec_body<LPR, WPR, CPW, RG, false, false>(m, tile, m.w, nullptr, m.n_items, xs);
 }
 
-// Row shapes with one 64-pair chunk per wave, and in_dim 32768 (two chunks on
-// each of four waves), take one or two row groups per wave slot; in_dim
-// 16384 takes one.  Two row groups on the widest rows halve their x reads
-// (decode5: 19.9 -> 18.4 us) and leave the list kernel at four waves per
-// SIMD, which the single-chunk shapes do not miss.
+// Row shapes with one 64-pair chunk per wave take one or two row groups per
+// wave slot; two-chunk rows take one, which keeps every body within two
+// coalesced-staging regions per wave.
 template <int LPR, int WPR, int CPW, class XS>
 __device__ __forceinline__ void list_tile_rg(int rg, const MatvecArgs &m, int64_t tile, XS &xs,
                                              uint32_t *wst) {
-  if constexpr (CPW == 1 || (CPW == 2 && WPR == 4)) {
+  if constexpr (CPW == 1) {
     if (rg == 2) {
       list_tile<LPR, WPR, CPW, 2>(m, tile, xs, wst);
       return;
@@ -752,8 +750,13 @@ hipError_t launch_matvec(float *out, int32_t *blocksums, const void *w, int64_t 
                          int64_t out_dim, const void *x_q, int64_t n_tok, hipStream_t s) {
   MatvecShape sh;
   if (!matvec_shape(in_dim, &sh)) return hipErrorInvalidValue;
-  const int rg = choose_rg(sh, out_dim, 1);
+  int rg = choose_rg(sh, out_dim, 1);
   const bool staged = n_tok >= 2;
+  // Single-token launches with rows of >= 4 pairs stage their weights through
+  // coalesced loads (at most two 64-pair regions per wave): cap the row groups
+  // to fit (in_dim 32768: one row group instead of four).
+  if (!staged && sh.lanes_per_row >= 4)
+    while (rg > 1 && rg * sh.chunks_per_wave > 2) rg /= 2;
   MatvecFn fn = blocksums ? pick_kernel<false, true>(sh, rg, staged)
                           : pick_kernel<false, false>(sh, rg, staged);
   if (!fn) return hipErrorInvalidValue;
@@ -927,8 +930,11 @@ hipError_t launch_matvec_list(const ListItem *items, int n_items, int64_t n_tok,
     d.out_dim = src.out_dim;
     d.nb = src.in_dim / kBlockElems;
     // Two row groups per wave slot where the item alone still fills 1024
-    // workgroups: fewer, fuller workgroups stay resident in one round.
-    const bool two = sh.chunks_per_wave == 1 || (sh.chunks_per_wave == 2 && sh.waves_per_row == 4);
+    // workgroups: fewer, fuller workgroups stay resident in one round.  Rows
+    // of two chunks per wave (in_dim 32768) keep one row group, so that their
+    // weights take the coalesced staging (at most two regions per wave):
+    // decode5 17.1 -> 15.1 us against two row groups with per-lane loads.
+    const bool two = sh.chunks_per_wave == 1;
     const int rg = (two && choose_rg(sh, src.out_dim, 1) >= 2) ? 2 : 1;
     d.shape = code;
     d.rg = rg;
