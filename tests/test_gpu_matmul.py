@@ -69,6 +69,25 @@ def test_matvec_shapes(in_dim):
     _run_and_check(wq, xq, wq_o, xq_o, in_dim, out_dim, n_tok, 1, where="generic")
 
 
+@pytest.mark.parametrize("out_dim", [1, 67, 300])
+@pytest.mark.parametrize("in_dim", [256, 512, 2048, 8192, 32768])
+def test_single_token_staged_weights(in_dim, out_dim):
+    # Single-token launches with rows of >= 4 pairs take their weights through
+    # coalesced loads and a per-wave LDS transpose; regions that reach past
+    # the last row are clamped to the matrix's end.  Out_dims that end inside
+    # a region, every row-chunk layout (4 and 32 pairs per row, 64-pair chunks
+    # over 2 and 4 waves, two chunks per wave), block sums and outputs.
+    w = workloads.normal((out_dim, in_dim), 0.02, "cuda", "st1", out_dim, in_dim, "w")
+    x = workloads.normal((1, in_dim), 1.0, "cuda", "st1", out_dim, in_dim, "x")
+    wq, xq, wq_o, xq_o = _prep(w, x)
+    _run_and_check(wq, xq, wq_o, xq_o, in_dim, out_dim, 1, 2, where="single-token matvec")
+    q8 = _q8()
+    got = q8.q8_0_matmul(wq, xq, in_dim, out_dim, 1)
+    torch.cuda.synchronize()
+    ref, mag, _ = oracle.matmul(wq_o, xq_o, in_dim)
+    assert_close(got.cpu().numpy(), ref, mag, "single-token auto plan")
+
+
 @pytest.mark.parametrize("n_tok", [1, 2, 5, 17, 33])
 @pytest.mark.parametrize("in_dim", [256, 1024, 4096, 16384])
 def test_matvec_token_counts(in_dim, n_tok):
