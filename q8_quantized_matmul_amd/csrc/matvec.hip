@@ -674,10 +674,18 @@ __device__ __forceinline__ void list_dispatch(int code, int rg, const MatvecArgs
 __global__ __launch_bounds__(256) void matvec_list_kernel(const ListArgs a) {
   __shared__ uint32_t xbuf[kFusePairs * kPairDwords];
   __shared__ __attribute__((aligned(16))) uint32_t wst[kCoalLdsDwords];
-  int i = 0;
-  for (int j = 1; j < a.n_items; ++j)
-    if ((int)blockIdx.x >= a.item[j].first_tile) i = j;
-  const ListItemDev it = a.item[i];
+  // The item of this workgroup: the last one whose first tile is at or below
+  // blockIdx.x.  The first tiles of all slots are read at once (no loop
+  // carried load), and item 0 is fetched beside them, so a one-item launch
+  // waits for a single round of argument loads.
+  ListItemDev it = a.item[0];
+  if (a.n_items > 1) {
+    int i = 0;
+#pragma unroll
+    for (int j = 1; j < kListMax; ++j)
+      if (j < a.n_items && (int)blockIdx.x >= a.item[j].first_tile) i = j;
+    if (i) it = a.item[i];
+  }
   MatvecArgs m{};
   m.out = it.out;
   m.w = it.w;
