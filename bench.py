@@ -396,7 +396,7 @@ def main():
                          "GBs": round(h["read_bytes"] / (h["read_us"] * 1e-6) / 1e9, 1),
                          "frac": round(ach / (h["read_bytes"] / (h["read_us"] * 1e-6) / 1e9), 4)},
                      "traffic": profiled_traffic("matvec_list_attn_q_b.md"),
-                     "kernel": "matvec_list_kernel (in-launch quantize + matvec)",
+                     "kernel": "matvec_fused_kernel (the one-item q8_0_matmul_list launch: in-launch quantize + matvec)",
                      "kernel_us": round(h["kernel_us"], 3), "bytes_per_launch": h["kernel_bytes"]},
         "separate_calls": {
             "ms_per_step": round(h["sec_separate"] * 1e3, 5),
