@@ -17,7 +17,10 @@
 //   * The per-element scale d_w[o] * d_x[t] of that block is the outer product
 //     of two binary16 vectors: one v_mfma_f32_32x32x8_f16 with only K-slot 0
 //     populated yields it exactly in fp32, in the same accumulator layout.
-//     The VALU then does 2 ops per element and block (int->float, fma).
+//     The VALU then does 2 ops per element and block (int->float, fma); the
+//     four-tile kernel moves the int->float conversion onto the matrix core
+//     as well (a biased int8 accumulator and an exact f16-MFMA unbias) and
+//     keeps one fma.
 //   * Workgroup = 4 waves in a 2x2 grid, each wave TI x TJ tiles of 32x32.
 //     A K-stage of KB blocks stages qs of 64*TI weight rows and 64*TJ token
 //     rows into LDS as aligned 16-byte chunks (row stride KB*32+16 bytes, so
