@@ -27,6 +27,7 @@
 //     (LdsX: the list launch); single-token launches read it per wave from
 //     global memory (GlobalX).
 #include <algorithm>
+#include <type_traits>
 
 #include "launch.h"
 #include "q8_device.h"
@@ -79,6 +80,12 @@ struct GlobalX {
     load_pair(x_q + xrow * row_bytes + pair * kPairBytes, d);
   }
 };
+
+// The same x source for the single-token matvec kernel, whose body loads
+// item 0's x pairs before the weights (attn_q_b separate matvec 7.78 -> 7.65
+// us on one box).  The list kernel keeps GlobalX: there the early load cost
+// decode5 15.0 -> 16.1 us.
+struct GlobalXFirst : GlobalX {};
 
 // StagedX: the x_q rows of the workgroup's items, XT at a time, copied into
 // LDS by direct global->LDS dword copies (64 consecutive dwords per wave
@@ -261,6 +268,16 @@ __device__ __forceinline__ void matvec_body(const MatvecArgs &a, int64_t tile, c
   for (int c = 0; c < CPW; ++c)
     pair_of[c] = (LPR < 64) ? (int64_t)(lane % LPR) : (int64_t)(c * WPR + part) * 64 + lane;
 
+  // A global x row is otherwise loaded only once the weights have landed:
+  // with GlobalXFirst (the single-token matvec kernel) item 0's pairs are
+  // loaded first here, so their latency overlaps the weight stream.  Callers
+  // launch with at least one item, and pair_of stays inside the row.
+  constexpr bool XPRE = std::is_same_v<XS, GlobalXFirst> && !GROUPED && CPW <= 2;
+  uint32_t xpre[CPW][kPairDwords];
+  if constexpr (XPRE) {
+#pragma unroll
+    for (int c = 0; c < CPW; ++c) xs.load(0, 0, pair_of[c], xpre[c]);
+  }
   // Every lane issues the same loads (rows past the end re-read the last row,
   // whose results are never stored), so the wait for the prefetched x rows
   // can leave the weight loads in flight.
@@ -349,7 +366,16 @@ __device__ __forceinline__ void matvec_body(const MatvecArgs &a, int64_t tile, c
 #pragma unroll
     for (int c = 0; c < CPW; ++c) {
       uint32_t xr[kPairDwords];
-      xs.load(it, xrow, pair_of[c], xr);
+      if constexpr (XPRE) {
+        if (it == 0) {
+#pragma unroll
+          for (int i = 0; i < kPairDwords; ++i) xr[i] = xpre[c][i];
+        } else {
+          xs.load(it, xrow, pair_of[c], xr);
+        }
+      } else {
+        xs.load(it, xrow, pair_of[c], xr);
+      }
       const float dxA = f16_bits_to_f32(xr[0]);
       const float dxB = f16_bits_to_f32(xr[8] >> 16);
 #pragma unroll
@@ -435,11 +461,11 @@ __global__ __launch_bounds__(256) void matvec_kernel(const MatvecArgs a) {
     matvec_body<LPR, WPR, CPW, RG, GROUPED, STORE_S>(a, blockIdx.x, w, items, n_items, xs);
   } else if constexpr (!GROUPED && coal_body(LPR, RG, CPW)) {
     __shared__ __attribute__((aligned(16))) uint32_t wst[kCoalLdsDwords];
-    GlobalX xs{a.x_q, a.row_bytes};
-    matvec_body<LPR, WPR, CPW, RG, GROUPED, STORE_S, GlobalX, false, true>(a, blockIdx.x, w, items,
-                                                                          n_items, xs, nullptr, wst);
+    GlobalXFirst xs{{a.x_q, a.row_bytes}};
+    matvec_body<LPR, WPR, CPW, RG, GROUPED, STORE_S, GlobalXFirst, false, true>(
+        a, blockIdx.x, w, items, n_items, xs, nullptr, wst);
   } else {
-    GlobalX xs{a.x_q, a.row_bytes};
+    GlobalXFirst xs{{a.x_q, a.row_bytes}};
     matvec_body<LPR, WPR, CPW, RG, GROUPED, STORE_S>(a, blockIdx.x, w, items, n_items, xs);
   }
 }
