@@ -226,6 +226,49 @@ struct LdsX {
   }
 };
 
+// LdsXWave: the one-item fused kernel when x has at most 16 pairs, which is
+// one wave's share of the quantizer: every wave quantizes the whole row into
+// its own 16-pair quarter of the buffer (lds points there), so no workgroup
+// barrier stands between the x loads and the dots.  The x_q copy is written
+// by wave 0 of the writer workgroup (x_q_out is null on the other waves).
+struct LdsXWave : LdsX {
+  __device__ __forceinline__ void prefetch() {
+    const int lane = threadIdx.x & 63;
+    const int j = lane & 3;
+    const int p = min(lane >> 2, n_pairs - 1);
+    const int row = p >> log2_ppr;
+    const int pp = p - (row << log2_ppr);
+    const float4 *src = reinterpret_cast<const float4 *>(x + row * in_dim + pp * 64 + j * 16);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) v[k] = src[k];
+  }
+  __device__ __forceinline__ void publish() {
+    const int lane = threadIdx.x & 63;
+    const int j = lane & 3;
+    const int p = lane >> 2;
+    uint32_t out[5];
+    quantize_pair4(v, j, out);
+    if (p < n_pairs) {
+      const int first = pair4_first(j), count = pair4_count(j);
+      uint32_t *l = lds + p * kPairDwords + first;
+#pragma unroll
+      for (int k = 0; k < 5; ++k)
+        if (k < count) l[k] = out[k];
+      if (x_q_out) {
+        uint32_t *g = reinterpret_cast<uint32_t *>(x_q_out + p * kPairBytes) + first;
+#pragma unroll
+        for (int k = 0; k < 5; ++k)
+          if (k < count) g[k] = out[k];
+      }
+    }
+    // LDS operations of one wave run in order: the wave's own reads of its
+    // quarter follow these writes without a workgroup barrier.
+    __builtin_amdgcn_wave_barrier();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  }
+};
+constexpr int kWaveXPairs = 16;
+
 // Coalesced weight staging (COAL bodies): a wave's 64 pairs are 4352 bytes =
 // 1088 dwords; at most two such regions per wave, four waves.
 constexpr int kCoalDwords = 64 * kPairDwords;
@@ -740,15 +783,18 @@ __global__ __launch_bounds__(256) void matvec_list_kernel(const ListArgs a) {
 // items (so the same outputs, bit for bit), in a kernel of its own with a
 // plain argument block and only that body's code.  Against the list kernel
 // this saves ~0.25 us per launch on the attn_q_b shape.
-template <int LPR, int RG>
+// WAVEX: at most kWaveXPairs pairs of x, quantized by every wave (LdsXWave).
+template <int LPR, int RG, bool WAVEX>
 __global__ __launch_bounds__(256) void matvec_fused_kernel(const MatvecArgs m, const float *x,
                                                            uint8_t *x_q_out) {
+  static_assert(4 * kWaveXPairs <= kFusePairs, "four wave quarters fit the x buffer");
   __shared__ uint32_t xbuf[kFusePairs * kPairDwords];
   __shared__ __attribute__((aligned(16))) uint32_t wst[kCoalLdsDwords];
-  LdsX xs;
-  xs.lds = xbuf;
+  std::conditional_t<WAVEX, LdsXWave, LdsX> xs;
+  const int wave = (int)(threadIdx.x >> 6);
+  xs.lds = WAVEX ? xbuf + wave * (kWaveXPairs * kPairDwords) : xbuf;
   xs.x = x;
-  xs.x_q_out = blockIdx.x == 0 ? x_q_out : nullptr;
+  xs.x_q_out = blockIdx.x == 0 && (!WAVEX || wave == 0) ? x_q_out : nullptr;
   xs.log2_ppr = __builtin_ctzll((uint64_t)(m.nb / 2));
   xs.n_pairs = (int)(m.n_items << xs.log2_ppr);
   xs.in_dim = m.nb * kBlockElems;
@@ -757,22 +803,28 @@ __global__ __launch_bounds__(256) void matvec_fused_kernel(const MatvecArgs m, c
 
 typedef void (*FusedFn)(const MatvecArgs, const float *, uint8_t *);
 
-template <int LPR>
+template <int LPR, bool WAVEX>
 FusedFn pick_fused_rg(int rg) {
-  return rg == 2 ? matvec_fused_kernel<LPR, 2> : matvec_fused_kernel<LPR, 1>;
+  return rg == 2 ? matvec_fused_kernel<LPR, 2, WAVEX> : matvec_fused_kernel<LPR, 1, WAVEX>;
 }
 
-FusedFn pick_fused(int code, int rg) {
+template <bool WAVEX>
+FusedFn pick_fused_shape(int code, int rg) {
   switch (code) {
-    case 0: return pick_fused_rg<1>(rg);
-    case 1: return pick_fused_rg<2>(rg);
-    case 2: return pick_fused_rg<4>(rg);
-    case 3: return pick_fused_rg<8>(rg);
-    case 4: return pick_fused_rg<16>(rg);
-    case 5: return pick_fused_rg<32>(rg);
-    case 6: return pick_fused_rg<64>(rg);
+    case 0: return pick_fused_rg<1, WAVEX>(rg);
+    case 1: return pick_fused_rg<2, WAVEX>(rg);
+    case 2: return pick_fused_rg<4, WAVEX>(rg);
+    case 3: return pick_fused_rg<8, WAVEX>(rg);
+    case 4: return pick_fused_rg<16, WAVEX>(rg);
+    case 5: return pick_fused_rg<32, WAVEX>(rg);
+    case 6: return pick_fused_rg<64, WAVEX>(rg);
     default: return nullptr;
   }
+}
+
+FusedFn pick_fused(int code, int rg, int64_t n_pairs) {
+  return n_pairs <= kWaveXPairs ? pick_fused_shape<true>(code, rg)
+                                : pick_fused_shape<false>(code, rg);
 }
 
 // Shape code of a matvec row shape, -1 when the list kernel has no body for
@@ -1019,7 +1071,7 @@ hipError_t launch_matvec_list(const ListItem *items, int n_items, int64_t n_tok,
   a.n_tok = (int32_t)n_tok;
   if (n_items == 1 && a.item[0].x) {
     const ListItemDev &d = a.item[0];
-    FusedFn fn = pick_fused(d.shape, d.rg);
+    FusedFn fn = pick_fused(d.shape, d.rg, n_tok * (d.nb / 2));
     if (!fn) return hipErrorInvalidValue;
     MatvecArgs m{};
     m.out = d.out;

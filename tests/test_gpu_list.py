@@ -129,6 +129,16 @@ def test_list_token_counts(n_tok):
     _run(specs, n_tok, f"ntok{n_tok}")
 
 
+@pytest.mark.parametrize("in_dim,n_tok", [(64, 1), (128, 3), (256, 4), (512, 2), (1024, 1),
+                                          (512, 3), (1024, 2), (2048, 1), (4096, 1)])
+def test_list_one_item_fused(in_dim, n_tok):
+    # One item with fp32 rows runs the dedicated fused kernel: with at most 16
+    # pairs of x every wave quantizes the rows itself, above that the
+    # workgroup shares one copy.  x_q is written too; 200 rows leave a ragged
+    # last tile.
+    _run([dict(in_dim=in_dim, out_dim=200, mode="x+xq")], n_tok, f"one{in_dim}x{n_tok}")
+
+
 @pytest.mark.parametrize("out_dim", [1, 3, 17, 1000])
 def test_list_ragged_rows_every_shape(out_dim):
     specs = [dict(in_dim=k, out_dim=out_dim, mode="x+xq" if k <= 4096 else "xq")
