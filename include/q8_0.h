@@ -28,8 +28,11 @@
  *     and returned as a negative Q8_0_E* code; nothing is written then.
  *   - n_tok == 0 or out_dim == 0 is a successful no-op.
  *   - Pointers must be at least 2-byte aligned (Q8_0_EALIGN otherwise); the
- *     fast kernels need 4-byte alignment (16-byte for fp32 inputs) and fall
- *     back to a generic kernel when it is missing.
+ *     fast kernels need 4-byte alignment (16-byte for fp32 inputs and for the
+ *     direct-to-LDS GEMM kernels) and fall back to a generic kernel when it is
+ *     missing.  The floor is 2 bytes, not 16, because Q8_0 rows are multiples
+ *     of 34 bytes: a slice starting at an odd block is only 2-byte aligned,
+ *     and such zero-copy views of a weight file are valid operands.
  *   - Results are deterministic: the same inputs give bit-identical outputs.
  *   - Calls on different streams touching disjoint outputs are independent.
  */
@@ -76,6 +79,8 @@ enum {
  * with amax == 0 (or d32 == 0) is all zeros.  A block holding a NaN or an
  * infinity, or whose d32 does not fit binary16 (d32 >= 65520), is stored with
  * scale 0x7E00 (NaN) and zero quants, so every output that uses it is NaN.
+ * (Such values are only seen by the device after the call has returned, so
+ * they are reported in the data rather than by a return code.)
  * Errors: in_dim % 32 != 0, negative sizes, null pointers -> Q8_0_EINVAL. */
 int q8_0_quantize_act(void *x_q, const float *x, int64_t n_tok, int64_t in_dim,
                       hipStream_t stream);
@@ -93,6 +98,10 @@ size_t q8_0_matmul_workspace_bytes(int64_t in_dim, int64_t out_dim, int64_t n_to
  *   workspace / workspace_bytes : optional caller scratch (device memory) for
  *     split-K partials; with less than q8_0_matmul_workspace_bytes() the
  *     library picks a plan that fits (same results up to fp32 summation order).
+ *     These two arguments are an addition to the pages' matmul signature: the
+ *     library allocates nothing ("Part 6: GPU 加速", summary: no allocation on
+ *     the hot path), so a split-K plan needs its partials from the caller;
+ *     NULL / 0 is always valid.
  * The fp32 result is within 1e-5 * sum_b |d_w d_x S_b| + 1e-6 of the exact
  * value; S_b itself is exact.  Errors: in_dim % 32 != 0 or in_dim == 0 with
  * out_dim > 0, negative sizes, null pointers -> Q8_0_EINVAL. */
@@ -100,13 +109,18 @@ int q8_0_matmul(float *out, const void *w, int64_t in_dim, int64_t out_dim,
                 const void *x_q, int64_t n_tok, void *workspace,
                 size_t workspace_bytes, hipStream_t stream);
 
-/* Workspace bytes q8_0_moe_grouped needs (routing tables and lists). */
+/* Workspace bytes q8_0_moe_grouped needs (routing tables and lists).  The
+ * size depends on the routing shape only (not on in_dim or out_dim): the
+ * workspace holds the per-expert counts, offsets and the pair list. */
 size_t q8_0_moe_workspace_bytes(int64_t n_tok, int32_t n_used, int32_t n_expert);
 
 /* Grouped expert matmul ("Part 6: 代码走读", trace 5: the gate/up and down
  * expert projections of ds4_gpu_routed_moe_one_tensor, one weight set per call).
  *   expert_w : DEVICE array of n_expert device pointers; expert e's weights are
- *              Q8_0 [out_dim][in_dim/32] blocks at expert_w[e].
+ *              Q8_0 [out_dim][in_dim/32] blocks at expert_w[e].  The table
+ *              lives on the device (like the pages' expert table, "Part 6: GPU
+ *              加速", section 4a) so a call copies nothing from the host and
+ *              can be captured in a HIP graph; build it once per weight set.
  *   selected : device int32 [n_tok][n_used], token -> expert ids (slot order).
  *   x_q      : Q8_0 rows; x_rows == 0: one row per token (gate/up input),
  *              x_rows == 1: one row per (token, slot) pair, row t*n_used + j

@@ -29,11 +29,7 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
-def build(verbose: bool = False) -> str:
-    srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    tmp = LIB + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, "-I", os.path.join(ROOT, "include"), "-I", CSRC,
-           "-o", tmp, *srcs]
+def _run(cmd, verbose, what):
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -43,9 +39,30 @@ def build(verbose: bool = False) -> str:
              and l.strip() != "1 warning generated."]
     if res.returncode != 0:
         sys.stderr.write(res.stderr)
-        raise RuntimeError("hipcc failed building libq8_0.so")
+        raise RuntimeError(f"hipcc failed building {what}")
     if verbose and noise:
         sys.stderr.write("\n".join(noise) + "\n")
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source to an object (in parallel), then link the library."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    objdir = os.path.join(PKG, "_build")
+    os.makedirs(objdir, exist_ok=True)
+    inc = ["-I", os.path.join(ROOT, "include"), "-I", CSRC]
+    compile_flags = [f for f in HIPCC_FLAGS if f != "-shared"]
+    jobs = []
+    for src in SOURCES:
+        obj = os.path.join(objdir, os.path.splitext(src)[0] + ".o")
+        jobs.append((obj, [hipcc(), *compile_flags, *inc, "-c", "-o", obj,
+                           os.path.join(CSRC, src)]))
+    workers = max(1, min(len(jobs), os.cpu_count() or 1, 8))
+    with ThreadPoolExecutor(workers) as pool:
+        list(pool.map(lambda j: _run(j[1], verbose, j[0]), jobs))
+    tmp = LIB + ".tmp"
+    _run([hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp,
+          *[obj for obj, _ in jobs]], verbose, "libq8_0.so")
     os.replace(tmp, LIB)
     return LIB
 

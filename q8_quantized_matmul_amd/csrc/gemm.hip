@@ -737,8 +737,12 @@ hipError_t launch_gemm(float *out, int32_t *blocksums, const void *w, int64_t in
                        int64_t out_dim, const void *x_q, int64_t n_tok, int split,
                        float *partials, hipStream_t s) {
   const int64_t nb = in_dim / kBlockElems;
-  const bool four = !blocksums && use_t4_kernel(nb, out_dim, n_tok);
-  const bool direct = !four && use_lds_kernel(nb, n_tok);
+  // The direct-to-LDS kernels copy 16-byte chunks; they take operands whose
+  // bases are 16-byte aligned (torch allocations are), the register-staged
+  // kernel the rest (it needs 4 bytes).
+  const bool a16 = ((reinterpret_cast<uintptr_t>(w) | reinterpret_cast<uintptr_t>(x_q)) & 15) == 0;
+  const bool four = a16 && !blocksums && use_t4_kernel(nb, out_dim, n_tok);
+  const bool direct = a16 && !four && use_lds_kernel(nb, n_tok);
   const int stage = four ? t4::KB : (direct ? lds::KB : kStageBlocks);
   int64_t bps = (nb + split - 1) / split;
   bps = (bps + stage - 1) / stage * stage;

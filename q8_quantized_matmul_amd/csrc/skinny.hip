@@ -87,20 +87,27 @@ __device__ __forceinline__ void skinny_block(const uint8_t *const (&xrow)[MT], c
 // Stage copies, dword granularity (any in_dim % 64 == 0): waves 0 .. MT-1
 // move token rows 32 w + r, waves 2 and 3 weight rows o_tile + 16 (w - 2) + r
 // (stage rows XROWS + 16 (w - 2) + r).  Lane l of copy k moves flat dword
-// 64 k + l of the wave's rows, through a buffer resource over them: rows past
-// the matrix, and bytes past the last row, lie outside its range and are not
-// read (what lands in LDS for them feeds only outputs that are not stored).
+// 64 k + l of a group of 16 rows.  Each group of 16 rows is read through a
+// buffer resource based at that group's first row plus the stage's byte
+// offset, whose range ends at the end of the wave's last valid row, and the
+// lane's whole offset is its 32-bit voffset: the hardware range check covers
+// voffset only (not the scalar offset), so everything a copy adds to the base
+// has to be in voffset or in the base.  Rows past the matrix, and the bytes
+// past the end of the last valid row (a short last stage), then lie outside
+// the range and read as zero; what lands in LDS for them feeds only outputs
+// that are not stored, or pairs past the split that no wave multiplies.
 template <int MT>
 struct DwordCopies {
   static constexpr int XROWS = 32 * MT;
-  rsrc_t rsrc;
+  const uint8_t *gbase = nullptr;
+  int64_t valid_bytes = 0;  // bytes of the wave's valid rows, from gbase
   uint32_t off[kCopyPeriod];
-  int grp_rows = 0, first = 0, rows16, p_begin;
+  int grp_rows = 0, first = 0, p_begin;
+  int64_t rows16;
 
   __device__ __forceinline__ DwordCopies(const SkinnyArgs &a, int wave, int lane, int64_t o_tile,
                                          int pb)
       : p_begin(pb) {
-    const uint8_t *gbase = a.w;
     int64_t valid = 0;
     if (wave < MT) {
       grp_rows = 32;
@@ -115,27 +122,34 @@ struct DwordCopies {
       valid = a.out_dim - o0;
     }
     valid = valid < 0 ? 0 : (valid > grp_rows ? grp_rows : valid);
-    rsrc = make_rsrc(gbase, (uint32_t)(valid * a.row_bytes));
+    valid_bytes = valid * a.row_bytes;
 #pragma unroll
     for (int k = 0; k < kCopyPeriod; ++k) {
       const int f = 64 * k + lane;
       const int r = f / kStageRowDwords;
       off[k] = (uint32_t)(r * (int)a.row_bytes + 4 * (f - r * kStageRowDwords));
     }
-    rows16 = (int)(16 * a.row_bytes);
+    rows16 = 16 * a.row_bytes;
   }
 
   __device__ __forceinline__ void issue(uint8_t *stage, int s) const {
     if (grp_rows == 0) return;
     const uint32_t lds = (uint32_t)reinterpret_cast<uintptr_t>(stage + first * kStageRowBytes);
-    const int sb = (p_begin + s * kStagePairs) * kPairBytes;
+    const int64_t sb = (int64_t)(p_begin + s * kStagePairs) * kPairBytes;
 #pragma unroll
-    for (int k = 0; k < 2 * kCopyPeriod; ++k) {
-      if (k >= kCopyPeriod && grp_rows == 16) break;
-      buffer_load_lds_raw(rsrc,
-                          reinterpret_cast<__attribute__((address_space(3))) uint32_t *>(
-                              (uintptr_t)(lds + 256 * k)),
-                          4, (int)off[k % kCopyPeriod], sb + (k / kCopyPeriod) * rows16, 0, 0);
+    for (int g = 0; g < 2; ++g) {
+      if (g == 1 && grp_rows == 16) break;
+      // Group g: rows 16 g .. 16 g + 15 of the wave, from byte sb of each row.
+      const int64_t start = sb + g * rows16;
+      const int64_t left = valid_bytes - start;
+      const rsrc_t rsrc = make_rsrc(gbase + start, (uint32_t)(left > 0 ? left : 0));
+#pragma unroll
+      for (int k = 0; k < kCopyPeriod; ++k) {
+        buffer_load_lds_raw(rsrc,
+                            reinterpret_cast<__attribute__((address_space(3))) uint32_t *>(
+                                (uintptr_t)(lds + 256 * (k + kCopyPeriod * g))),
+                            4, (int)off[k], 0, 0, 0);
+      }
     }
   }
 };

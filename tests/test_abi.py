@@ -33,6 +33,35 @@ def test_exports_every_declared_symbol(q8):
     assert set(declared) == set(q8.EXPORTED)
 
 
+def _prototype(name):
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    m = re.search(r"\b(\w[\w\s\*]*?)\b" + name + r"\s*\(([^;]*?)\)\s*;", text, flags=re.S)
+    assert m, name
+    ret = " ".join(m.group(1).split())
+    params = [" ".join(p.split()) for p in m.group(2).split(",")]
+    return ret, params
+
+
+def test_boundary_signatures():
+    """The three calls of the path and their departures from the plain
+    (out, w, in_dim, out_dim, x, n_tok) form: caller workspace for split-K,
+    a device expert table, and a workspace size without out_dim."""
+    assert _prototype("q8_0_quantize_act") == (
+        "int", ["void *x_q", "const float *x", "int64_t n_tok", "int64_t in_dim",
+                "hipStream_t stream"])
+    assert _prototype("q8_0_matmul") == (
+        "int", ["float *out", "const void *w", "int64_t in_dim", "int64_t out_dim",
+                "const void *x_q", "int64_t n_tok", "void *workspace", "size_t workspace_bytes",
+                "hipStream_t stream"])
+    assert _prototype("q8_0_moe_grouped") == (
+        "int", ["float *out", "const void *const *expert_w", "int32_t n_expert",
+                "int64_t in_dim", "int64_t out_dim", "const int32_t *selected",
+                "int32_t n_used", "const void *x_q", "int32_t x_rows", "int64_t n_tok",
+                "void *workspace", "size_t workspace_bytes", "hipStream_t stream"])
+    assert _prototype("q8_0_moe_workspace_bytes") == (
+        "size_t", ["int64_t n_tok", "int32_t n_used", "int32_t n_expert"])
+
+
 def test_strerror(q8):
     assert q8.q8_0_strerror(0) == "ok"
     for code in (-1, -2, -3, -4, -5):
