@@ -1,7 +1,8 @@
 """CPU oracle for the Q8_0 quantized matmul (TEST INFRASTRUCTURE ONLY).
 
-Thin ctypes wrapper over ``q8o.c``: a plain, slow, single-threaded C
-restatement of the method (see the header of ``q8o.c`` for the passages it
+Thin ctypes wrapper over ``q8o.c``: a plain, slow C restatement of the
+method (single-threaded unless ``set_threads`` asks for OpenMP threads over
+independent outputs, which gives bit-identical results) (see the header of ``q8o.c`` for the passages it
 follows and the readings it takes).  Only the tests, the smoke check and the
 benchmark's CPU-baseline leg may import this package.  It shares no code with
 the HIP library, and the HIP library never calls it.
@@ -27,7 +28,7 @@ _lib = None
 def build() -> str:
     """Compile q8o.c into oracle/libq8o.so with gcc (always recompiles)."""
     cmd = [
-        "gcc", "-std=c11", "-O2", "-ffp-contract=off", "-fno-fast-math",
+        "gcc", "-std=c11", "-O2", "-ffp-contract=off", "-fno-fast-math", "-fopenmp",
         "-fPIC", "-shared", "-Wall", "-Wextra", "-o", _LIB + ".tmp", _SRC, "-lm",
     ]
     subprocess.run(cmd, check=True)
@@ -43,6 +44,10 @@ def _load():
         build()
     lib = ctypes.CDLL(_LIB)
     i64, i32, vp = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p
+    lib.q8o_set_threads.argtypes = [ctypes.c_int]
+    lib.q8o_set_threads.restype = None
+    lib.q8o_get_threads.argtypes = []
+    lib.q8o_get_threads.restype = ctypes.c_int
     lib.q8o_f16_from_f32.argtypes = [ctypes.c_float]
     lib.q8o_f16_from_f32.restype = ctypes.c_uint16
     lib.q8o_f16_to_f64.argtypes = [ctypes.c_uint16]
@@ -59,6 +64,39 @@ def _load():
     lib.q8o_moe_combine.restype = None
     _lib = lib
     return lib
+
+
+def host_threads() -> int:
+    """Threads for the oracle on this host: OMP_NUM_THREADS if set (the
+    share of the host a job may use), else every core, at most 16."""
+    env = os.environ.get("OMP_NUM_THREADS", "")
+    n = int(env) if env.isdigit() and int(env) > 0 else (os.cpu_count() or 1)
+    return max(1, min(n, 16))
+
+
+def set_threads(n: int) -> None:
+    """OpenMP threads for the loops over independent outputs (1 = serial)."""
+    _load().q8o_set_threads(int(n))
+
+
+def get_threads() -> int:
+    return int(_load().q8o_get_threads())
+
+
+class threads:
+    """Context manager: run the oracle on n threads inside the block."""
+
+    def __init__(self, n: int | None = None):
+        self.n = host_threads() if n is None else n
+
+    def __enter__(self):
+        self.prev = get_threads()
+        set_threads(self.n)
+        return self
+
+    def __exit__(self, *exc):
+        set_threads(self.prev)
+        return False
 
 
 def _ptr(a: np.ndarray) -> int:

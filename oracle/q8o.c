@@ -5,9 +5,16 @@
  * the method, used by the tests, the smoke check and the benchmark's CPU
  * baseline.  Nothing here is shared with the GPU library.
  *
- * Build: gcc -std=c11 -O2 -ffp-contract=off -fno-fast-math -fPIC -shared
- * (no fast-math, no FMA contraction: every float operation is the IEEE one
- * that the source code spells out).
+ * Build: gcc -std=c11 -O2 -ffp-contract=off -fno-fast-math -fopenmp -fPIC
+ * -shared (no fast-math, no FMA contraction: every float operation is the
+ * IEEE one that the source code spells out).
+ *
+ * Threads: q8o_set_threads(n) lets the loops over independent outputs (rows
+ * of the quantizer, (token, output) pairs of the matmul, (token, slot) pairs
+ * of the grouped call) run on n OpenMP threads with a static partition.  Each
+ * output is computed by exactly the same code in the same order whatever the
+ * thread count, so results are bit-identical to the single-threaded run
+ * (tested).  The default is one thread.
  *
  * Readings of the pages taken here (the pages show a Q8_K snippet only; see
  * "Part 3: 模型架构", section 2, the ds4_quantize_row_q8_K listing):
@@ -35,6 +42,11 @@
 
 #define QK 32          /* values per Q8_0 block */
 #define BLOCK_BYTES 34 /* 2-byte binary16 scale + 32 int8 quants */
+
+static int g_threads = 1;
+
+void q8o_set_threads(int n) { g_threads = n < 1 ? 1 : n; }
+int q8o_get_threads(void) { return g_threads; }
 
 /* ---- binary16 ---------------------------------------------------------- */
 
@@ -128,6 +140,7 @@ static void quantize_block(const float *v, uint8_t *blk) {
 int q8o_quantize(const float *x, int64_t n_rows, int64_t k, uint8_t *blocks) {
     if (n_rows < 0 || k < 0 || k % QK != 0) return -1;
     int64_t nb = k / QK;
+    #pragma omp parallel for collapse(2) schedule(static) num_threads(g_threads)
     for (int64_t t = 0; t < n_rows; t++) {
         for (int64_t b = 0; b < nb; b++) {
             quantize_block(x + t * k + b * QK, blocks + (t * nb + b) * BLOCK_BYTES);
@@ -147,6 +160,7 @@ int q8o_matmul(const uint8_t *w, int64_t in_dim, int64_t out_dim,
                float *out, double *mag, int32_t *blocksums) {
     if (in_dim < 0 || out_dim < 0 || n_tok < 0 || in_dim % QK != 0) return -1;
     int64_t nb = in_dim / QK;
+    #pragma omp parallel for collapse(2) schedule(static) num_threads(g_threads)
     for (int64_t t = 0; t < n_tok; t++) {
         for (int64_t o = 0; o < out_dim; o++) {
             double acc = 0.0;
@@ -185,6 +199,9 @@ int q8o_moe_grouped(const uint8_t *const *expert_w, int32_t n_expert,
     }
     int64_t row_bytes = (in_dim / QK) * BLOCK_BYTES;
     int invalid = 0;
+    /* Pairs are independent; the matmul inside runs single-threaded there
+     * (nested parallel regions get one thread). */
+    #pragma omp parallel for collapse(2) schedule(static) num_threads(g_threads) reduction(+:invalid)
     for (int64_t t = 0; t < n_tok; t++) {
         for (int32_t j = 0; j < n_used; j++) {
             int64_t pair = t * n_used + j;

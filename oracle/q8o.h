@@ -1,8 +1,9 @@
 /*
  * q8o.h -- CPU oracle for the Q8_0 quantized matmul.
  *
- * TEST INFRASTRUCTURE ONLY.  This header and q8o.c are a plain, slow,
- * single-threaded restatement of what the GPU path computes.  Only the tests,
+ * TEST INFRASTRUCTURE ONLY.  This header and q8o.c are a plain, slow
+ * restatement of what the GPU path computes (optionally on several OpenMP
+ * threads over independent outputs).  Only the tests,
  * the smoke check and the benchmark's CPU-baseline leg may load it.  It shares
  * no code, header, table or helper with the HIP library.
  *
@@ -28,6 +29,12 @@
 #ifdef __cplusplus
 extern "C" {
 #endif
+
+/* OpenMP threads for the loops over independent outputs (default 1).  The
+ * results do not depend on it: every output is computed by the same code in
+ * the same order. */
+void q8o_set_threads(int n);
+int q8o_get_threads(void);
 
 /* IEEE 754 binary16 conversions, written from the format definition. */
 uint16_t q8o_f16_from_f32(float f);   /* round to nearest, ties to even */
