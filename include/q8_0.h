@@ -142,6 +142,29 @@ int q8_0_moe_grouped(float *out, const void *const *expert_w, int32_t n_expert,
                      int64_t n_tok, void *workspace, size_t workspace_bytes,
                      hipStream_t stream);
 
+/* For callers that cannot allocate device memory -- code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation: the grouped
+ * expert matmul of q8_0_moe_grouped without the workspace argument.  The
+ * routing tables go to a static device array inside the library instead, of
+ * Q8_0_MOE_STATIC_SCRATCH_BYTES bytes, which each GPU the library runs on
+ * holds until the process ends.  Arguments, results and errors are those of
+ * q8_0_moe_grouped (same kernels, bit-identical outputs), except:
+ *   n_invalid : optional device int32; when not NULL it receives, once the
+ *               stream reaches the end of the call, the number of pairs whose
+ *               expert id lies outside [0, n_expert) (their rows are NaN).
+ *   A routing shape with q8_0_moe_workspace_bytes(n_tok, n_used, n_expert)
+ *   above Q8_0_MOE_STATIC_SCRATCH_BYTES (about 260,000 (token, slot) pairs
+ *   at 256 experts) -> Q8_0_EWORKSPACE, nothing enqueued.
+ * The call allocates nothing.  Every call on one GPU shares that GPU's array
+ * (the routing writes every word it later reads, so no clearing is needed):
+ * calls that overlap on one GPU, e.g. on two streams at once, race and give
+ * undefined results; serialize them. */
+#define Q8_0_MOE_STATIC_SCRATCH_BYTES (1u << 20)
+int q8_0_moe_grouped_noalloc(float *out, const void *const *expert_w, int32_t n_expert,
+                             int64_t in_dim, int64_t out_dim, const int32_t *selected,
+                             int32_t n_used, const void *x_q, int32_t x_rows, int64_t n_tok,
+                             int32_t *n_invalid, hipStream_t stream);
+
 /* Arguments of q8_0_moe_ffn. */
 typedef struct q8_0_moe_ffn_args {
     float *out;                  /* fp32 [n_tok][d_model], written                  */

@@ -69,6 +69,8 @@ _sig = {
     "q8_0_moe_workspace_bytes": ([_i64, _i32, _i32], _sz),
     "q8_0_moe_grouped": ([_vp, _vp, _i32, _i64, _i64, _vp, _i32, _vp, _i32, _i64, _vp, _sz, _vp],
                          ctypes.c_int),
+    "q8_0_moe_grouped_noalloc": ([_vp, _vp, _i32, _i64, _i64, _vp, _i32, _vp, _i32, _i64, _vp,
+                                  _vp], ctypes.c_int),
     "q8_0_matmul_debug": ([_vp, _vp, _vp, _i64, _i64, _vp, _i64, _vp, _sz, _i32, _i32, _vp],
                           ctypes.c_int),
     "q8_0_moe_grouped_debug": ([_vp, _vp, _vp, _i32, _i64, _i64, _vp, _i32, _vp, _i32, _i64, _vp,
@@ -245,6 +247,26 @@ def q8_0_moe_grouped(table, n_expert, selected, x_q, in_dim, out_dim, x_rows=0, 
     out, _, ws = _moe(False, table, n_expert, selected, x_q, in_dim, out_dim, x_rows, out,
                       workspace)
     return out, ws
+
+
+MOE_STATIC_SCRATCH_BYTES = 1 << 20
+
+
+def q8_0_moe_grouped_noalloc(table, n_expert, selected, x_q, in_dim, out_dim, x_rows=0,
+                             out=None, n_invalid=None):
+    """q8_0_moe_grouped with the routing tables in the library's static
+    device array (the C call allocates nothing).  out is allocated here when
+    not given; n_invalid, an optional device int32 tensor of one element,
+    receives the count of invalid expert ids.  Returns out."""
+    n_tok, n_used = selected.shape
+    if out is None:
+        out = torch.empty((n_tok, n_used, out_dim), dtype=torch.float32, device=x_q.device)
+    _check(_lib.q8_0_moe_grouped_noalloc(
+        _dev(out, "out", torch.float32), _dev(table, "expert table", torch.int64), n_expert,
+        in_dim, out_dim, _dev(selected, "selected", torch.int32), n_used, _dev(x_q, "x_q"),
+        x_rows, n_tok, _dev(n_invalid, "n_invalid", torch.int32), _stream()),
+        "q8_0_moe_grouped_noalloc")
+    return out
 
 
 def q8_0_moe_grouped_debug(table, n_expert, selected, x_q, in_dim, out_dim, x_rows=0, out=None,

@@ -1,6 +1,8 @@
 // api.hip -- the C ABI of include/q8_0.h: host-side argument checks, kernel
 // selection and launches on the caller's stream.  Nothing here allocates
-// device memory; every buffer, including scratch, belongs to the caller.
+// device memory; every buffer, including scratch, belongs to the caller, except
+// the routing tables of q8_0_moe_grouped_noalloc, which live in a static
+// device array of the library (moe.hip).
 #include <stdint.h>
 
 #include <algorithm>
@@ -9,6 +11,9 @@
 
 #include "launch.h"
 #include "q8_0.h"
+
+static_assert(Q8_0_MOE_STATIC_SCRATCH_BYTES == q8::kMoeStaticScratchBytes,
+              "header and library agree on the static routing scratch");
 
 namespace {
 
@@ -128,10 +133,12 @@ int run_matmul(float *out, int32_t *blocksums, const void *w, int64_t in_dim, in
   }
 }
 
-int run_moe(float *out, int32_t *blocksums, const void *const *expert_w, int32_t n_expert,
-            int64_t in_dim, int64_t out_dim, const int32_t *selected, int32_t n_used,
-            const void *x_q, int32_t x_rows, int64_t n_tok, void *workspace,
-            size_t workspace_bytes, hipStream_t stream) {
+// Checks of the grouped call's arguments other than the workspace.  Returns
+// Q8_0_OK with *empty set when there is nothing to do.
+int validate_moe(const float *out, const void *const *expert_w, int32_t n_expert, int64_t in_dim,
+                 int64_t out_dim, const int32_t *selected, int32_t n_used, const void *x_q,
+                 int32_t x_rows, int64_t n_tok, bool *empty) {
+  *empty = true;
   if (n_expert < 1 || n_expert > kMaxExperts || n_used < 1 || n_tok < 0 || in_dim < 0 ||
       out_dim < 0 || (x_rows != 0 && x_rows != 1) || in_dim % Q8_0_BLOCK_ELEMS != 0)
     return Q8_0_EINVAL;
@@ -141,18 +148,56 @@ int run_moe(float *out, int32_t *blocksums, const void *const *expert_w, int32_t
   if (!out || !expert_w || !selected || !x_q) return Q8_0_EINVAL;
   if (!aligned(out, 4) || !aligned(selected, 4) || !aligned(expert_w, 8) || !aligned(x_q, 2))
     return Q8_0_EALIGN;
-  if (!workspace || workspace_bytes < q8_0_moe_workspace_bytes(n_tok, n_used, n_expert))
-    return Q8_0_EWORKSPACE;
-  if (!aligned(workspace, 16)) return Q8_0_EALIGN;
-  int st = check_device();
-  if (st != Q8_0_OK) return st;
+  *empty = false;
+  return Q8_0_OK;
+}
+
+int launch_moe_checked(float *out, int32_t *blocksums, const void *const *expert_w,
+                       int32_t n_expert, int64_t in_dim, int64_t out_dim,
+                       const int32_t *selected, int32_t n_used, const void *x_q, int32_t x_rows,
+                       int64_t n_tok, int32_t *ws, int32_t *invalid_out, hipStream_t stream) {
   // Expert matrices are only known on the device; the fast kernel needs the
   // x rows and every expert base dword aligned, which torch allocations and
   // even-block-count row slices satisfy.  x_q alignment is checked here.
   const bool fast = aligned(x_q, 4) && matvec_ok(in_dim);
   return status_of(q8::launch_moe(out, blocksums, expert_w, n_expert, in_dim, out_dim, selected,
-                                  n_used, x_q, x_rows, n_tok, static_cast<int32_t *>(workspace),
-                                  fast, stream));
+                                  n_used, x_q, x_rows, n_tok, ws, fast, stream, invalid_out));
+}
+
+int run_moe(float *out, int32_t *blocksums, const void *const *expert_w, int32_t n_expert,
+            int64_t in_dim, int64_t out_dim, const int32_t *selected, int32_t n_used,
+            const void *x_q, int32_t x_rows, int64_t n_tok, void *workspace,
+            size_t workspace_bytes, hipStream_t stream) {
+  bool empty = true;
+  int st = validate_moe(out, expert_w, n_expert, in_dim, out_dim, selected, n_used, x_q, x_rows,
+                        n_tok, &empty);
+  if (st != Q8_0_OK || empty) return st;
+  if (!workspace || workspace_bytes < q8_0_moe_workspace_bytes(n_tok, n_used, n_expert))
+    return Q8_0_EWORKSPACE;
+  if (!aligned(workspace, 16)) return Q8_0_EALIGN;
+  if ((st = check_device()) != Q8_0_OK) return st;
+  return launch_moe_checked(out, blocksums, expert_w, n_expert, in_dim, out_dim, selected, n_used,
+                            x_q, x_rows, n_tok, static_cast<int32_t *>(workspace), nullptr,
+                            stream);
+}
+
+// q8_0_moe_grouped_noalloc: the routing tables live in the library's static
+// device array (moe.hip) instead of caller workspace.
+int run_moe_noalloc(float *out, const void *const *expert_w, int32_t n_expert, int64_t in_dim,
+                    int64_t out_dim, const int32_t *selected, int32_t n_used, const void *x_q,
+                    int32_t x_rows, int64_t n_tok, int32_t *n_invalid, hipStream_t stream) {
+  bool empty = true;
+  int st = validate_moe(out, expert_w, n_expert, in_dim, out_dim, selected, n_used, x_q, x_rows,
+                        n_tok, &empty);
+  if (st != Q8_0_OK || empty) return st;
+  if (n_invalid && !aligned(n_invalid, 4)) return Q8_0_EALIGN;
+  if (q8_0_moe_workspace_bytes(n_tok, n_used, n_expert) > Q8_0_MOE_STATIC_SCRATCH_BYTES)
+    return Q8_0_EWORKSPACE;
+  if ((st = check_device()) != Q8_0_OK) return st;
+  int32_t *scratch = nullptr;
+  if (q8::moe_static_scratch(&scratch) != hipSuccess || !scratch) return Q8_0_ENODEV;
+  return launch_moe_checked(out, nullptr, expert_w, n_expert, in_dim, out_dim, selected, n_used,
+                            x_q, x_rows, n_tok, scratch, n_invalid, stream);
 }
 
 // Byte layout of the q8_0_moe_ffn workspace: routing ints, then mid, mid_q
@@ -356,6 +401,14 @@ int q8_0_moe_grouped(float *out, const void *const *expert_w, int32_t n_expert, 
                      hipStream_t stream) {
   return run_moe(out, nullptr, expert_w, n_expert, in_dim, out_dim, selected, n_used, x_q, x_rows,
                  n_tok, workspace, workspace_bytes, stream);
+}
+
+int q8_0_moe_grouped_noalloc(float *out, const void *const *expert_w, int32_t n_expert,
+                             int64_t in_dim, int64_t out_dim, const int32_t *selected,
+                             int32_t n_used, const void *x_q, int32_t x_rows, int64_t n_tok,
+                             int32_t *n_invalid, hipStream_t stream) {
+  return run_moe_noalloc(out, expert_w, n_expert, in_dim, out_dim, selected, n_used, x_q, x_rows,
+                         n_tok, n_invalid, stream);
 }
 
 int q8_0_moe_grouped_debug(float *out, int32_t *blocksums, const void *const *expert_w,

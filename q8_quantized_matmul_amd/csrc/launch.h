@@ -61,7 +61,12 @@ struct MoeLayout {
 MoeLayout moe_layout(int64_t n_tok, int32_t n_used, int32_t n_expert);
 hipError_t launch_moe_route(const int32_t *selected, int64_t n_tok, int32_t n_used,
                             int32_t n_expert, int32_t *ws, float *nan_rows, int64_t nan_dim,
-                            hipStream_t s);
+                            hipStream_t s, int32_t *invalid_out);
+// Routing tables of q8_0_moe_grouped_noalloc: a static device array of this
+// many bytes; moe_static_scratch gives its address on the current device.
+constexpr size_t kMoeStaticScratchBytes = size_t{1} << 20;
+constexpr int kMaxDevicesStatic = 64;
+hipError_t moe_static_scratch(int32_t **ptr);
 // The routed expert FFN: buffers already validated, intermediates placed.
 struct MoeFfn {
   float *out;
@@ -81,7 +86,7 @@ hipError_t launch_moe(float *out, int32_t *blocksums, const void *const *expert_
                       int32_t n_expert, int64_t in_dim, int64_t out_dim,
                       const int32_t *selected, int32_t n_used, const void *x_q,
                       int32_t x_rows, int64_t n_tok, int32_t *workspace, bool fast,
-                      hipStream_t s);
+                      hipStream_t s, int32_t *invalid_out = nullptr);
 
 // skinny.hip: matrix-core matmul for up to kSkinnyMaxTokens tokens, weights
 // streamed into registers, split-K through caller partials.

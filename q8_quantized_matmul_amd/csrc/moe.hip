@@ -18,6 +18,8 @@
 // ballots (lanes sharing an expert id are found bit by bit) and waves taking
 // their turn in index order.  The ids are read from memory once, in the
 // counting pass, and kept in LDS.
+#include <mutex>
+
 #include "launch.h"
 #include "q8_device.h"
 
@@ -41,7 +43,7 @@ __device__ __forceinline__ int32_t wave_inclusive_scan(int32_t v, int lane) {
 __global__ __launch_bounds__(kRouteThreads) void moe_route_kernel(
     const int32_t *__restrict__ selected, int64_t n_pairs, int32_t n_expert, int32_t key_bits,
     int32_t *__restrict__ ws, int64_t off_counts, int64_t off_offsets, int64_t off_pairs,
-    float *__restrict__ out, int64_t out_dim) {
+    float *__restrict__ out, int64_t out_dim, int32_t *__restrict__ invalid_out) {
   extern __shared__ int32_t lds[];
   int32_t *running = lds;                  // [n_expert]
   int32_t *keys = lds + n_expert;          // [kKeyChunk]
@@ -91,6 +93,7 @@ __global__ __launch_bounds__(kRouteThreads) void moe_route_kernel(
   if (tid == 0) {
     ws[off_offsets + n_expert] = total;
     ws[0] = invalid;
+    if (invalid_out) *invalid_out = invalid;
   }
   __syncthreads();
 
@@ -157,23 +160,25 @@ size_t moe_route_lds_bytes(int32_t n_expert) {
 
 hipError_t launch_moe_route(const int32_t *selected, int64_t n_tok, int32_t n_used,
                             int32_t n_expert, int32_t *ws, float *nan_rows, int64_t nan_dim,
-                            hipStream_t s) {
+                            hipStream_t s, int32_t *invalid_out) {
   const MoeLayout L = moe_layout(n_tok, n_used, n_expert);
   const int64_t n_pairs = n_tok * n_used;
   int key_bits = 1;
   while ((1ll << key_bits) <= (int64_t)n_expert) ++key_bits;  // n_expert itself is the sentinel
   hipLaunchKernelGGL(moe_route_kernel, dim3(1), dim3(kRouteThreads), moe_route_lds_bytes(n_expert),
                      s, selected, n_pairs, n_expert, key_bits, ws, L.counts, L.offsets, L.pairs,
-                     nan_rows, nan_dim);
+                     nan_rows, nan_dim, invalid_out);
   return hipGetLastError();
 }
 
 hipError_t launch_moe(float *out, int32_t *blocksums, const void *const *expert_w,
                       int32_t n_expert, int64_t in_dim, int64_t out_dim,
                       const int32_t *selected, int32_t n_used, const void *x_q, int32_t x_rows,
-                      int64_t n_tok, int32_t *ws, bool fast, hipStream_t s) {
+                      int64_t n_tok, int32_t *ws, bool fast, hipStream_t s,
+                      int32_t *invalid_out) {
   const MoeLayout L = moe_layout(n_tok, n_used, n_expert);
-  hipError_t err = launch_moe_route(selected, n_tok, n_used, n_expert, ws, out, out_dim, s);
+  hipError_t err =
+      launch_moe_route(selected, n_tok, n_used, n_expert, ws, out, out_dim, s, invalid_out);
   if (err != hipSuccess) return err;
   if (fast) {
     return launch_matvec_grouped(out, blocksums, expert_w, n_expert, in_dim, out_dim, x_q, x_rows,
@@ -181,6 +186,39 @@ hipError_t launch_moe(float *out, int32_t *blocksums, const void *const *expert_
   }
   return launch_generic_grouped(out, blocksums, expert_w, n_expert, in_dim, out_dim, selected,
                                 n_used, x_q, x_rows, n_tok, s);
+}
+
+// ---- Routing tables without caller workspace.
+//
+// For callers that cannot allocate device memory, q8_0_moe_grouped_noalloc
+// keeps the routing tables (the same layout as the caller workspace of
+// q8_0_moe_grouped) in this file-scope device array.  Each GPU the library
+// runs on holds its own copy until the process ends.  In host code the
+// array's name is only a host-side stand-in for the symbol, never a device
+// address: the device address comes from hipGetSymbolAddress, looked up once
+// per device with that device current, and only that address is passed to
+// kernels.  Every call on one GPU shares the array; the routing kernel writes
+// every word a call reads before reading it, so nothing needs clearing, and
+// calls that overlap on one GPU (different streams) race on it.
+static __device__ __align__(256) int32_t scratch[kMoeStaticScratchBytes / sizeof(int32_t)];
+
+hipError_t moe_static_scratch(int32_t **ptr) {
+  static std::mutex mu;
+  static int32_t *per_device[kMaxDevicesStatic] = {};
+  int dev = -1;
+  hipError_t err = hipGetDevice(&dev);
+  if (err != hipSuccess) return err;
+  if (dev < 0 || dev >= kMaxDevicesStatic) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!per_device[dev]) {
+    void *p = nullptr;
+    err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (err != hipSuccess) return err;
+    if (!p) return hipErrorInvalidSymbol;
+    per_device[dev] = static_cast<int32_t *>(p);
+  }
+  *ptr = per_device[dev];
+  return hipSuccess;
 }
 
 namespace {
@@ -210,7 +248,8 @@ hipError_t launch_moe_ffn(const MoeFfn &f, int32_t *ws, hipStream_t s) {
   const MoeLayout L = moe_layout(f.n_tok, f.n_used, f.n_expert);
   const int64_t n_pairs = f.n_tok * f.n_used;
   // 1. Routing; the down outputs of pairs with an invalid id are set to NaN.
-  hipError_t err = launch_moe_route(f.selected, f.n_tok, f.n_used, f.n_expert, ws, f.y, f.d_model, s);
+  hipError_t err =
+      launch_moe_route(f.selected, f.n_tok, f.n_used, f.n_expert, ws, f.y, f.d_model, s, nullptr);
   if (err != hipSuccess) return err;
   // 2. gate and up of every pair in one pass, SwiGLU into mid.
   err = launch_matvec_grouped_pair(f.mid, f.gate_w, f.up_w, f.n_expert, f.d_model, f.d_ff, f.x_q,

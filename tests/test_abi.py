@@ -27,7 +27,7 @@ def q8():
 def test_exports_every_declared_symbol(q8):
     lib = ctypes.CDLL(q8.LIB_PATH)
     declared = _declared()
-    assert len(declared) == 14
+    assert len(declared) == 15
     for name in declared:
         assert hasattr(lib, name), name
     assert set(declared) == set(q8.EXPORTED)
@@ -123,6 +123,29 @@ def test_moe_validation(q8):
     assert call(ws_bytes=need - 4) == q8.Q8_0_EWORKSPACE
     assert call(ws=None) == q8.Q8_0_EWORKSPACE
     assert call(n_tok=0) == q8.Q8_0_OK
+
+
+def test_moe_noalloc_validation(q8):
+    lib = q8.raw_library()
+    mo = lib.q8_0_moe_grouped_noalloc
+    assert q8.MOE_STATIC_SCRATCH_BYTES == 1 << 20
+
+    def call(n_expert=256, in_dim=4096, out_dim=2048, n_used=8, x_rows=0, n_tok=64, inv=None,
+             out=FAKE):
+        return mo(out, FAKE, n_expert, in_dim, out_dim, FAKE, n_used, FAKE, x_rows, n_tok, inv,
+                  None)
+
+    assert call(n_expert=0) == q8.Q8_0_EINVAL
+    assert call(n_used=0) == q8.Q8_0_EINVAL
+    assert call(x_rows=2) == q8.Q8_0_EINVAL
+    assert call(in_dim=4100) == q8.Q8_0_EINVAL
+    assert call(out=FAKE + 2) == q8.Q8_0_EALIGN
+    assert call(inv=FAKE + 2) == q8.Q8_0_EALIGN
+    assert call(n_tok=0) == q8.Q8_0_OK
+    # The largest routing shape the static tables hold, and one pair more.
+    ints = q8.MOE_STATIC_SCRATCH_BYTES // 4 - (16 + 2 * 256 + 1)
+    assert q8.q8_0_moe_workspace_bytes(ints, 1, 256) <= q8.MOE_STATIC_SCRATCH_BYTES
+    assert call(n_tok=ints + 1, n_used=1) == q8.Q8_0_EWORKSPACE
 
 
 def test_list_validation(q8):
