@@ -81,19 +81,27 @@ def capture(torch, fn, n):
 
 
 def time_steps(torch, fn, steps, warmup, per_graph=ROT):
-    """Whole-step throughput: `steps` steps as replays of a graph holding
-    `per_graph` consecutive steps, wall clock bracketed by synchronize."""
+    """Whole-step throughput: exactly `steps` steps, as replays of a graph
+    holding `per_graph` consecutive steps fn(0..per_graph-1) plus one graph of
+    the remaining steps, wall clock bracketed by synchronize.  `warmup`
+    untimed steps run first, the same way."""
+    steps = max(1, int(steps))
+    per_graph = max(1, min(per_graph, steps))
     g = capture(torch, fn, per_graph)
-    reps = max(1, -(-steps // per_graph))
-    for _ in range(max(1, warmup // per_graph)):
+    rest = steps % per_graph
+    g_rest = capture(torch, fn, rest) if rest else None
+    full = steps // per_graph
+    for _ in range(-(-max(0, warmup) // per_graph)):
         g.replay()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(reps):
+    for _ in range(full):
         g.replay()
+    if g_rest is not None:
+        g_rest.replay()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    return (t1 - t0) / (reps * per_graph), reps * per_graph
+    return (t1 - t0) / steps, steps
 
 
 def time_kernel(torch, fn, n_per_graph, reps=20):
@@ -325,27 +333,119 @@ def bench_prefill(torch, q8, wl, name, steps, warmup):
                 plan=q8.q8_0_matmul_plan(k, n, t, ws.numel()))
 
 
-def cpu_baseline(wl, seconds):
-    """The oracle (single-threaded C, as committed) on the attn_q_b workload,
-    repeated for about `seconds` seconds on this host's CPU."""
-    import numpy as np
-    import oracle
-    d = wl.attn_q_b("cpu")
-    wq = oracle.quantize(d["w"].numpy())
-    x = d["x"].numpy()
-    k, n = d["in_dim"], d["out_dim"]
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _time_cpu(fn, seconds):
+    """Mean seconds per call of fn, repeated for about `seconds` (at least once)."""
     reps, t0 = 0, time.perf_counter()
     while True:
-        xq = oracle.quantize(x)
-        oracle.matmul(wq, xq, k, want_mag=False)
+        fn()
         reps += 1
         if time.perf_counter() - t0 >= seconds:
             break
-    sec = (time.perf_counter() - t0) / reps
-    step_bytes = n * row_bytes(k) + row_bytes(k) + 4 * n + 4 * k + row_bytes(k)
-    return dict(value=round(step_bytes / sec / 1e9, 4), unit="GB/s", cores=1, kind="oracle",
-                sample=f"full attn_q_b step (quantize 1x1024 + matmul 32768x1024), {reps} repetitions "
-                       f"in {reps * sec:.1f} s, single thread; {np.round(sec * 1e3, 2)} ms/step")
+    return (time.perf_counter() - t0) / reps, reps
+
+
+def cpu_baseline(wl, seconds):
+    """The oracle (plain C as committed) on every workload, on this host's CPU:
+    once single-threaded and once on the host's cores (OpenMP over independent
+    outputs, same results).  Each workload gets a bounded sample (stated),
+    repeated for about seconds / 10 per thread setting, and is reported in the
+    unit the GPU line uses for that workload.  Rates of a sample are its own
+    algorithmic bytes (or operations) over its time."""
+    import numpy as np
+    import oracle
+
+    threads = oracle.host_threads()
+    per = max(0.2, seconds / 10.0)
+    rows = []
+
+    def measure(name, unit, work, sample, fn):
+        res = {"workload": name, "unit": unit, "sample": sample}
+        for th in (1, threads):
+            with oracle.threads(th):
+                sec, reps = _time_cpu(fn, per)
+            res["single_thread" if th == 1 else "all_threads"] = round(work / sec / 1e9, 4)
+            res["ms_single" if th == 1 else "ms_all"] = round(sec * 1e3, 3)
+        res["threads"] = threads
+        rows.append(res)
+
+    # tiny: quantize both operands and multiply (the whole workload).
+    d = wl.tiny("cpu")
+    w, x = d["w"].numpy(), d["x"].numpy()
+    measure("tiny", "GB/s", 128 * row_bytes(256) + 4 * row_bytes(256) + 4 * 128 * 4,
+            "whole workload: quantize W and x, matmul 128x256 by 4 tokens",
+            lambda: oracle.matmul(oracle.quantize(w), oracle.quantize(x), 256, want_mag=False))
+    # attn_q_b: the whole decode step (quantize x + matvec 32768 x 1024).
+    d = wl.attn_q_b("cpu")
+    wq = oracle.quantize(d["w"].numpy())
+    xa = d["x"].numpy()
+    step = 32768 * row_bytes(1024) + 4 * 1024 + 4 * 32768
+    measure("attn_q_b", "GB/s", step, "whole step: quantize 1x1024, matmul 32768x1024",
+            lambda: oracle.matmul(wq, oracle.quantize(xa), 1024, want_mag=False))
+    headline = rows[-1]
+    del wq
+    # decode5: the five projections from fp32 rows.
+    ps = wl.decode5("cpu")
+    qs = [(oracle.quantize(p["w"].numpy()), p["x"].numpy(), p["in_dim"]) for p in ps]
+    step = sum(p["out_dim"] * row_bytes(p["in_dim"]) + 4 * p["in_dim"] + 4 * p["out_dim"] for p in ps)
+    measure("decode5", "GB/s", step, "whole step: five projections, each quantize + matvec",
+            lambda: [oracle.matmul(w_, oracle.quantize(x_), k_, want_mag=False) for w_, x_, k_ in qs])
+    del qs, ps
+    # moe: the gate, up and down projections of the pairs of the first 2
+    # tokens (16 of 512 pairs); bytes as for the GPU line: each touched
+    # expert matrix once, plus x_q, mid_q and the outputs.
+    cfg = wl.MOE
+    D, F, k = cfg["d_model"], cfg["d_ff"], cfg["n_used"]
+    n_t = 2
+    sel = np.ascontiguousarray(wl.moe_routing().numpy()[:n_t])
+    x, mid = wl.moe_acts("cpu")
+    experts = sorted(set(sel.reshape(-1).tolist()))
+    mats = {}
+    with oracle.threads(threads):
+        xq = oracle.quantize(x.numpy()[:n_t])
+        mq = oracle.quantize(mid.numpy()[:n_t * k])
+        for which in ("gate", "up", "down"):
+            lst = [np.zeros((1, 34), np.uint8)] * cfg["n_expert"]
+            for e in experts:
+                lst[e] = oracle.quantize(wl.moe_expert(e, which, "cpu").numpy())
+            mats[which] = lst
+    pairs = n_t * k
+    mat = F * row_bytes(D)
+    work = (3 * len(experts) * mat + n_t * row_bytes(D) + 2 * pairs * F * 4
+            + pairs * (row_bytes(F) + 4 * D))
+    measure("moe", "GB/s", work,
+            f"gate, up and down of the {pairs} (token, slot) pairs of tokens 0..{n_t - 1} "
+            f"({len(experts)} experts)",
+            lambda: [oracle.moe_grouped(mats["gate"], sel, xq, D, F, 0, want_mag=False),
+                     oracle.moe_grouped(mats["up"], sel, xq, D, F, 0, want_mag=False),
+                     oracle.moe_grouped(mats["down"], sel, mq, F, D, 1, want_mag=False)])
+    del mats
+    # prefill: 64 tokens x 256 output rows of each GEMM, whole K (TOPS).
+    for name in ("prefill_a", "prefill_b"):
+        d = wl.prefill(name, "cpu", rows=256, tokens=64)
+        kk = d["in_dim"]
+        wq = oracle.quantize(d["w"].numpy())
+        xq = oracle.quantize(d["x"].numpy())
+        measure(name, "TOPS", 2.0 * 64 * 256 * kk / 1e3,
+                f"64 tokens x 256 output rows, whole K = {kk} (operands quantized beforehand)",
+                lambda: oracle.matmul(wq, xq, kk, want_mag=False))
+        del wq, xq, d
+    return dict(value=headline["all_threads"], unit="GB/s", cores=threads, kind="oracle",
+                sample=f"attn_q_b whole step (quantize 1x1024 + matvec 32768x1024) on {threads} "
+                       f"threads: {headline['ms_all']} ms/step (single thread "
+                       f"{headline['single_thread']} GB/s, {headline['ms_single']} ms/step); "
+                       f"per_config has every workload",
+                cpu_model=_cpu_model(), nproc=os.cpu_count(), threads_used=threads,
+                per_config=rows)
 
 
 def main():

@@ -263,6 +263,8 @@ int q8_0_matmul_list(const q8_0_matmul_item *items, int32_t n_items, int64_t n_t
 /* Test hook: q8_0_matmul with a forced kernel variant and split-K count
  * (0 = automatic) that also writes every block's exact integer dot S_b into
  * blocksums (device int32 [n_tok][out_dim][in_dim/32]) when it is not NULL.
+ * The kernel that runs is the one the same call without blocksums would run
+ * (its debug instantiation), so the S_b checked are those of the timed path.
  * Errors as q8_0_matmul, plus Q8_0_EINVAL when the forced variant cannot run
  * this shape, and Q8_0_EWORKSPACE when a forced split needs more workspace. */
 int q8_0_matmul_debug(float *out, int32_t *blocksums, const void *w,

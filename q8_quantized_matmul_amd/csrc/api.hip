@@ -100,8 +100,7 @@ int run_matmul(float *out, int32_t *blocksums, const void *w, int64_t in_dim, in
     if (variant != Q8_0_KERNEL_GENERIC && !fast_align) return Q8_0_EINVAL;
     if (variant == Q8_0_KERNEL_MATVEC && !matvec_ok(in_dim)) return Q8_0_EINVAL;
     if (variant == Q8_0_KERNEL_MFMA && !q8::gemm_supported(in_dim)) return Q8_0_EINVAL;
-    if (variant == Q8_0_KERNEL_SKINNY && (!q8::skinny_supported(in_dim, n_tok) || blocksums))
-      return Q8_0_EINVAL;
+    if (variant == Q8_0_KERNEL_SKINNY && !q8::skinny_supported(in_dim, n_tok)) return Q8_0_EINVAL;
     if (variant != p.variant) p.split = 1;
     p.variant = variant;
   }
@@ -110,8 +109,6 @@ int run_matmul(float *out, int32_t *blocksums, const void *w, int64_t in_dim, in
       return Q8_0_EINVAL;
     p.split = split_k;
   }
-  // A block-sum debug call takes the GEMM where the plan chose the skinny kernel.
-  if (blocksums && p.variant == Q8_0_KERNEL_SKINNY) p.variant = Q8_0_KERNEL_MFMA;
   if (p.variant == Q8_0_KERNEL_MFMA && p.split > 1 &&
       q8::gemm_workspace_bytes(out_dim, n_tok, p.split) > workspace_bytes)
     return Q8_0_EWORKSPACE;
@@ -124,7 +121,7 @@ int run_matmul(float *out, int32_t *blocksums, const void *w, int64_t in_dim, in
       return status_of(q8::launch_gemm(out, blocksums, w, in_dim, out_dim, x_q, n_tok, p.split,
                                        static_cast<float *>(workspace), stream));
     case Q8_0_KERNEL_SKINNY:
-      return status_of(q8::launch_skinny(out, w, in_dim, out_dim, x_q, n_tok, p.split,
+      return status_of(q8::launch_skinny(out, blocksums, w, in_dim, out_dim, x_q, n_tok, p.split,
                                          static_cast<float *>(workspace), stream));
     case Q8_0_KERNEL_MATVEC:
       return status_of(q8::launch_matvec(out, blocksums, w, in_dim, out_dim, x_q, n_tok, stream));

@@ -502,8 +502,8 @@ __global__ __launch_bounds__(512, 1) void gemm_lds_kernel(const GemmArgs a) {
 //
 // The MFMA's A operand is the token tile and B the weight tile, so a lane's
 // column of the result is an output column and the stores coalesce.  Only
-// whole tiles: out_dim and n_tok multiples of 128, in_dim of 128.  It has no
-// block-sum debug output; debug calls take the direct-LDS kernel.
+// whole tiles: out_dim and n_tok multiples of 128, in_dim of 128.  Its debug
+// instantiation writes every block's S_b as well.
 namespace t4 {
 constexpr int BO = 128;                     // output rows per workgroup
 constexpr int BT = 128;                     // tokens per workgroup
@@ -516,6 +516,9 @@ constexpr int NCOPY = 64 * CH / 64;         // 9 copy instructions per wave and 
 static_assert(KB * kBlockBytes <= RB && RB % 16 == 0, "stage row pitch");
 }  // namespace t4
 
+// STORE_S (debug): also writes each block's exact S_b to a.blocksums,
+// [n_tok][out_dim][nb] int32, from the same MFMA results the outputs use.
+template <bool STORE_S>
 __global__ __launch_bounds__(256, 2) void gemm_t4_kernel(const GemmArgs a) {
   using namespace t4;
   __shared__ __attribute__((aligned(16))) uint8_t ring[2 * STAGE];
@@ -615,8 +618,12 @@ __global__ __launch_bounds__(256, 2) void gemm_t4_kernel(const GemmArgs a) {
     t4_read<0, true>(arow1, h, ra1);
     t4_read<0, true>(brow0, h, rb0);
     t4_read<0, true>(brow1, h, rb1);
+    const int64_t stage_b0 = b_begin + (int64_t)s * KB;
     [&]<int... B>(std::integer_sequence<int, B...>) {
       (([&] {
+         // This block's index, bound here in the block's own scope (a pack
+         // element used inside the nested tile lambda is not reliable).
+         const int64_t blk = stage_b0 + B;
          uint32_t sa0, sa1, sb0, sb1;
          const i32x4 A0 = t4_prep<B>(ra0, h, sa0);
          const i32x4 A1 = t4_prep<B>(ra1, h, sa1);
@@ -650,6 +657,16 @@ __global__ __launch_bounds__(256, 2) void gemm_t4_kernel(const GemmArgs a) {
               cur.C = __builtin_amdgcn_mfma_f32_32x32x8f16(SA[Q >> 1], SB[Q & 1], fzero, 0, 0, 0);
               cur.S = __builtin_amdgcn_mfma_f32_32x32x8f16(unbias_a, unbias_b,
                                                           __builtin_bit_cast(f32x16, biased), 0, 0, 0);
+              if constexpr (STORE_S) {
+                // Tile Q: tokens t_tile + 64 wt + 32 (Q >> 1) + 8 (r >> 2) + 4 h + (r & 3),
+                // output column o_tile + 64 wo + 32 (Q & 1) + lrow.
+                const int64_t o = o_tile + 64 * wo + 32 * (Q & 1) + lrow;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                  const int64_t t = t_tile + 64 * wt + 32 * (Q >> 1) + 8 * (r >> 2) + 4 * h + (r & 3);
+                  a.blocksums[(t * a.out_dim + o) * a.nb + blk] = (int32_t)cur.S[r];
+                }
+              }
               epilogue.template operator()<(Q + 3) & 3>(prev);
               // 3 MFMAs, the 16 fmas of the previous tile between them.
               __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
@@ -668,6 +685,239 @@ __global__ __launch_bounds__(256, 2) void gemm_t4_kernel(const GemmArgs a) {
 
   // acc[q]: tokens t_tile + 64 wt + 32 (q >> 1) + 8 (r >> 2) + 4 h + (r & 3),
   // output column o_tile + 64 wo + 32 (q & 1) + lrow.
+  float *dstp = a.out + (int64_t)ts * a.n_tok * a.out_dim;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int64_t o = o_tile + 64 * wo + 32 * (q & 1) + lrow;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int64_t t = t_tile + 64 * wt + 32 * (q >> 1) + 8 * (r >> 2) + 4 * h + (r & 3);
+      dstp[t * a.out_dim + o] = acc[q][r];
+    }
+  }
+}
+
+// ---- Aligned-chunk kernel: 128 x 128 workgroup tiles, 4 waves of 64 x 64.
+//
+// Same tiles, MFMA chain and epilogue as the four-tile kernel; what changes is
+// what a stage holds.  A block pair is 68 bytes = 17 dwords d0..d16:
+//   d0 = [scale_A, qA0 qA1], d1..d7 = qA2..qA29, d8 = [qA30 qA31, scale_B],
+//   d9..d16 = qB0..qB31.
+// Block B's quants are four aligned dword pairs; block A's are not: they start
+// two bytes into d0 and end two bytes into d8.  A block dot sums qw_k * qx_k
+// over k, so any permutation of k applied to both operands gives the same S_b.
+// Block A is fed in the order (qA30 qA31 qA0 qA1, qA2..qA13 | qA14..qA29):
+// the first dword is d0 with its low half (the scale) replaced by d8's low half
+// (qA30 qA31), one v_bfi per operand; everything else is whole dwords.  So
+// each row's stage slice is staged as the 16-byte chunks
+//   d0..d3, d4..d7, d9..d12, d13..d16  (pair 0), the same for pair 1,
+// nine 16-byte slots at a 144-byte pitch (the ninth repeats the eighth), plus
+// d8 of each pair in a dword plane [pair][stage row].  Every MFMA operand is
+// then one aligned 16-byte LDS read (conflict-free: consecutive rows sit 9
+// chunks apart), block A's also one dword read of the plane (consecutive rows,
+// consecutive dwords), and the block scales come out of those reads: block
+// A's is the low half of d0, block B's the high half of d8.
+namespace p4 {
+constexpr int BO = 128;
+constexpr int BT = 128;
+constexpr int KB = 4;                     // blocks per stage (two pairs)
+constexpr int RB = 144;                   // LDS pitch of a row's slots
+constexpr int CH = RB / 16;               // 9 slots
+constexpr int ROWS = BO + BT;
+constexpr int QBYTES = ROWS * RB;         // 36864
+constexpr int STAGE = QBYTES + 2 * ROWS * 4;  // + d8 plane [pair][row]: 38912
+constexpr int WAVE_BYTES = 64 * RB;
+constexpr int NCOPY = 64 * CH / 64;       // 9 chunk copies per wave and stage
+// Source byte of slot j inside the row's 136-byte stage slice.
+__host__ __device__ constexpr int slot_src(int j) {
+  return j >= 8 ? 120 : 68 * (j >> 2) + ((j & 3) == 0 ? 0 : (j & 3) == 1 ? 16 : (j & 3) == 2 ? 36 : 52);
+}
+static_assert(slot_src(7) + 16 <= KB * kBlockBytes, "slots stay inside the slice");
+}  // namespace p4
+
+__global__ __launch_bounds__(256, 2) void gemm_p4_kernel(const GemmArgs a) {
+  using namespace p4;
+  __shared__ __attribute__((aligned(16))) uint8_t ring[2 * STAGE];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  int to, tt, ts;
+  tile_of(a, to, tt, ts);
+  const int64_t o_tile = (int64_t)to * BO;
+  const int64_t t_tile = (int64_t)tt * BT;
+  const int64_t b_begin = (int64_t)ts * a.blocks_per_split;
+  const int64_t b_end = min(b_begin + a.blocks_per_split, a.nb);
+  const int nstages = (int)((b_end - b_begin) / KB);  // splits are whole stages
+
+  // Copies: waves 0, 1 move token rows t_tile + 64 w + r, waves 2, 3 weight
+  // rows o_tile + 64 (w - 2) + r, into stage rows 64 w + r.  Chunk copy k,
+  // lane l: slot (64k + l) % 9 of row (64k + l) / 9.  Plane copy pp, lane l:
+  // d8 of pair pp of row l.
+  uint32_t off[NCOPY];
+#pragma unroll
+  for (int k = 0; k < NCOPY; ++k) {
+    const int f = 64 * k + lane;
+    const int r = f / CH;
+    off[k] = (uint32_t)(r * (int)a.row_bytes + slot_src(f - r * CH));
+  }
+  const uint32_t doff = (uint32_t)(lane * (int)a.row_bytes + 32);
+  const uint8_t *copy_base = wave < 2 ? a.x_q + (t_tile + 64 * wave) * a.row_bytes
+                                      : a.w + (o_tile + 64 * (wave - 2)) * a.row_bytes;
+  const rsrc_t rsrc = make_rsrc(copy_base, (uint32_t)(64 * a.row_bytes));
+  auto issue = [&](int64_t b0, int buf) {
+    const uint32_t lds = (uint32_t)reinterpret_cast<uintptr_t>(ring + buf * STAGE + wave * WAVE_BYTES);
+    const uint32_t plane = (uint32_t)reinterpret_cast<uintptr_t>(ring + buf * STAGE + QBYTES + 256 * wave);
+    const int sb = (int)(b0 * kBlockBytes);
+#pragma unroll
+    for (int k = 0; k < NCOPY; ++k) {
+      buffer_load_lds_raw(rsrc,
+                          reinterpret_cast<__attribute__((address_space(3))) uint32_t *>(
+                              (uintptr_t)(lds + 1024 * k)),
+                          16, (int)off[k], sb, 0, 0);
+    }
+    buffer_load_lds_raw(rsrc,
+                        reinterpret_cast<__attribute__((address_space(3))) uint32_t *>((uintptr_t)plane),
+                        4, (int)doff, sb, 0, 0);
+    // (An LDS-DMA load adds its instruction offset to the LDS address as
+    // well, so the pair offset goes in the scalar offset.)
+    buffer_load_lds_raw(rsrc,
+                        reinterpret_cast<__attribute__((address_space(3))) uint32_t *>(
+                            (uintptr_t)(plane + 4 * ROWS)),
+                        4, (int)doff, sb + 68, 0, 0);
+  };
+
+  const int wt = wave & 1;   // tokens [64 wt, 64 wt + 64) of the tile
+  const int wo = wave >> 1;  // outputs [64 wo, 64 wo + 64)
+  const int lrow = lane & 31;
+  const int h = lane >> 5;
+  const f32x16 fzero = {};
+  f32x16 acc[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[q][r] = 0.0f;
+
+  typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+  const i32x16 ibias = {0x4B400000, 0x4B400000, 0x4B400000, 0x4B400000, 0x4B400000, 0x4B400000,
+                        0x4B400000, 0x4B400000, 0x4B400000, 0x4B400000, 0x4B400000, 0x4B400000,
+                        0x4B400000, 0x4B400000, 0x4B400000, 0x4B400000};
+  const f16x4 unbias_a = h ? f16x4{0, 0, 0, 0} : f16x4{(_Float16)-3072.0f, 0, 0, 0};
+  const f16x4 unbias_b = h ? f16x4{0, 0, 0, 0} : f16x4{(_Float16)4096.0f, 0, 0, 0};
+  // Lane constants: the first dword of block A's operand keeps d0's high half
+  // and takes d8's low half (half 0; half 1 keeps its own dword), and the
+  // scale selectors leave the scale's two bytes in the low half (half 0) or
+  // zero (half 1: its K slots of the scale MFMA are zero).
+  const uint32_t keep_hi = h ? 0xFFFFFFFFu : 0xFFFF0000u;
+  const uint32_t sel_a = h ? 0x0C0C0C0Cu : 0x0C0C0100u;  // bytes 0, 1 of d0
+  const uint32_t sel_b = h ? 0x0C0C0C0Cu : 0x0C0C0302u;  // bytes 2, 3 of d8
+
+  struct TileOut {
+    f32x16 S;
+    f32x16 C;
+  };
+  TileOut slot[2];
+  slot[1].S = fzero;
+  slot[1].C = fzero;
+  auto epilogue = [&]<int Q>(const TileOut &o) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[Q][r] = fmaf(o.S[r], o.C[r], acc[Q][r]);
+  };
+
+  // Raw LDS data of one operand of block B of the stage: the 16-byte slot,
+  // and for block A of a pair (even B) the pair's d8.
+  struct Raw {
+    i32x4 v;
+    uint32_t d8;
+  };
+  auto read_raw = [&]<int B>(const uint8_t *st, int row, Raw &r) {
+    constexpr int pp = B >> 1;
+    r.v = *reinterpret_cast<const i32x4 *>(st + row * RB + 16 * (4 * pp + 2 * (B & 1)) + 16 * h);
+    if constexpr ((B & 1) == 0)
+      r.d8 = *reinterpret_cast<const uint32_t *>(st + QBYTES + 4 * (ROWS * pp + row));
+  };
+  // The operand and its scale bits (low half; zero on half 1).
+  auto prep = [&]<int B>(const Raw &r, uint32_t d8, uint32_t &scale) -> i32x4 {
+    if constexpr ((B & 1) == 0) {
+      scale = __builtin_amdgcn_perm(0u, (uint32_t)r.v.x, sel_a);
+      const uint32_t first = ((uint32_t)r.v.x & keep_hi) | (d8 & ~keep_hi);
+      return i32x4{(int)first, r.v.y, r.v.z, r.v.w};
+    } else {
+      scale = __builtin_amdgcn_perm(0u, d8, sel_b);
+      return r.v;
+    }
+  };
+
+  issue(b_begin, 0);
+  for (int s = 0; s < nstages; ++s) {
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's copies of stage s have landed
+    __syncthreads();                // ... and every wave's; buffer (s+1)&1 is free
+    if (s + 1 < nstages) issue(b_begin + (int64_t)(s + 1) * KB, (s + 1) & 1);
+    const uint8_t *st = ring + (s & 1) * STAGE;
+    const int ra0 = 64 * wt + lrow, ra1 = ra0 + 32;            // token rows
+    const int rb0 = BT + 64 * wo + lrow, rb1 = rb0 + 32;       // weight rows
+
+    Raw xa0, xa1, xb0, xb1;
+    uint32_t d8a0 = 0, d8a1 = 0, d8b0 = 0, d8b1 = 0;  // the current pair's d8
+    read_raw.template operator()<0>(st, ra0, xa0);
+    read_raw.template operator()<0>(st, ra1, xa1);
+    read_raw.template operator()<0>(st, rb0, xb0);
+    read_raw.template operator()<0>(st, rb1, xb1);
+    [&]<int... B>(std::integer_sequence<int, B...>) {
+      (([&] {
+         if constexpr ((B & 1) == 0) {
+           d8a0 = xa0.d8;
+           d8a1 = xa1.d8;
+           d8b0 = xb0.d8;
+           d8b1 = xb1.d8;
+         }
+         uint32_t sa0, sa1, sb0, sb1;
+         const i32x4 A0 = prep.template operator()<B>(xa0, d8a0, sa0);
+         const i32x4 A1 = prep.template operator()<B>(xa1, d8a1, sa1);
+         const i32x4 B0 = prep.template operator()<B>(xb0, d8b0, sb0);
+         const i32x4 B1 = prep.template operator()<B>(xb1, d8b1, sb1);
+         __builtin_amdgcn_sched_barrier(0);
+         if constexpr (B + 1 < KB) {
+           read_raw.template operator()<B + 1>(st, ra0, xa0);
+           read_raw.template operator()<B + 1>(st, ra1, xa1);
+           read_raw.template operator()<B + 1>(st, rb0, xb0);
+           read_raw.template operator()<B + 1>(st, rb1, xb1);
+         }
+         __builtin_amdgcn_sched_barrier(0);
+         const f16x4 SA[2] = {__builtin_bit_cast(f16x4, u32x2{sa0, 0u}),
+                              __builtin_bit_cast(f16x4, u32x2{sa1, 0u})};
+         const f16x4 SB[2] = {__builtin_bit_cast(f16x4, u32x2{sb0, 0u}),
+                              __builtin_bit_cast(f16x4, u32x2{sb1, 0u})};
+         const i32x4 AA[2] = {A0, A1};
+         const i32x4 BB[2] = {B0, B1};
+         [&]<int... Q>(std::integer_sequence<int, Q...>) {
+           (([&] {
+              TileOut &cur = slot[Q & 1];
+              const TileOut &prev = slot[(Q + 1) & 1];
+              __builtin_amdgcn_s_setprio(1);
+              const i32x16 biased =
+                  __builtin_amdgcn_mfma_i32_32x32x32_i8(AA[Q >> 1], BB[Q & 1], ibias, 0, 0, 0);
+              cur.C = __builtin_amdgcn_mfma_f32_32x32x8f16(SA[Q >> 1], SB[Q & 1], fzero, 0, 0, 0);
+              cur.S = __builtin_amdgcn_mfma_f32_32x32x8f16(unbias_a, unbias_b,
+                                                          __builtin_bit_cast(f32x16, biased), 0, 0, 0);
+              epilogue.template operator()<(Q + 3) & 3>(prev);
+              // Block sums and scales of this tile, 8 fmas of the previous
+              // tile, the unbias of this tile, its other 8 fmas: the unbias
+              // waits on the int8 MFMA across a group, and the next step's
+              // fmas wait on this unbias across two MFMAs.
+              __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+              __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+              __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+              __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+              __builtin_amdgcn_s_setprio(0);
+              __builtin_amdgcn_sched_barrier(0);
+            }()), ...);
+         }(std::make_integer_sequence<int, 4>{});
+       }()), ...);
+    }(std::make_integer_sequence<int, KB>{});
+  }
+  epilogue.template operator()<3>(slot[1]);
+
   float *dstp = a.out + (int64_t)ts * a.n_tok * a.out_dim;
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
@@ -741,7 +991,7 @@ hipError_t launch_gemm(float *out, int32_t *blocksums, const void *w, int64_t in
   // bases are 16-byte aligned (torch allocations are), the register-staged
   // kernel the rest (it needs 4 bytes).
   const bool a16 = ((reinterpret_cast<uintptr_t>(w) | reinterpret_cast<uintptr_t>(x_q)) & 15) == 0;
-  const bool four = a16 && !blocksums && use_t4_kernel(nb, out_dim, n_tok);
+  const bool four = a16 && use_t4_kernel(nb, out_dim, n_tok);
   const bool direct = a16 && !four && use_lds_kernel(nb, n_tok);
   const int stage = four ? t4::KB : (direct ? lds::KB : kStageBlocks);
   int64_t bps = (nb + split - 1) / split;
@@ -762,7 +1012,8 @@ hipError_t launch_gemm(float *out, int32_t *blocksums, const void *w, int64_t in
     a.tiles_o = (int32_t)(out_dim / t4::BO);
     a.tiles_t = (int32_t)(n_tok / t4::BT);
     const dim3 grid((uint32_t)a.tiles_o * (uint32_t)a.tiles_t * (uint32_t)n_split);
-    hipLaunchKernelGGL(gemm_t4_kernel, grid, dim3(256), 0, s, a);
+    if (blocksums) hipLaunchKernelGGL(gemm_t4_kernel<true>, grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL(gemm_t4_kernel<false>, grid, dim3(256), 0, s, a);
   } else if (direct) {
     a.tiles_o = (int32_t)((out_dim + lds::BO - 1) / lds::BO);
     a.tiles_t = (int32_t)((n_tok + lds::BT - 1) / lds::BT);

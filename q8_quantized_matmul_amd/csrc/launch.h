@@ -94,9 +94,9 @@ constexpr int64_t kSkinnyMaxTokens = 64;
 bool skinny_supported(int64_t in_dim, int64_t n_tok);
 int skinny_auto_split(int64_t in_dim, int64_t out_dim);
 size_t skinny_workspace_bytes(int64_t out_dim, int64_t n_tok, int split);
-hipError_t launch_skinny(float *out, const void *w, int64_t in_dim, int64_t out_dim,
-                         const void *x_q, int64_t n_tok, int split, float *partials,
-                         hipStream_t s);
+hipError_t launch_skinny(float *out, int32_t *blocksums, const void *w, int64_t in_dim,
+                         int64_t out_dim, const void *x_q, int64_t n_tok, int split,
+                         float *partials, hipStream_t s);
 
 // gemm.hip: int8 MFMA GEMM with per-block scales.
 bool gemm_supported(int64_t in_dim);

@@ -32,6 +32,7 @@ namespace {
 
 struct SkinnyArgs {
   float *out;            // [n_tok][out_dim], or partials [n_split][n_tok][out_dim]
+  int32_t *blocksums;    // debug: S_b [n_tok][out_dim][2 * n_pairs], or null
   const uint8_t *w;      // [out_dim][row_bytes]
   const uint8_t *x_q;    // [n_tok][row_bytes]
   int64_t out_dim;
@@ -58,10 +59,12 @@ struct SkinnyStage {
 
 // One block of the wave's pair: operands from the staged rows, then per
 // token tile one int8 MFMA (S_b) and one scale MFMA (d_x * d_w), added as
-// acc += float(S_b) * scale.
-template <int B, int MT>
+// acc += float(S_b) * scale.  STORE_S (debug) also writes S_b of block `blk`
+// for output column `o`.
+template <int B, int MT, bool STORE_S>
 __device__ __forceinline__ void skinny_block(const uint8_t *const (&xrow)[MT], const uint8_t *wrow,
-                                             int h, float (&acc)[MT][16]) {
+                                             int h, float (&acc)[MT][16], const SkinnyArgs &a,
+                                             int64_t blk, int64_t o) {
   typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
   const i32x16 izero = {};
   const f32x16 fzero = {};
@@ -81,6 +84,14 @@ __device__ __forceinline__ void skinny_block(const uint8_t *const (&xrow)[MT], c
     const f32x16 C = __builtin_amdgcn_mfma_f32_32x32x8f16(SA, SB, fzero, 0, 0, 0);
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[m][r] = fmaf((float)S[r], C[r], acc[m][r]);
+    if constexpr (STORE_S) {
+      // Element r: token 32 m + 8 (r / 4) + 4 h + r % 4.
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int64_t t = 32 * m + 8 * (r >> 2) + 4 * h + (r & 3);
+        if (t < a.n_tok && o < a.out_dim) a.blocksums[(t * a.out_dim + o) * 2 * a.n_pairs + blk] = S[r];
+      }
+    }
   }
 }
 
@@ -193,7 +204,7 @@ struct ChunkCopies {
 };
 
 // MT token tiles of 32.  Grid: x = 32-row output tiles, y = K splits.
-template <int MT, class COPY>
+template <int MT, class COPY, bool STORE_S>
 __global__ __launch_bounds__(256) void skinny_kernel(const SkinnyArgs a) {
   using St = SkinnyStage<MT>;
   __shared__ __attribute__((aligned(16))) uint8_t ring[2 * St::BYTES];
@@ -224,18 +235,21 @@ __global__ __launch_bounds__(256) void skinny_kernel(const SkinnyArgs a) {
     if (s + 1 < nstages) issue(s + 1, (s + 1) & 1);
     // Wave w takes pair w of the stage (blocks 2w, 2w+1), which starts 68 w
     // bytes into each staged row: in the 136-byte slice w / 2, at block 0 or 2.
-    if (p_begin + s * kStagePairs + wave < p_end) {
+    const int pair = p_begin + s * kStagePairs + wave;
+    if (pair < p_end) {
       const uint8_t *st = ring + (s & 1) * St::BYTES + 136 * (wave >> 1);
       const uint8_t *xrow[MT];
 #pragma unroll
       for (int m = 0; m < MT; ++m) xrow[m] = st + (32 * m + lrow) * kStageRowBytes;
       const uint8_t *wrow = st + (St::XROWS + lrow) * kStageRowBytes;
+      const int64_t blk = 2 * (int64_t)pair;  // the pair's first block
+      const int64_t o = o_tile + lrow;
       if (wave & 1) {
-        skinny_block<2, MT>(xrow, wrow, h, acc);
-        skinny_block<3, MT>(xrow, wrow, h, acc);
+        skinny_block<2, MT, STORE_S>(xrow, wrow, h, acc, a, blk, o);
+        skinny_block<3, MT, STORE_S>(xrow, wrow, h, acc, a, blk + 1, o);
       } else {
-        skinny_block<0, MT>(xrow, wrow, h, acc);
-        skinny_block<1, MT>(xrow, wrow, h, acc);
+        skinny_block<0, MT, STORE_S>(xrow, wrow, h, acc, a, blk, o);
+        skinny_block<1, MT, STORE_S>(xrow, wrow, h, acc, a, blk + 1, o);
       }
     }
   }
@@ -264,6 +278,29 @@ __global__ __launch_bounds__(256) void skinny_kernel(const SkinnyArgs a) {
   }
 }
 
+// Every variant explicitly instantiated: without this the host side of the
+// front end dropped two of them (the host stubs were referenced but never
+// emitted).
+template __global__ void skinny_kernel<1, ChunkCopies<1>, false>(const SkinnyArgs);
+template __global__ void skinny_kernel<2, ChunkCopies<2>, false>(const SkinnyArgs);
+template __global__ void skinny_kernel<1, ChunkCopies<1>, true>(const SkinnyArgs);
+template __global__ void skinny_kernel<2, ChunkCopies<2>, true>(const SkinnyArgs);
+template __global__ void skinny_kernel<1, DwordCopies<1>, false>(const SkinnyArgs);
+template __global__ void skinny_kernel<2, DwordCopies<2>, false>(const SkinnyArgs);
+template __global__ void skinny_kernel<1, DwordCopies<1>, true>(const SkinnyArgs);
+template __global__ void skinny_kernel<2, DwordCopies<2>, true>(const SkinnyArgs);
+
+template <int MT, bool STORE_S>
+void launch_skinny_variant(bool wide, dim3 grid, const SkinnyArgs &a, hipStream_t s) {
+  if (wide) {
+    auto k = skinny_kernel<MT, ChunkCopies<MT>, STORE_S>;
+    hipLaunchKernelGGL(k, grid, dim3(256), 0, s, a);
+  } else {
+    auto k = skinny_kernel<MT, DwordCopies<MT>, STORE_S>;
+    hipLaunchKernelGGL(k, grid, dim3(256), 0, s, a);
+  }
+}
+
 }  // namespace
 
 bool skinny_supported(int64_t in_dim, int64_t n_tok) {
@@ -286,10 +323,11 @@ size_t skinny_workspace_bytes(int64_t out_dim, int64_t n_tok, int split) {
   return split > 1 ? (size_t)split * (size_t)out_dim * (size_t)n_tok * sizeof(float) : 0;
 }
 
-hipError_t launch_skinny(float *out, const void *w, int64_t in_dim, int64_t out_dim,
-                         const void *x_q, int64_t n_tok, int split, float *partials,
-                         hipStream_t s) {
+hipError_t launch_skinny(float *out, int32_t *blocksums, const void *w, int64_t in_dim,
+                         int64_t out_dim, const void *x_q, int64_t n_tok, int split,
+                         float *partials, hipStream_t s) {
   SkinnyArgs a{};
+  a.blocksums = blocksums;
   a.n_pairs = (int32_t)(in_dim / 64);
   // Splits are whole stages (the last one may be short).
   const int pps = (((a.n_pairs + split - 1) / split + kStagePairs - 1) / kStagePairs) * kStagePairs;
@@ -305,12 +343,13 @@ hipError_t launch_skinny(float *out, const void *w, int64_t in_dim, int64_t out_
   // 16-byte copies need whole 16-byte chunks: rows of 8k blocks, 16-aligned bases.
   const bool wide = in_dim % 256 == 0 && (reinterpret_cast<uintptr_t>(w) & 15) == 0 &&
                     (reinterpret_cast<uintptr_t>(x_q) & 15) == 0;
-  if (n_tok > 32) {
-    if (wide) hipLaunchKernelGGL((skinny_kernel<2, ChunkCopies<2>>), grid, dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((skinny_kernel<2, DwordCopies<2>>), grid, dim3(256), 0, s, a);
+  const bool two = n_tok > 32;
+  if (blocksums) {
+    if (two) launch_skinny_variant<2, true>(wide, grid, a, s);
+    else launch_skinny_variant<1, true>(wide, grid, a, s);
   } else {
-    if (wide) hipLaunchKernelGGL((skinny_kernel<1, ChunkCopies<1>>), grid, dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((skinny_kernel<1, DwordCopies<1>>), grid, dim3(256), 0, s, a);
+    if (two) launch_skinny_variant<2, false>(wide, grid, a, s);
+    else launch_skinny_variant<1, false>(wide, grid, a, s);
   }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || n_split == 1) return err;

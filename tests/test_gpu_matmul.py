@@ -109,14 +109,21 @@ def test_matvec_token_counts(in_dim, n_tok):
 
 
 def _run_skinny(wq, xq, wq_o, xq_o, in_dim, out_dim, n_tok, split, where):
+    # The skinny kernel's debug instantiation: outputs to tolerance and every
+    # block's S_b bit-exactly; then the same call without block sums (the
+    # product instantiation) must give the same outputs bit for bit.
     q8 = _q8()
     say(f"[matmul] {where} in={in_dim} out={out_dim} n_tok={n_tok} skinny split={split}")
     out = torch.full((n_tok, out_dim), float("nan"), device="cuda")
     ws = torch.empty(max(4 * split * out_dim * n_tok, 1), dtype=torch.uint8, device="cuda")
-    got, _ = q8.q8_0_matmul_debug(wq, xq, in_dim, out_dim, n_tok, variant=q8.KERNEL_SKINNY,
-                                  split_k=split, blocksums=False, out=out, workspace=ws)
+    got, bs = q8.q8_0_matmul_debug(wq, xq, in_dim, out_dim, n_tok, variant=q8.KERNEL_SKINNY,
+                                   split_k=split, blocksums=True, out=out, workspace=ws)
+    plain, _ = q8.q8_0_matmul_debug(wq, xq, in_dim, out_dim, n_tok, variant=q8.KERNEL_SKINNY,
+                                    split_k=split, blocksums=False, workspace=ws)
     torch.cuda.synchronize()
-    ref, mag, _ = oracle.matmul(wq_o, xq_o, in_dim)
+    ref, mag, rbs = oracle.matmul(wq_o, xq_o, in_dim, want_blocksums=True)
+    assert np.array_equal(bs.cpu().numpy(), rbs), f"{where}: block sums differ"
+    assert torch.equal(plain.view(torch.int32), got.view(torch.int32)), f"{where}: debug build differs"
     got = got.cpu().numpy()
     assert_close(got, ref, mag, where)
     return got, ref
@@ -125,7 +132,7 @@ def _run_skinny(wq, xq, wq_o, xq_o, in_dim, out_dim, n_tok, split, where):
 @pytest.mark.parametrize("in_dim,out_dim,n_tok,split", [
     (4096, 2048, 64, 4), (4096, 2048, 32, 4), (2048, 4096, 33, 2), (4096, 1000, 40, 1),
     (1024, 300, 17, 2), (64, 50, 64, 1), (192, 65, 31, 1), (128, 33, 5, 1), (4096, 64, 48, 16),
-    (1024, 32768, 64, 1), (8192, 96, 1, 3), (2048, 4096, 64, 2)])
+    (1024, 32768, 64, 1), (8192, 96, 1, 3), (2048, 4096, 64, 2), (4096, 2048, 64, 0)])
 def test_skinny_shapes(in_dim, out_dim, n_tok, split):
     # Ragged rows and token counts, one or two token tiles, waves with no
     # block pair (192 values = 3 pairs), and split-K with uneven splits.
@@ -339,27 +346,50 @@ def test_decode5_full():
 
 
 @pytest.mark.parametrize("name", ["prefill_a", "prefill_b"])
-def test_prefill_full_sampled(name):
-    """Full-size launch as timed by the benchmark; the oracle checks a sample of
-    64 tokens x 96 output rows, plus every quantized activation byte."""
+def test_prefill_full(name):
+    """Full-size launch as timed by the benchmark (the automatic plan, its
+    split-K workspace): every quantized weight and activation byte and every
+    output element against the oracle (on the host's cores)."""
     q8 = _q8()
     d = workloads.prefill(name, "cuda")
     k, n, t = d["in_dim"], d["out_dim"], d["n_tok"]
     wq = q8.q8_0_quantize_act(d["w"])
     xq = q8.q8_0_quantize_act(d["x"])
-    say(f"[matmul] {name} full plan={q8.q8_0_matmul_plan(k, n, t, 1 << 40)}")
-    got = q8.q8_0_matmul(wq, xq, k, n, t)
+    ws = q8.matmul_workspace(k, n, t)
+    plan = q8.q8_0_matmul_plan(k, n, t, ws.numel())
+    say(f"[matmul] {name} full plan={plan}")
+    assert plan[0] == q8.KERNEL_MFMA
+    out = torch.full((t, n), float("nan"), device="cuda")
+    got = q8.q8_0_matmul(wq, xq, k, n, t, out=out, workspace=ws)
     torch.cuda.synchronize()
-    assert q8.q8_0_matmul_plan(k, n, t, 1 << 40)[0] == 3
-    rng = np.random.default_rng(5)
-    toks = np.sort(rng.choice(t, 64, replace=False))
-    rows = np.sort(rng.choice(n, 96, replace=False))
-    xq_o = oracle_quantize(d["x"][torch.as_tensor(toks, device="cuda")])
-    wq_o = oracle_quantize(d["w"][torch.as_tensor(rows, device="cuda")])
-    assert np.array_equal(cpu_u8(xq)[toks], xq_o)
-    assert np.array_equal(cpu_u8(wq)[rows], wq_o)
-    ref, mag, _ = oracle.matmul(wq_o, xq_o, k)
-    assert_close(got.cpu().numpy()[np.ix_(toks, rows)], ref, mag, name)
+    with oracle.threads():
+        xq_o = oracle_quantize(d["x"])
+        wq_o = oracle_quantize(d["w"])
+        assert np.array_equal(cpu_u8(xq), xq_o)
+        assert np.array_equal(cpu_u8(wq), wq_o)
+        say(f"[matmul] {name} oracle on {oracle.get_threads()} threads")
+        ref, mag, _ = oracle.matmul(wq_o, xq_o, k)
+    assert_close(got.cpu().numpy(), ref, mag, name)
+
+
+@pytest.mark.parametrize("name,rows,tokens,split", [
+    ("prefill_a", 256, 256, 1), ("prefill_a", 128, 384, 2), ("prefill_b", 128, 256, 0)])
+def test_prefill_whole_tile_blocksums(name, rows, tokens, split):
+    # Whole 128 x 128 tiles of each prefill workload (whole K), so the call
+    # runs the four-tile kernel the benchmark times, in its debug
+    # instantiation: every block's S_b bit-exactly and the outputs, which must
+    # equal the product instantiation's bit for bit.
+    q8 = _q8()
+    d = workloads.prefill(name, "cuda", rows=rows, tokens=tokens)
+    wq, xq, wq_o, xq_o = _prep(d["w"], d["x"])
+    k = d["in_dim"]
+    got = _run_and_check(wq, xq, wq_o, xq_o, k, rows, tokens, q8.KERNEL_MFMA, split,
+                         where=f"{name} whole tiles")
+    ws = torch.empty(max(16 * rows * tokens * 4, 1), dtype=torch.uint8, device="cuda")
+    plain, _ = q8.q8_0_matmul_debug(wq, xq, k, rows, tokens, variant=q8.KERNEL_MFMA, split_k=split,
+                                    blocksums=False, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(plain.view(torch.int32), got.view(torch.int32))
 
 
 def test_prefill_slices_blocksums():

@@ -82,54 +82,74 @@ def test_moe_invalid_ids_and_duplicates():
     assert_close(got.cpu().numpy(), ref, mag, "moe invalid")
 
 
-def test_moe_workload_full_sampled():
-    """The benchmark's MoE workload at full size (256 experts x 3 matrices +
-    shared expert); the oracle checks 12 sampled (token, slot) pairs of every
-    projection in full, plus the shared expert on 8 tokens."""
+def _moe_stack(q8, which, E, rows, cols):
+    st = torch.empty((E, rows, q8.row_bytes(cols)), dtype=torch.uint8, device="cuda")
+    for e in range(E):
+        q8.q8_0_quantize_act(workloads.moe_expert(e, which, "cuda"), out=st[e])
+    return st
+
+
+@pytest.mark.parametrize("which", ["gate", "up", "down"])
+def test_moe_workload_full(which):
+    """The benchmark's MoE workload at full size (256 experts, 64 tokens x 8
+    slots), one projection per test: every (token, slot) pair's whole output
+    row against the oracle, and every touched expert's quantized bytes."""
     q8 = _q8()
     cfg = workloads.MOE
     E, k, T, D, F = cfg["n_expert"], cfg["n_used"], cfg["n_tok"], cfg["d_model"], cfg["d_ff"]
+    in_dim, out_dim = (D, F) if which != "down" else (F, D)
+    x_rows = 1 if which == "down" else 0
     sel = workloads.moe_routing()
     x, mid = workloads.moe_acts("cuda")
-    xq = q8.q8_0_quantize_act(x)
-    midq = q8.q8_0_quantize_act(mid)
-    say("[moe] quantizing 256 experts x 3")
-    stacks = {}
-    for which, (rows, cols) in (("gate", (F, D)), ("up", (F, D)), ("down", (D, F))):
-        st = torch.empty((E, rows, q8.row_bytes(cols)), dtype=torch.uint8, device="cuda")
-        for e in range(E):
-            q8.q8_0_quantize_act(workloads.moe_expert(e, which, "cuda"), out=st[e])
-        stacks[which] = st
+    src_f = mid[: T * k] if x_rows else x
+    src = q8.q8_0_quantize_act(src_f)
+    say(f"[moe] full {which}: quantizing 256 experts")
+    st = _moe_stack(q8, which, E, out_dim, in_dim)
+    got, ws = q8.q8_0_moe_grouped(q8.expert_table(st), E, sel.cuda(), src, in_dim, out_dim, x_rows)
     torch.cuda.synchronize()
-    rng = np.random.default_rng(17)
-    pairs = sorted(rng.choice(T * k, 12, replace=False).tolist())
-    for which in ("gate", "up", "down"):
-        in_dim, out_dim = (D, F) if which != "down" else (F, D)
-        x_rows = 1 if which == "down" else 0
-        src = midq[: T * k] if x_rows else xq
-        say(f"[moe] full {which}")
-        got, ws = q8.q8_0_moe_grouped(q8.expert_table(stacks[which]), E, sel.cuda(), src, in_dim,
-                                      out_dim, x_rows)
-        torch.cuda.synchronize()
-        assert q8.moe_invalid_count(ws) == 0
-        g = got.cpu().numpy().reshape(T * k, out_dim)
-        src_f = mid[: T * k] if x_rows else x
-        for p in pairs:
-            t, j = divmod(p, k)
-            e = int(sel[t, j])
+    assert q8.moe_invalid_count(ws) == 0
+    touched = sorted(set(sel.reshape(-1).tolist()))
+    dummy = np.zeros((1, q8.row_bytes(in_dim)), dtype=np.uint8)
+    mats = [dummy] * E
+    with oracle.threads():
+        src_o = oracle_quantize(src_f)
+        assert np.array_equal(cpu_u8(src), src_o)
+        for e in touched:
             w_o = oracle_quantize(workloads.moe_expert(e, which, "cuda"))
-            assert np.array_equal(cpu_u8(stacks[which][e]), w_o)
-            xr = oracle_quantize(src_f[p if x_rows else t][None, :])
-            ref, mag, _ = oracle.matmul(w_o, xr, in_dim)
-            assert_close(g[p][None, :], ref, mag, f"moe {which} pair {p}")
-    # Shared expert: dense q8_0_matmul at n_tok = 64 (matrix-core path).
-    w_sh = workloads.moe_expert(-1, "gate", "cuda")
-    wq_sh = q8.q8_0_quantize_act(w_sh)
-    got = q8.q8_0_matmul(wq_sh, xq, D, F, T)
+            assert np.array_equal(cpu_u8(st[e]), w_o), f"expert {e} bytes"
+            mats[e] = w_o
+        say(f"[moe] full {which}: oracle over {T * k} pairs, {len(touched)} experts")
+        ref, mag, bad = oracle.moe_grouped(mats, sel.numpy(), src_o, in_dim, out_dim, x_rows)
+    assert bad == 0
+    assert_close(got.cpu().numpy(), ref, mag, f"moe {which} full")
+
+
+@pytest.mark.parametrize("which", ["gate", "up", "down"])
+def test_moe_shared_expert_full(which):
+    """The shared expert of the MoE workload: a dense q8_0_matmul at 64 tokens
+    (the skinny matrix-core kernel, split-K through its workspace), every
+    output against the oracle."""
+    q8 = _q8()
+    cfg = workloads.MOE
+    k, T, D, F = cfg["n_used"], cfg["n_tok"], cfg["d_model"], cfg["d_ff"]
+    in_dim, out_dim = (D, F) if which != "down" else (F, D)
+    x, mid = workloads.moe_acts("cuda")
+    src_f = mid[T * k:] if which == "down" else x
+    w = workloads.moe_expert(-1, which, "cuda")
+    wq = q8.q8_0_quantize_act(w)
+    xq = q8.q8_0_quantize_act(src_f)
+    ws = q8.matmul_workspace(in_dim, out_dim, T)
+    plan = q8.q8_0_matmul_plan(in_dim, out_dim, T, ws.numel())
+    say(f"[moe] shared {which} plan={plan}")
+    out = torch.full((T, out_dim), float("nan"), device="cuda")
+    got = q8.q8_0_matmul(wq, xq, in_dim, out_dim, T, out=out, workspace=ws)
     torch.cuda.synchronize()
-    toks = np.arange(0, T, 8)
-    ref, mag, _ = oracle.matmul(oracle_quantize(w_sh), oracle_quantize(x[torch.as_tensor(toks, device="cuda")]), D)
-    assert_close(got.cpu().numpy()[toks], ref, mag, "shared gate")
+    with oracle.threads():
+        wq_o = oracle_quantize(w)
+        xq_o = oracle_quantize(src_f)
+        assert np.array_equal(cpu_u8(wq), wq_o) and np.array_equal(cpu_u8(xq), xq_o)
+        ref, mag, _ = oracle.matmul(wq_o, xq_o, in_dim)
+    assert_close(got.cpu().numpy(), ref, mag, f"shared {which}")
 
 
 @pytest.mark.parametrize("n_expert,n_tok,n_used,n_bad", [
