@@ -299,12 +299,20 @@ def bench_moe(torch, q8, wl, steps, warmup):
                 shared_bytes=mat + T * F * 4 + T * row_bytes(D), touched_experts=touched, ops=ops)
 
 
-def probe_mfma_tops(torch, q8):
-    """Measured matrix-core ceiling: independent int8 MFMA chains, no memory
-    traffic (q8_0_probe_mfma_i8), in TOPS."""
+def probe_mfma_tops(torch, q8, mix=None):
+    """Measured matrix-core ceilings, no memory traffic, in TOPS of int8 work:
+    independent int8 MFMA chains (q8_0_probe_mfma_i8), or with `mix` the
+    GEMM's whole per-tile-block instruction mix (q8_0_probe_mfma_mix: 1 =
+    int8 + scale + unbias MFMAs and 16 fmas, the ceiling of the exact
+    formulation as the kernel issues it; 2 = the int->float conversion on the
+    VALU instead)."""
     sink = torch.zeros(1, dtype=torch.int32, device="cuda")
     iters = 2000
-    us = time_kernel(torch, lambda i: q8.q8_0_probe_mfma_i8(iters, sink), 1, reps=5)
+    if mix is None:
+        fn = lambda i: q8.q8_0_probe_mfma_i8(iters, sink)
+    else:
+        fn = lambda i: q8.q8_0_probe_mfma_mix(iters, mix, sink)
+    us = time_kernel(torch, fn, 1, reps=5)
     return q8.PROBE_MFMA_OPS_PER_ITER * iters / (us * 1e-6) / 1e12
 
 
@@ -545,8 +553,10 @@ def main():
             "routed_ffn_GBs": round(mo["ffn_bytes"] / (mo["ffn_us"] * 1e-6) / 1e9, 1),
             "frac_hbm_routed_ffn": round(mo["ffn_bytes"] / (mo["ffn_us"] * 1e-6) / 1e9
                                          / HBM_PEAK_GBS, 4)})
-        log("[bench] int8 MFMA probe")
+        log("[bench] int8 MFMA probes")
         mfma_tops = probe_mfma_tops(torch, q8)
+        mix_tops = probe_mfma_tops(torch, q8, mix=1)
+        mix_valu_tops = probe_mfma_tops(torch, q8, mix=2)
         for name in ("prefill_a", "prefill_b"):
             log(f"[bench] {name}")
             pf = bench_prefill(torch, q8, wl, name, max(args.steps // 40, 10), 3)
@@ -557,6 +567,9 @@ def main():
                 "gemm_TOPS": round(tops, 1), "frac_int8_mfma": round(tops / INT8_MFMA_PEAK_TOPS, 4),
                 "measured_mfma_TOPS": round(mfma_tops, 1),
                 "frac_of_measured_mfma": round(tops / mfma_tops, 4),
+                "formulation_ceiling_TOPS": round(mix_tops, 1),
+                "frac_of_formulation_ceiling": round(tops / mix_tops, 4),
+                "formulation_ceiling_valu_convert_TOPS": round(mix_valu_tops, 1),
                 "quantize_us": round(pf["quant_us"], 2),
                 "quantize_GBs": round(pf["quant_bytes"] / (pf["quant_us"] * 1e-6) / 1e9, 1),
                 "plan": list(pf["plan"])})

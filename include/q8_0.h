@@ -306,6 +306,20 @@ int q8_0_probe_read(const void *buf, size_t bytes, uint32_t *sink, hipStream_t s
  * Errors: iters < 1, null sink -> Q8_0_EINVAL. */
 int q8_0_probe_mfma_i8(int32_t iters, uint32_t *sink, hipStream_t stream);
 
+/* Measurement probe (the ceiling of the prefill GEMM's own formulation):
+ * the GEMM's per-tile-block instruction mix on registers only, no memory
+ * traffic, in the same grid and with the same int8 work per round as
+ * q8_0_probe_mfma_i8 (so the rates compare directly):
+ *   mix 0: the int8 MFMA alone;
+ *   mix 1: per 32x32 tile and block, the biased int8 MFMA, the f16 MFMA of
+ *          the scale outer product, the f16 MFMA that removes the bias, and
+ *          16 fp32 fmas (the four-tile kernel's tile step);
+ *   mix 2: the int8 MFMA and the scale MFMA, with the int->float
+ *          conversion as 16 VALU converts before the 16 fmas.
+ * sink as above.  Errors: iters < 1, mix outside 0..2, null sink ->
+ * Q8_0_EINVAL. */
+int q8_0_probe_mfma_mix(int32_t iters, int32_t mix, uint32_t *sink, hipStream_t stream);
+
 /* Static description of a status code. */
 const char *q8_0_strerror(int status);
 

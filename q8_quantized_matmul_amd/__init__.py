@@ -82,6 +82,7 @@ _sig = {
     "q8_0_moe_ffn": ([ctypes.POINTER(MoeFfnArgs), _vp, _sz, _vp], ctypes.c_int),
     "q8_0_probe_read": ([_vp, _sz, _vp, _vp], ctypes.c_int),
     "q8_0_probe_mfma_i8": ([_i32, _vp, _vp], ctypes.c_int),
+    "q8_0_probe_mfma_mix": ([_i32, _i32, _vp, _vp], ctypes.c_int),
     "q8_0_strerror": ([ctypes.c_int], ctypes.c_char_p),
 }
 for _name, (_args, _res) in _sig.items():
@@ -321,3 +322,11 @@ def q8_0_probe_read(buf: torch.Tensor, sink: torch.Tensor) -> None:
 def q8_0_probe_mfma_i8(iters: int, sink: torch.Tensor) -> None:
     _check(_lib.q8_0_probe_mfma_i8(int(iters), _dev(sink, "sink"), _stream()),
            "q8_0_probe_mfma_i8")
+
+
+def q8_0_probe_mfma_mix(iters: int, mix: int, sink: torch.Tensor) -> None:
+    """The GEMM's per-tile-block instruction mix (mix 1, or 2 with VALU
+    conversion; 0 = int8 MFMA alone), int8 work per round as
+    PROBE_MFMA_OPS_PER_ITER."""
+    _check(_lib.q8_0_probe_mfma_mix(int(iters), int(mix), _dev(sink, "sink"), _stream()),
+           "q8_0_probe_mfma_mix")

@@ -450,6 +450,13 @@ int q8_0_probe_mfma_i8(int32_t iters, uint32_t *sink, hipStream_t stream) {
   return status_of(q8::launch_probe_mfma(iters, sink, stream));
 }
 
+int q8_0_probe_mfma_mix(int32_t iters, int32_t mix, uint32_t *sink, hipStream_t stream) {
+  if (iters < 1 || mix < 0 || mix > 2 || !sink || !aligned(sink, 4)) return Q8_0_EINVAL;
+  int st = check_device();
+  if (st != Q8_0_OK) return st;
+  return status_of(q8::launch_probe_mix(iters, mix, sink, stream));
+}
+
 const char *q8_0_strerror(int status) {
   switch (status) {
     case Q8_0_OK: return "ok";

@@ -114,5 +114,6 @@ constexpr int kProbeWorkgroups = 512;  // 2 per CU, 4 waves each
 constexpr int kProbeChains = 4;        // independent MFMA chains per wave
 hipError_t launch_probe_read(const void *buf, int64_t bytes, uint32_t *sink, hipStream_t s);
 hipError_t launch_probe_mfma(int32_t iters, uint32_t *sink, hipStream_t s);
+hipError_t launch_probe_mix(int32_t iters, int32_t mix, uint32_t *sink, hipStream_t s);
 
 }  // namespace q8

@@ -60,6 +60,94 @@ __global__ __launch_bounds__(256) void probe_mfma_kernel(int32_t iters, uint32_t
   if (s == kNever) sink[0] = s;
 }
 
+// The prefill GEMM's per-tile-block instruction mix on registers only (no
+// memory traffic): MIX 1 is the four-tile kernel's tile step -- a biased int8
+// MFMA, the f16 scale MFMA, the f16 unbias MFMA and 16 fp32 fmas of the
+// previous tile, issued as [2 MFMA, 8 fma, 1 MFMA, 8 fma] -- and MIX 2 the
+// alternative with the int->float conversion on the VALU (int8 MFMA, scale
+// MFMA, then 16 converts and 16 fmas).  MIX 0 is the int8 MFMA alone in the
+// same loop.  Each wave runs 4 independent 32x32 tiles per round; two waves
+// per SIMD (512 workgroups of 4 waves).  Operands pass through empty asm
+// statements each round, so nothing is hoisted; the int8 work per round is
+// that of q8_0_probe_mfma_i8, so the rates compare directly.
+template <int MIX>
+__global__ __launch_bounds__(256, 2) void probe_mix_kernel(int32_t iters, uint32_t *sink) {
+  typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+  const int lane = threadIdx.x & 63;
+  const int h = lane >> 5;
+  i32x4 A[2] = {{lane, 3 * lane + 1, 5, 7}, {lane ^ 9, 2, 3, lane}};
+  i32x4 B[2] = {{11, lane ^ 5, 13, 17}, {lane, 1, 2, 3}};
+  uint32_t sa[2] = {0x3C00u + (uint32_t)lane, 0x3800u}, sb[2] = {0x3400u, 0x3000u + (uint32_t)lane};
+  const i32x16 ibias = {0x4B400000, 0x4B400000, 0x4B400000, 0x4B400000, 0x4B400000, 0x4B400000,
+                        0x4B400000, 0x4B400000, 0x4B400000, 0x4B400000, 0x4B400000, 0x4B400000,
+                        0x4B400000, 0x4B400000, 0x4B400000, 0x4B400000};
+  const f16x4 ua = h ? f16x4{0, 0, 0, 0} : f16x4{(_Float16)-3072.0f, 0, 0, 0};
+  const f16x4 ub = h ? f16x4{0, 0, 0, 0} : f16x4{(_Float16)4096.0f, 0, 0, 0};
+  const f32x16 fz = {};
+  const i32x16 iz = {};
+  f32x16 acc[4];
+  i32x16 iacc[4];
+  f32x16 Sf[2], Cf[2];
+  i32x16 Si[2];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    acc[q] = fz;
+    iacc[q] = iz;
+  }
+  Sf[1] = fz;
+  Cf[1] = fz;
+  Si[1] = iz;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) asm volatile("" : "+v"(acc[q]), "+v"(iacc[q]));
+  asm volatile("" : "+v"(Sf[1]), "+v"(Cf[1]), "+v"(Si[1]));
+  for (int it = 0; it < iters; ++it) {
+    asm volatile("" : "+v"(A[0]), "+v"(A[1]), "+v"(B[0]), "+v"(B[1]), "+v"(sa[0]), "+v"(sa[1]),
+                 "+v"(sb[0]), "+v"(sb[1]));
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int cs = q & 1, ps = (q + 1) & 1, pq = (q + 3) & 3;
+      const f16x4 SA = __builtin_bit_cast(f16x4, u32x2{sa[q >> 1], 0u});
+      const f16x4 SB = __builtin_bit_cast(f16x4, u32x2{sb[q & 1], 0u});
+      if constexpr (MIX == 0) {
+        iacc[q] = __builtin_amdgcn_mfma_i32_32x32x32_i8(A[q >> 1], B[q & 1], iacc[q], 0, 0, 0);
+      } else if constexpr (MIX == 1) {
+        const i32x16 biased = __builtin_amdgcn_mfma_i32_32x32x32_i8(A[q >> 1], B[q & 1], ibias, 0, 0, 0);
+        Cf[cs] = __builtin_amdgcn_mfma_f32_32x32x8f16(SA, SB, fz, 0, 0, 0);
+        Sf[cs] = __builtin_amdgcn_mfma_f32_32x32x8f16(ua, ub, __builtin_bit_cast(f32x16, biased), 0, 0, 0);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[pq][r] = fmaf(Sf[ps][r], Cf[ps][r], acc[pq][r]);
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      } else {
+        Si[cs] = __builtin_amdgcn_mfma_i32_32x32x32_i8(A[q >> 1], B[q & 1], iz, 0, 0, 0);
+        Cf[cs] = __builtin_amdgcn_mfma_f32_32x32x8f16(SA, SB, fz, 0, 0, 0);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[pq][r] = fmaf((float)Si[ps][r], Cf[ps][r], acc[pq][r]);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 16, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 16, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  }
+  // The results stay live through empty asm statements and a float sum (a
+  // bit cast of single vector elements is not used: it miscompiles here).
+#pragma unroll
+  for (int q = 0; q < 4; ++q) asm volatile("" : "+v"(acc[q]), "+v"(iacc[q]));
+  asm volatile("" : "+v"(Sf[0]), "+v"(Cf[1]), "+v"(Si[0]));
+  float v = Sf[0][0] + Cf[1][1] + (float)Si[0][2];
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) v += acc[q][r] + (float)iacc[q][r];
+  const uint32_t s = __builtin_bit_cast(uint32_t, v);
+  if (s == kNever) sink[0] = s;
+}
+
 }  // namespace
 
 hipError_t launch_probe_read(const void *buf, int64_t bytes, uint32_t *sink, hipStream_t s) {
@@ -72,6 +160,13 @@ hipError_t launch_probe_read(const void *buf, int64_t bytes, uint32_t *sink, hip
 
 hipError_t launch_probe_mfma(int32_t iters, uint32_t *sink, hipStream_t s) {
   hipLaunchKernelGGL(probe_mfma_kernel, dim3(kProbeWorkgroups), dim3(256), 0, s, iters, sink);
+  return hipGetLastError();
+}
+
+hipError_t launch_probe_mix(int32_t iters, int32_t mix, uint32_t *sink, hipStream_t s) {
+  if (mix == 0) hipLaunchKernelGGL(probe_mix_kernel<0>, dim3(kProbeWorkgroups), dim3(256), 0, s, iters, sink);
+  else if (mix == 1) hipLaunchKernelGGL(probe_mix_kernel<1>, dim3(kProbeWorkgroups), dim3(256), 0, s, iters, sink);
+  else hipLaunchKernelGGL(probe_mix_kernel<2>, dim3(kProbeWorkgroups), dim3(256), 0, s, iters, sink);
   return hipGetLastError();
 }
 

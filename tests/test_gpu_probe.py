@@ -53,3 +53,16 @@ def test_probe_mfma_runs_and_scales():
     say(f"[probe] mfma 100 rounds {t1:.1f} us, 800 rounds {t8:.1f} us ({tops:.0f} TOPS)")
     assert int(sink.item()) == 0
     assert t8 > 4 * t1
+
+
+@pytest.mark.parametrize("mix", [0, 1, 2])
+def test_probe_mfma_mix_runs_and_scales(mix):
+    q8 = _q8()
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    t1 = _time_us(lambda: q8.q8_0_probe_mfma_mix(100, mix, sink))
+    t8 = _time_us(lambda: q8.q8_0_probe_mfma_mix(800, mix, sink))
+    tops = q8.PROBE_MFMA_OPS_PER_ITER * 800 / (t8 * 1e-6) / 1e12
+    say(f"[probe] mix {mix}: 100 rounds {t1:.1f} us, 800 rounds {t8:.1f} us ({tops:.0f} TOPS of int8 work)")
+    assert int(sink.item()) == 0
+    assert t8 > 4 * t1
+
