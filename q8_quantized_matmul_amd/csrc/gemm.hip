@@ -488,36 +488,53 @@ __global__ __launch_bounds__(512, 1) void gemm_lds_kernel(const GemmArgs a) {
 // Each wave owns four independent 32x32 MFMA tiles, so the scale epilogue of
 // one tile (one fma per output and block; the int32 -> fp32 conversion runs
 // on the matrix core, see below) overlaps the matrix-core work of the next,
-// and two workgroups per CU give each SIMD two such waves.  That fits LDS only with 4-block stages:
-// a row's 4 blocks are 136 bytes, kept at a 144-byte LDS pitch so a stage
-// row is nine whole 16-byte chunks; (128 token rows + 128 weight rows) x 144
+// and two workgroups per CU give each SIMD two such waves.
+//
+// Stages of 4 blocks: a row's 4 blocks are a 136-byte slice (dwords d0..d33),
+// staged as nine 16-byte slots at a 144-byte LDS pitch -- slice dwords 0..3,
+// 4..7, ..., 28..31 and 30..33 -- so (128 token rows + 128 weight rows) x 144
 // bytes = 36 KB per stage, two stages per workgroup.  The stage is filled by
-// 16-byte direct-to-LDS loads: lane l of copy instruction k moves chunk
-// 64k + l of its wave's 64-row region, i.e. row (64k + l) / 9, chunk
-// (64k + l) % 9, so nine instructions with nine per-lane offsets cover the
-// wave's rows.  Chunks 0..7 are slice bytes 0..127; chunk 8 is slice bytes
-// 120..135 (it overlaps chunk 7, so no copy reads outside the slice), which
-// puts slice bytes 128..135 at LDS offset 136..143: the upper half of the
-// fourth block's quants is read from 8 bytes further on.
+// 16-byte direct-to-LDS loads: lane l of copy instruction k moves slot
+// (64k + l) % 9 of row (64k + l) / 9 of its wave's 64-row region, so nine
+// instructions cover the wave's rows.  The copies of the next stage are
+// spread over the current one (three after each of its first three blocks)
+// rather than issued together after the barrier.
+//
+// Operands.  A block dot sums qw_k * qx_k over k, so any permutation of k
+// applied to both operands gives the same S_b.  With the slice's pairs
+// d0..d16 and e0..e16 = d17..d33, a pair being
+//   [sA | qA0 qA1] [qA2 .. qA29] [qA30 qA31 | sB] [qB0 .. qB31],
+// the two 16-byte halves of each block's operand are
+//   block 0: {bfi(d0, d8), d1, d2, d3}   | {d4, d5, d6, d7}     slots 0 | 1
+//   block 1: {d16, d9, d10, d11}         | {d12, d13, d14, d15} slots 2 | 3
+//   block 2: {e7, bfi(e0, e8), e1, e2}   | {e3, e4, e5, e6}     slots 4 | 5
+//   block 3: {e11, e12, e9, e10}         | {e13, e14, e15, e16} slots 6 | 8
+// where bfi(a, b) takes a's high half (the block's first two quants) and b's
+// low half (its last two).  So every operand is one aligned 16-byte LDS read
+// (consecutive rows sit 9 slots apart, which keeps those reads free of bank
+// conflicts) plus, for half 0, one or two dwords of the next slot patched in
+// with v_bfi; half 1 reads the same patch address and keeps its own dwords.
+// The scales come out of the same reads: block 0's in d0's low half, block
+// 1's in d8's high half, block 2's in e0's low half, block 3's in e8's high
+// half.  (An earlier version realigned 24-byte windows with four v_alignbyte
+// per operand, from 8-byte reads that conflicted on every other row; this
+// one takes 1 instead of 4 VALU operations per operand and tile-block.)
 //
 // The MFMA's A operand is the token tile and B the weight tile, so a lane's
 // column of the result is an output column and the stores coalesce.  Only
 // whole tiles: out_dim and n_tok multiples of 128, in_dim of 128.  Its debug
 // instantiation writes every block's S_b as well.
 namespace t4 {
-constexpr int BO = 128;                     // output rows per workgroup
-constexpr int BT = 128;                     // tokens per workgroup
-constexpr int KB = 4;                       // blocks per stage
-constexpr int RB = 144;                     // LDS pitch of a row's 4-block slice (136 bytes used)
-constexpr int CH = RB / 16;                 // 9 chunks of 16 bytes per row
-constexpr int STAGE = (BO + BT) * RB;       // 36864 bytes
-constexpr int WAVE_BYTES = 64 * RB;         // each wave copies 64 rows
-constexpr int NCOPY = 64 * CH / 64;         // 9 copy instructions per wave and stage
-static_assert(KB * kBlockBytes <= RB && RB % 16 == 0, "stage row pitch");
+constexpr int BO = 128;
+constexpr int BT = 128;
+constexpr int KB = 4;
+constexpr int RB = 144;
+constexpr int CH = RB / 16;
+constexpr int STAGE = (BO + BT) * RB;
+constexpr int WAVE_BYTES = 64 * RB;
+constexpr int NCOPY = 64 * CH / 64;
 }  // namespace t4
 
-// STORE_S (debug): also writes each block's exact S_b to a.blocksums,
-// [n_tok][out_dim][nb] int32, from the same MFMA results the outputs use.
 template <bool STORE_S>
 __global__ __launch_bounds__(256, 2) void gemm_t4_kernel(const GemmArgs a) {
   using namespace t4;
@@ -532,11 +549,10 @@ __global__ __launch_bounds__(256, 2) void gemm_t4_kernel(const GemmArgs a) {
   const int64_t t_tile = (int64_t)tt * BT;
   const int64_t b_begin = (int64_t)ts * a.blocks_per_split;
   const int64_t b_end = min(b_begin + a.blocks_per_split, a.nb);
-  const int nstages = (int)((b_end - b_begin) / KB);  // splits are whole stages
+  const int nstages = (int)((b_end - b_begin) / KB);
 
-  // Copies: waves 0, 1 move token rows t_tile + 64 w + r, waves 2, 3 weight
-  // rows o_tile + 64 (w - 2) + r, into stage rows 64 w + r.  The base is
-  // uniform per wave; each lane adds its 32-bit offset.
+  // Copies as in the four-tile kernel: waves 0, 1 token rows, 2, 3 weight
+  // rows; lane l of copy k moves slot (64k + l) % 9 of row (64k + l) / 9.
   uint32_t off[NCOPY];
 #pragma unroll
   for (int k = 0; k < NCOPY; ++k) {
@@ -545,9 +561,6 @@ __global__ __launch_bounds__(256, 2) void gemm_t4_kernel(const GemmArgs a) {
     const int j = f - r * CH;
     off[k] = (uint32_t)(r * (int)a.row_bytes + (j < CH - 1 ? 16 * j : KB * kBlockBytes - 16));
   }
-  // The wave's 64 rows as one buffer (64 * row_bytes <= 2^30: the launcher
-  // takes this kernel only for rows of at most 2^24 bytes); the stage offset
-  // goes in the scalar offset.
   const uint8_t *copy_base = wave < 2 ? a.x_q + (t_tile + 64 * wave) * a.row_bytes
                                       : a.w + (o_tile + 64 * (wave - 2)) * a.row_bytes;
   const rsrc_t rsrc = make_rsrc(copy_base, (uint32_t)(64 * a.row_bytes));
@@ -563,232 +576,8 @@ __global__ __launch_bounds__(256, 2) void gemm_t4_kernel(const GemmArgs a) {
     }
   };
 
-  const int wt = wave & 1;   // tokens [64 wt, 64 wt + 64) of the tile
-  const int wo = wave >> 1;  // outputs [64 wo, 64 wo + 64)
-  const int lrow = lane & 31;
-  const int h = lane >> 5;
-  const f32x16 fzero = {};
-  f32x16 acc[4];
-#pragma unroll
-  for (int q = 0; q < 4; ++q)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) acc[q][r] = 0.0f;
-
-  typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-  // int32 -> fp32 on the matrix core.  The int8 MFMA accumulates onto
-  // 0x4B400000 (the bits of 1.5 * 2^23), so for |S_b| < 2^22 its result, read
-  // as fp32, is exactly 1.5 * 2^23 + S_b; a second f16 MFMA adds the constant
-  // product (-3072) * 4096 = -1.5 * 2^23 (K-slot 0, exact in f16 and fp32) to
-  // it, which leaves exactly float(S_b).  The vector ALU is then left with one
-  // fma per output and block instead of a convert and an fma.
-  const i32x16 ibias = {0x4B400000, 0x4B400000, 0x4B400000, 0x4B400000, 0x4B400000, 0x4B400000,
-                        0x4B400000, 0x4B400000, 0x4B400000, 0x4B400000, 0x4B400000, 0x4B400000,
-                        0x4B400000, 0x4B400000, 0x4B400000, 0x4B400000};
-  const f16x4 unbias_a = h ? f16x4{0, 0, 0, 0} : f16x4{(_Float16)-3072.0f, 0, 0, 0};
-  const f16x4 unbias_b = h ? f16x4{0, 0, 0, 0} : f16x4{(_Float16)4096.0f, 0, 0, 0};
-  // MFMA results of one tile: exact float(S_b) and the scale product.  Tile q
-  // of a block goes to slot q & 1 and its epilogue runs after the next tile's
-  // MFMAs are issued, from that slot; with four tiles per block the previous
-  // tile is always in the other slot.
-  struct TileOut {
-    f32x16 S;
-    f32x16 C;
-  };
-  TileOut slot[2];
-  slot[1].S = fzero;  // the tile "before" the first: adds exactly 0
-  slot[1].C = fzero;
-  auto epilogue = [&]<int Q>(const TileOut &o) {
-#pragma unroll
-    for (int r = 0; r < 16; ++r) acc[Q][r] = fmaf(o.S[r], o.C[r], acc[Q][r]);
-  };
-
-  issue(b_begin, 0);
-  for (int s = 0; s < nstages; ++s) {
-    __builtin_amdgcn_s_waitcnt(0);  // this wave's copies of stage s have landed
-    __syncthreads();                // ... and every wave's; buffer (s+1)&1 is free
-    if (s + 1 < nstages) issue(b_begin + (int64_t)(s + 1) * KB, (s + 1) & 1);
-    const uint8_t *st = ring + (s & 1) * STAGE;
-    const uint8_t *arow0 = st + (64 * wt + lrow) * RB;         // token rows
-    const uint8_t *arow1 = arow0 + 32 * RB;
-    const uint8_t *brow0 = st + (BT + 64 * wo + lrow) * RB;    // weight rows
-    const uint8_t *brow1 = brow0 + 32 * RB;
-
-    T4Raw ra0, ra1, rb0, rb1;
-    t4_read<0, true>(arow0, h, ra0);
-    t4_read<0, true>(arow1, h, ra1);
-    t4_read<0, true>(brow0, h, rb0);
-    t4_read<0, true>(brow1, h, rb1);
-    const int64_t stage_b0 = b_begin + (int64_t)s * KB;
-    [&]<int... B>(std::integer_sequence<int, B...>) {
-      (([&] {
-         // This block's index, bound here in the block's own scope (a pack
-         // element used inside the nested tile lambda is not reliable).
-         const int64_t blk = stage_b0 + B;
-         uint32_t sa0, sa1, sb0, sb1;
-         const i32x4 A0 = t4_prep<B>(ra0, h, sa0);
-         const i32x4 A1 = t4_prep<B>(ra1, h, sa1);
-         const i32x4 B0 = t4_prep<B>(rb0, h, sb0);
-         const i32x4 B1 = t4_prep<B>(rb1, h, sb1);
-         __builtin_amdgcn_sched_barrier(0);
-         if constexpr (B + 1 < KB) {
-           t4_read<B + 1, true>(arow0, h, ra0);
-           t4_read<B + 1, true>(arow1, h, ra1);
-           t4_read<B + 1, true>(brow0, h, rb0);
-           t4_read<B + 1, true>(brow1, h, rb1);
-         }
-         __builtin_amdgcn_sched_barrier(0);
-         const f16x4 SA[2] = {__builtin_bit_cast(f16x4, u32x2{sa0, 0u}),
-                              __builtin_bit_cast(f16x4, u32x2{sa1, 0u})};
-         const f16x4 SB[2] = {__builtin_bit_cast(f16x4, u32x2{sb0, 0u}),
-                              __builtin_bit_cast(f16x4, u32x2{sb1, 0u})};
-         const i32x4 AA[2] = {A0, A1};
-         const i32x4 BB[2] = {B0, B1};
-         [&]<int... Q>(std::integer_sequence<int, Q...>) {
-           (([&] {
-              TileOut &cur = slot[Q & 1];
-              const TileOut &prev = slot[(Q + 1) & 1];
-              // The tile steps run at raised wave priority and the operand
-              // preparation between blocks at the base level, so a wave
-              // entering its MFMAs is issued ahead of one preparing operands
-              // (prefill_a 93 -> 85 us on one box).
-              __builtin_amdgcn_s_setprio(1);
-              const i32x16 biased =
-                  __builtin_amdgcn_mfma_i32_32x32x32_i8(AA[Q >> 1], BB[Q & 1], ibias, 0, 0, 0);
-              cur.C = __builtin_amdgcn_mfma_f32_32x32x8f16(SA[Q >> 1], SB[Q & 1], fzero, 0, 0, 0);
-              cur.S = __builtin_amdgcn_mfma_f32_32x32x8f16(unbias_a, unbias_b,
-                                                          __builtin_bit_cast(f32x16, biased), 0, 0, 0);
-              if constexpr (STORE_S) {
-                // Tile Q: tokens t_tile + 64 wt + 32 (Q >> 1) + 8 (r >> 2) + 4 h + (r & 3),
-                // output column o_tile + 64 wo + 32 (Q & 1) + lrow.
-                const int64_t o = o_tile + 64 * wo + 32 * (Q & 1) + lrow;
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                  const int64_t t = t_tile + 64 * wt + 32 * (Q >> 1) + 8 * (r >> 2) + 4 * h + (r & 3);
-                  a.blocksums[(t * a.out_dim + o) * a.nb + blk] = (int32_t)cur.S[r];
-                }
-              }
-              epilogue.template operator()<(Q + 3) & 3>(prev);
-              // 3 MFMAs, the 16 fmas of the previous tile between them.
-              __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-              __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
-              __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-              __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
-              __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-              __builtin_amdgcn_s_setprio(0);
-              __builtin_amdgcn_sched_barrier(0);
-            }()), ...);
-         }(std::make_integer_sequence<int, 4>{});
-       }()), ...);
-    }(std::make_integer_sequence<int, KB>{});
-  }
-  epilogue.template operator()<3>(slot[1]);
-
-  // acc[q]: tokens t_tile + 64 wt + 32 (q >> 1) + 8 (r >> 2) + 4 h + (r & 3),
-  // output column o_tile + 64 wo + 32 (q & 1) + lrow.
-  float *dstp = a.out + (int64_t)ts * a.n_tok * a.out_dim;
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int64_t o = o_tile + 64 * wo + 32 * (q & 1) + lrow;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int64_t t = t_tile + 64 * wt + 32 * (q >> 1) + 8 * (r >> 2) + 4 * h + (r & 3);
-      dstp[t * a.out_dim + o] = acc[q][r];
-    }
-  }
-}
-
-// ---- Aligned-chunk kernel: 128 x 128 workgroup tiles, 4 waves of 64 x 64.
-//
-// Same tiles, MFMA chain and epilogue as the four-tile kernel; what changes is
-// what a stage holds.  A block pair is 68 bytes = 17 dwords d0..d16:
-//   d0 = [scale_A, qA0 qA1], d1..d7 = qA2..qA29, d8 = [qA30 qA31, scale_B],
-//   d9..d16 = qB0..qB31.
-// Block B's quants are four aligned dword pairs; block A's are not: they start
-// two bytes into d0 and end two bytes into d8.  A block dot sums qw_k * qx_k
-// over k, so any permutation of k applied to both operands gives the same S_b.
-// Block A is fed in the order (qA30 qA31 qA0 qA1, qA2..qA13 | qA14..qA29):
-// the first dword is d0 with its low half (the scale) replaced by d8's low half
-// (qA30 qA31), one v_bfi per operand; everything else is whole dwords.  So
-// each row's stage slice is staged as the 16-byte chunks
-//   d0..d3, d4..d7, d9..d12, d13..d16  (pair 0), the same for pair 1,
-// nine 16-byte slots at a 144-byte pitch (the ninth repeats the eighth), plus
-// d8 of each pair in a dword plane [pair][stage row].  Every MFMA operand is
-// then one aligned 16-byte LDS read (conflict-free: consecutive rows sit 9
-// chunks apart), block A's also one dword read of the plane (consecutive rows,
-// consecutive dwords), and the block scales come out of those reads: block
-// A's is the low half of d0, block B's the high half of d8.
-namespace p4 {
-constexpr int BO = 128;
-constexpr int BT = 128;
-constexpr int KB = 4;                     // blocks per stage (two pairs)
-constexpr int RB = 144;                   // LDS pitch of a row's slots
-constexpr int CH = RB / 16;               // 9 slots
-constexpr int ROWS = BO + BT;
-constexpr int QBYTES = ROWS * RB;         // 36864
-constexpr int STAGE = QBYTES + 2 * ROWS * 4;  // + d8 plane [pair][row]: 38912
-constexpr int WAVE_BYTES = 64 * RB;
-constexpr int NCOPY = 64 * CH / 64;       // 9 chunk copies per wave and stage
-// Source byte of slot j inside the row's 136-byte stage slice.
-__host__ __device__ constexpr int slot_src(int j) {
-  return j >= 8 ? 120 : 68 * (j >> 2) + ((j & 3) == 0 ? 0 : (j & 3) == 1 ? 16 : (j & 3) == 2 ? 36 : 52);
-}
-static_assert(slot_src(7) + 16 <= KB * kBlockBytes, "slots stay inside the slice");
-}  // namespace p4
-
-__global__ __launch_bounds__(256, 2) void gemm_p4_kernel(const GemmArgs a) {
-  using namespace p4;
-  __shared__ __attribute__((aligned(16))) uint8_t ring[2 * STAGE];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  int to, tt, ts;
-  tile_of(a, to, tt, ts);
-  const int64_t o_tile = (int64_t)to * BO;
-  const int64_t t_tile = (int64_t)tt * BT;
-  const int64_t b_begin = (int64_t)ts * a.blocks_per_split;
-  const int64_t b_end = min(b_begin + a.blocks_per_split, a.nb);
-  const int nstages = (int)((b_end - b_begin) / KB);  // splits are whole stages
-
-  // Copies: waves 0, 1 move token rows t_tile + 64 w + r, waves 2, 3 weight
-  // rows o_tile + 64 (w - 2) + r, into stage rows 64 w + r.  Chunk copy k,
-  // lane l: slot (64k + l) % 9 of row (64k + l) / 9.  Plane copy pp, lane l:
-  // d8 of pair pp of row l.
-  uint32_t off[NCOPY];
-#pragma unroll
-  for (int k = 0; k < NCOPY; ++k) {
-    const int f = 64 * k + lane;
-    const int r = f / CH;
-    off[k] = (uint32_t)(r * (int)a.row_bytes + slot_src(f - r * CH));
-  }
-  const uint32_t doff = (uint32_t)(lane * (int)a.row_bytes + 32);
-  const uint8_t *copy_base = wave < 2 ? a.x_q + (t_tile + 64 * wave) * a.row_bytes
-                                      : a.w + (o_tile + 64 * (wave - 2)) * a.row_bytes;
-  const rsrc_t rsrc = make_rsrc(copy_base, (uint32_t)(64 * a.row_bytes));
-  auto issue = [&](int64_t b0, int buf) {
-    const uint32_t lds = (uint32_t)reinterpret_cast<uintptr_t>(ring + buf * STAGE + wave * WAVE_BYTES);
-    const uint32_t plane = (uint32_t)reinterpret_cast<uintptr_t>(ring + buf * STAGE + QBYTES + 256 * wave);
-    const int sb = (int)(b0 * kBlockBytes);
-#pragma unroll
-    for (int k = 0; k < NCOPY; ++k) {
-      buffer_load_lds_raw(rsrc,
-                          reinterpret_cast<__attribute__((address_space(3))) uint32_t *>(
-                              (uintptr_t)(lds + 1024 * k)),
-                          16, (int)off[k], sb, 0, 0);
-    }
-    buffer_load_lds_raw(rsrc,
-                        reinterpret_cast<__attribute__((address_space(3))) uint32_t *>((uintptr_t)plane),
-                        4, (int)doff, sb, 0, 0);
-    // (An LDS-DMA load adds its instruction offset to the LDS address as
-    // well, so the pair offset goes in the scalar offset.)
-    buffer_load_lds_raw(rsrc,
-                        reinterpret_cast<__attribute__((address_space(3))) uint32_t *>(
-                            (uintptr_t)(plane + 4 * ROWS)),
-                        4, (int)doff, sb + 68, 0, 0);
-  };
-
-  const int wt = wave & 1;   // tokens [64 wt, 64 wt + 64) of the tile
-  const int wo = wave >> 1;  // outputs [64 wo, 64 wo + 64)
+  const int wt = wave & 1;
+  const int wo = wave >> 1;
   const int lrow = lane & 31;
   const int h = lane >> 5;
   const f32x16 fzero = {};
@@ -804,13 +593,14 @@ __global__ __launch_bounds__(256, 2) void gemm_p4_kernel(const GemmArgs a) {
                         0x4B400000, 0x4B400000, 0x4B400000, 0x4B400000};
   const f16x4 unbias_a = h ? f16x4{0, 0, 0, 0} : f16x4{(_Float16)-3072.0f, 0, 0, 0};
   const f16x4 unbias_b = h ? f16x4{0, 0, 0, 0} : f16x4{(_Float16)4096.0f, 0, 0, 0};
-  // Lane constants: the first dword of block A's operand keeps d0's high half
-  // and takes d8's low half (half 0; half 1 keeps its own dword), and the
-  // scale selectors leave the scale's two bytes in the low half (half 0) or
-  // zero (half 1: its K slots of the scale MFMA are zero).
+  // bfi masks (bits taken from the slot dword; the rest from the patch):
+  // keep the high half on half 0 / everything on half 1; keep nothing on
+  // half 0 / everything on half 1.
   const uint32_t keep_hi = h ? 0xFFFFFFFFu : 0xFFFF0000u;
-  const uint32_t sel_a = h ? 0x0C0C0C0Cu : 0x0C0C0100u;  // bytes 0, 1 of d0
-  const uint32_t sel_b = h ? 0x0C0C0C0Cu : 0x0C0C0302u;  // bytes 2, 3 of d8
+  const uint32_t keep_h1 = h ? 0xFFFFFFFFu : 0u;
+  const uint32_t sel_lo = h ? 0x0C0C0C0Cu : 0x0C0C0100u;  // bytes 0, 1 (scale in the low half)
+  const uint32_t sel_hi = h ? 0x0C0C0C0Cu : 0x0C0C0302u;  // bytes 2, 3 (scale in the high half)
+  auto bfi = [](uint32_t keep, uint32_t x, uint32_t y) { return (x & keep) | (y & ~keep); };
 
   struct TileOut {
     f32x16 S;
@@ -824,64 +614,82 @@ __global__ __launch_bounds__(256, 2) void gemm_p4_kernel(const GemmArgs a) {
     for (int r = 0; r < 16; ++r) acc[Q][r] = fmaf(o.S[r], o.C[r], acc[Q][r]);
   };
 
-  // Raw LDS data of one operand of block B of the stage: the 16-byte slot,
-  // and for block A of a pair (even B) the pair's d8.
+  // Raw operand of block B for the row at `row`: the half's 16-byte slot and
+  // the patch dwords from the slot after half 0's.
   struct Raw {
     i32x4 v;
-    uint32_t d8;
+    uint32_t p0, p1;
   };
-  auto read_raw = [&]<int B>(const uint8_t *st, int row, Raw &r) {
-    constexpr int pp = B >> 1;
-    r.v = *reinterpret_cast<const i32x4 *>(st + row * RB + 16 * (4 * pp + 2 * (B & 1)) + 16 * h);
-    if constexpr ((B & 1) == 0)
-      r.d8 = *reinterpret_cast<const uint32_t *>(st + QBYTES + 4 * (ROWS * pp + row));
-  };
-  // The operand and its scale bits (low half; zero on half 1).
-  auto prep = [&]<int B>(const Raw &r, uint32_t d8, uint32_t &scale) -> i32x4 {
-    if constexpr ((B & 1) == 0) {
-      scale = __builtin_amdgcn_perm(0u, (uint32_t)r.v.x, sel_a);
-      const uint32_t first = ((uint32_t)r.v.x & keep_hi) | (d8 & ~keep_hi);
-      return i32x4{(int)first, r.v.y, r.v.z, r.v.w};
+  auto read_raw = [&]<int B>(const uint8_t *row, Raw &r) {
+    constexpr int S0 = B == 0 ? 0 : B == 1 ? 2 : B == 2 ? 4 : 6;   // half 0's slot
+    constexpr int S1 = B == 3 ? 8 : S0 + 1;                         // half 1's slot
+    constexpr int SP = B == 3 ? 7 : S0 + 2;                         // patch slot
+    r.v = *reinterpret_cast<const i32x4 *>(row + 16 * (h ? S1 : S0));
+    if constexpr (B < 2) {
+      r.p0 = *reinterpret_cast<const uint32_t *>(row + 16 * SP);
     } else {
-      scale = __builtin_amdgcn_perm(0u, d8, sel_b);
-      return r.v;
+      const u32x2 pp = *reinterpret_cast<const u32x2 *>(row + 16 * SP);
+      r.p0 = pp.x;
+      r.p1 = pp.y;
     }
+  };
+  auto prep = [&]<int B>(const Raw &r, uint32_t &scale) -> i32x4 {
+    uint32_t v0 = (uint32_t)r.v.x, v1 = (uint32_t)r.v.y;
+    if constexpr (B == 0) {           // {bfi(d0, d8), d1, d2, d3}
+      scale = __builtin_amdgcn_perm(0u, v0, sel_lo);
+      v0 = bfi(keep_hi, v0, r.p0);
+    } else if constexpr (B == 1) {    // {d16, d9, d10, d11}
+      scale = __builtin_amdgcn_perm(0u, v0, sel_hi);
+      v0 = bfi(keep_h1, v0, r.p0);
+    } else if constexpr (B == 2) {    // {e7, bfi(e0, e8), e1, e2}
+      scale = __builtin_amdgcn_perm(0u, v1, sel_lo);
+      v1 = bfi(keep_hi, v1, r.p1);
+      v0 = bfi(keep_h1, v0, r.p0);
+    } else {                          // {e11, e12, e9, e10}
+      scale = __builtin_amdgcn_perm(0u, v1, sel_hi);
+      v0 = bfi(keep_h1, v0, r.p0);
+      v1 = bfi(keep_h1, v1, r.p1);
+    }
+    return i32x4{(int)v0, (int)v1, r.v.z, r.v.w};
   };
 
   issue(b_begin, 0);
   for (int s = 0; s < nstages; ++s) {
     __builtin_amdgcn_s_waitcnt(0);  // this wave's copies of stage s have landed
     __syncthreads();                // ... and every wave's; buffer (s+1)&1 is free
-    if (s + 1 < nstages) issue(b_begin + (int64_t)(s + 1) * KB, (s + 1) & 1);
     const uint8_t *st = ring + (s & 1) * STAGE;
-    const int ra0 = 64 * wt + lrow, ra1 = ra0 + 32;            // token rows
-    const int rb0 = BT + 64 * wo + lrow, rb1 = rb0 + 32;       // weight rows
+    const uint8_t *arow0 = st + (64 * wt + lrow) * RB;
+    const uint8_t *arow1 = arow0 + 32 * RB;
+    const uint8_t *brow0 = st + (BT + 64 * wo + lrow) * RB;
+    const uint8_t *brow1 = brow0 + 32 * RB;
+    const int64_t stage_b0 = b_begin + (int64_t)s * KB;
+    // The next stage's copies go out three at a time after blocks 0..2.  On
+    // the last stage they re-read this stage into the idle buffer (in
+    // bounds, never read) instead of branching: a branch in the middle of
+    // the pipelined block sequence made the compiler spill.
+    const uint32_t next_lds =
+        (uint32_t)reinterpret_cast<uintptr_t>(ring + ((s + 1) & 1) * STAGE + wave * WAVE_BYTES);
+    const int next_sb = (int)((b_begin + (int64_t)(s + 1 < nstages ? s + 1 : s) * KB) * kBlockBytes);
 
     Raw xa0, xa1, xb0, xb1;
-    uint32_t d8a0 = 0, d8a1 = 0, d8b0 = 0, d8b1 = 0;  // the current pair's d8
-    read_raw.template operator()<0>(st, ra0, xa0);
-    read_raw.template operator()<0>(st, ra1, xa1);
-    read_raw.template operator()<0>(st, rb0, xb0);
-    read_raw.template operator()<0>(st, rb1, xb1);
+    read_raw.template operator()<0>(arow0, xa0);
+    read_raw.template operator()<0>(arow1, xa1);
+    read_raw.template operator()<0>(brow0, xb0);
+    read_raw.template operator()<0>(brow1, xb1);
     [&]<int... B>(std::integer_sequence<int, B...>) {
       (([&] {
-         if constexpr ((B & 1) == 0) {
-           d8a0 = xa0.d8;
-           d8a1 = xa1.d8;
-           d8b0 = xb0.d8;
-           d8b1 = xb1.d8;
-         }
+         const int64_t blk = stage_b0 + B;
          uint32_t sa0, sa1, sb0, sb1;
-         const i32x4 A0 = prep.template operator()<B>(xa0, d8a0, sa0);
-         const i32x4 A1 = prep.template operator()<B>(xa1, d8a1, sa1);
-         const i32x4 B0 = prep.template operator()<B>(xb0, d8b0, sb0);
-         const i32x4 B1 = prep.template operator()<B>(xb1, d8b1, sb1);
+         const i32x4 A0 = prep.template operator()<B>(xa0, sa0);
+         const i32x4 A1 = prep.template operator()<B>(xa1, sa1);
+         const i32x4 B0 = prep.template operator()<B>(xb0, sb0);
+         const i32x4 B1 = prep.template operator()<B>(xb1, sb1);
          __builtin_amdgcn_sched_barrier(0);
          if constexpr (B + 1 < KB) {
-           read_raw.template operator()<B + 1>(st, ra0, xa0);
-           read_raw.template operator()<B + 1>(st, ra1, xa1);
-           read_raw.template operator()<B + 1>(st, rb0, xb0);
-           read_raw.template operator()<B + 1>(st, rb1, xb1);
+           read_raw.template operator()<B + 1>(arow0, xa0);
+           read_raw.template operator()<B + 1>(arow1, xa1);
+           read_raw.template operator()<B + 1>(brow0, xb0);
+           read_raw.template operator()<B + 1>(brow1, xb1);
          }
          __builtin_amdgcn_sched_barrier(0);
          const f16x4 SA[2] = {__builtin_bit_cast(f16x4, u32x2{sa0, 0u}),
@@ -900,11 +708,15 @@ __global__ __launch_bounds__(256, 2) void gemm_p4_kernel(const GemmArgs a) {
               cur.C = __builtin_amdgcn_mfma_f32_32x32x8f16(SA[Q >> 1], SB[Q & 1], fzero, 0, 0, 0);
               cur.S = __builtin_amdgcn_mfma_f32_32x32x8f16(unbias_a, unbias_b,
                                                           __builtin_bit_cast(f32x16, biased), 0, 0, 0);
+              if constexpr (STORE_S) {
+                const int64_t o = o_tile + 64 * wo + 32 * (Q & 1) + lrow;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                  const int64_t t = t_tile + 64 * wt + 32 * (Q >> 1) + 8 * (r >> 2) + 4 * h + (r & 3);
+                  a.blocksums[(t * a.out_dim + o) * a.nb + blk] = (int32_t)cur.S[r];
+                }
+              }
               epilogue.template operator()<(Q + 3) & 3>(prev);
-              // Block sums and scales of this tile, 8 fmas of the previous
-              // tile, the unbias of this tile, its other 8 fmas: the unbias
-              // waits on the int8 MFMA across a group, and the next step's
-              // fmas wait on this unbias across two MFMAs.
               __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
               __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
               __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
@@ -913,10 +725,22 @@ __global__ __launch_bounds__(256, 2) void gemm_p4_kernel(const GemmArgs a) {
               __builtin_amdgcn_sched_barrier(0);
             }()), ...);
          }(std::make_integer_sequence<int, 4>{});
+         if constexpr (B < 3) {
+#pragma unroll
+           for (int kk = 0; kk < 3; ++kk) {
+             const int k = 3 * B + kk;
+             buffer_load_lds_raw(rsrc,
+                                 reinterpret_cast<__attribute__((address_space(3))) uint32_t *>(
+                                     (uintptr_t)(next_lds + 1024 * k)),
+                                 16, (int)off[k], next_sb, 0, 0);
+           }
+         }
+         __builtin_amdgcn_sched_barrier(0);
        }()), ...);
     }(std::make_integer_sequence<int, KB>{});
   }
   epilogue.template operator()<3>(slot[1]);
+  __builtin_amdgcn_s_waitcnt(0);  // the last stage's copies land before the workgroup ends
 
   float *dstp = a.out + (int64_t)ts * a.n_tok * a.out_dim;
 #pragma unroll
