@@ -95,9 +95,15 @@ size_t q8_0_matmul_workspace_bytes(int64_t in_dim, int64_t out_dim, int64_t n_to
  *   out : fp32 [n_tok][out_dim], written.
  *   w   : Q8_0 [out_dim][in_dim/32] blocks.
  *   x_q : Q8_0 [n_tok][in_dim/32] blocks (e.g. from q8_0_quantize_act).
- *   workspace / workspace_bytes : optional caller scratch (device memory) for
- *     split-K partials; with less than q8_0_matmul_workspace_bytes() the
- *     library picks a plan that fits (same results up to fp32 summation order).
+ *   workspace / workspace_bytes : optional caller scratch (device memory,
+ *     16-byte aligned) for split-K plans; with less than
+ *     q8_0_matmul_workspace_bytes() the library picks a plan that fits (same
+ *     results up to fp32 summation order).  Zero-fill it once before its
+ *     first use and keep it for later calls: its first 4096 bytes hold the
+ *     arrival counters of the in-launch split-K reduction, which every call
+ *     leaves at zero again (the partial sums after them need no
+ *     initialization).  Calls that share a workspace must not overlap in time
+ *     (issue them on one stream).
  *     These two arguments are an addition to the pages' matmul signature: the
  *     library allocates nothing ("Part 6: GPU 加速", summary: no allocation on
  *     the hot path), so a split-K plan needs its partials from the caller;
@@ -266,7 +272,9 @@ int q8_0_matmul_list(const q8_0_matmul_item *items, int32_t n_items, int64_t n_t
  * The kernel that runs is the one the same call without blocksums would run
  * (its debug instantiation), so the S_b checked are those of the timed path.
  * Errors as q8_0_matmul, plus Q8_0_EINVAL when the forced variant cannot run
- * this shape, and Q8_0_EWORKSPACE when a forced split needs more workspace. */
+ * this shape (also a skinny split-K over more than 1024 output tiles of 32
+ * rows), and Q8_0_EWORKSPACE when a forced split needs more workspace than
+ * q8_0_matmul_debug_workspace_bytes() reports for it. */
 int q8_0_matmul_debug(float *out, int32_t *blocksums, const void *w,
                       int64_t in_dim, int64_t out_dim, const void *x_q,
                       int64_t n_tok, void *workspace, size_t workspace_bytes,
@@ -281,6 +289,13 @@ int q8_0_moe_grouped_debug(float *out, int32_t *blocksums,
                            const void *x_q, int32_t x_rows, int64_t n_tok,
                            void *workspace, size_t workspace_bytes,
                            hipStream_t stream);
+
+/* Host-only: workspace bytes q8_0_matmul_debug needs for this shape with the
+ * forced variant and split-K count (as there; 0 = automatic), under the same
+ * zero-fill rule as q8_0_matmul's workspace.  0 when that plan needs none or
+ * cannot run this shape. */
+size_t q8_0_matmul_debug_workspace_bytes(int64_t in_dim, int64_t out_dim, int64_t n_tok,
+                                         int32_t variant, int32_t split_k);
 
 /* Host-only: the kernel variant and split-K count q8_0_matmul would use for
  * this shape and workspace, assuming suitably aligned pointers.  Touches no

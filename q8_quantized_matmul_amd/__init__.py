@@ -75,6 +75,7 @@ _sig = {
                           ctypes.c_int),
     "q8_0_moe_grouped_debug": ([_vp, _vp, _vp, _i32, _i64, _i64, _vp, _i32, _vp, _i32, _i64, _vp,
                                 _sz, _vp], ctypes.c_int),
+    "q8_0_matmul_debug_workspace_bytes": ([_i64, _i64, _i64, _i32, _i32], _sz),
     "q8_0_matmul_plan": ([_i64, _i64, _i64, _sz, ctypes.POINTER(_i32), ctypes.POINTER(_i32)],
                          ctypes.c_int),
     "q8_0_matmul_list": ([ctypes.POINTER(MatmulItem), _i32, _i64, _vp], ctypes.c_int),
@@ -142,9 +143,17 @@ def q8_0_matmul_workspace_bytes(in_dim: int, out_dim: int, n_tok: int) -> int:
     return int(_lib.q8_0_matmul_workspace_bytes(in_dim, out_dim, n_tok))
 
 
-def matmul_workspace(in_dim: int, out_dim: int, n_tok: int, device="cuda") -> torch.Tensor:
-    n = q8_0_matmul_workspace_bytes(in_dim, out_dim, n_tok)
-    return torch.empty(max(n, 1), dtype=torch.uint8, device=device)
+def q8_0_matmul_debug_workspace_bytes(in_dim: int, out_dim: int, n_tok: int, variant: int = 0,
+                                      split_k: int = 0) -> int:
+    return int(_lib.q8_0_matmul_debug_workspace_bytes(in_dim, out_dim, n_tok, variant, split_k))
+
+
+def matmul_workspace(in_dim: int, out_dim: int, n_tok: int, device="cuda", variant: int = 0,
+                     split_k: int = 0) -> torch.Tensor:
+    """A zero-filled workspace for this shape and plan (the split-K counters
+    at its start must be zero before first use; calls leave them zero)."""
+    n = q8_0_matmul_debug_workspace_bytes(in_dim, out_dim, n_tok, variant, split_k)
+    return torch.zeros(max(n, 1), dtype=torch.uint8, device=device)
 
 
 def q8_0_matmul(w: torch.Tensor, x_q: torch.Tensor, in_dim: int, out_dim: int, n_tok: int,
@@ -171,7 +180,7 @@ def q8_0_matmul_debug(w, x_q, in_dim, out_dim, n_tok, variant=KERNEL_AUTO, split
         bs = torch.empty((n_tok, out_dim, in_dim // BLOCK_ELEMS), dtype=torch.int32,
                          device=w.device)
     if workspace is None:
-        workspace = matmul_workspace(in_dim, out_dim, n_tok, w.device)
+        workspace = matmul_workspace(in_dim, out_dim, n_tok, w.device, variant, split_k)
     _check(_lib.q8_0_matmul_debug(_dev(out, "out", torch.float32),
                                   _dev(bs, "blocksums") if bs is not None else None,
                                   _dev(w, "w"), in_dim, out_dim, _dev(x_q, "x_q"), n_tok,

@@ -61,7 +61,7 @@ Plan make_plan(int64_t in_dim, int64_t out_dim, int64_t n_tok, size_t ws_bytes, 
   if (!fast_align) return p;
   if (n_tok >= kSkinnyMinTokens && q8::skinny_supported(in_dim, n_tok)) {
     p.variant = Q8_0_KERNEL_SKINNY;
-    int split = q8::skinny_auto_split(in_dim, out_dim);
+    int split = q8::skinny_split_ok(out_dim, 2) ? q8::skinny_auto_split(in_dim, out_dim, n_tok) : 1;
     while (split > 1 && q8::skinny_workspace_bytes(out_dim, n_tok, split) > ws_bytes) --split;
     p.split = split;
   } else if (n_tok > q8::kSkinnyMaxTokens && q8::gemm_supported(in_dim)) {
@@ -73,6 +73,35 @@ Plan make_plan(int64_t in_dim, int64_t out_dim, int64_t n_tok, size_t ws_bytes, 
     p.variant = Q8_0_KERNEL_MATVEC;
   }
   return p;
+}
+
+// The plan for a forced variant and split-K count (0 = automatic).
+int forced_plan(int64_t in_dim, int64_t out_dim, int64_t n_tok, size_t ws_bytes, bool fast_align,
+                int32_t variant, int32_t split_k, Plan *out) {
+  if (split_k < 0 || variant < 0 || variant > Q8_0_KERNEL_SKINNY) return Q8_0_EINVAL;
+  Plan p = make_plan(in_dim, out_dim, n_tok, ws_bytes, fast_align);
+  if (variant != Q8_0_KERNEL_AUTO) {
+    if (variant != Q8_0_KERNEL_GENERIC && !fast_align) return Q8_0_EINVAL;
+    if (variant == Q8_0_KERNEL_MATVEC && !matvec_ok(in_dim)) return Q8_0_EINVAL;
+    if (variant == Q8_0_KERNEL_MFMA && !q8::gemm_supported(in_dim)) return Q8_0_EINVAL;
+    if (variant == Q8_0_KERNEL_SKINNY && !q8::skinny_supported(in_dim, n_tok)) return Q8_0_EINVAL;
+    if (variant != p.variant) p.split = 1;
+    p.variant = variant;
+  }
+  if (split_k > 0) {
+    if (p.variant != Q8_0_KERNEL_MFMA && p.variant != Q8_0_KERNEL_SKINNY && split_k != 1)
+      return Q8_0_EINVAL;
+    p.split = split_k;
+  }
+  if (p.variant == Q8_0_KERNEL_SKINNY && !q8::skinny_split_ok(out_dim, p.split)) return Q8_0_EINVAL;
+  *out = p;
+  return Q8_0_OK;
+}
+
+size_t plan_workspace_bytes(const Plan &p, int64_t out_dim, int64_t n_tok) {
+  if (p.variant == Q8_0_KERNEL_SKINNY) return q8::skinny_workspace_bytes(out_dim, n_tok, p.split);
+  if (p.variant == Q8_0_KERNEL_MFMA) return q8::gemm_workspace_bytes(out_dim, n_tok, p.split);
+  return 0;
 }
 
 int validate_matmul(const float *out, const void *w, int64_t in_dim, int64_t out_dim,
@@ -93,36 +122,20 @@ int run_matmul(float *out, int32_t *blocksums, const void *w, int64_t in_dim, in
   if (st != Q8_0_OK || n_tok == 0 || out_dim == 0) return st;
   if (workspace == nullptr) workspace_bytes = 0;
   if (workspace && !aligned(workspace, 16)) return Q8_0_EALIGN;
-  if (split_k < 0 || variant < 0 || variant > Q8_0_KERNEL_SKINNY) return Q8_0_EINVAL;
   const bool fast_align = aligned(w, 4) && aligned(x_q, 4);
-  Plan p = make_plan(in_dim, out_dim, n_tok, workspace_bytes, fast_align);
-  if (variant != Q8_0_KERNEL_AUTO) {
-    if (variant != Q8_0_KERNEL_GENERIC && !fast_align) return Q8_0_EINVAL;
-    if (variant == Q8_0_KERNEL_MATVEC && !matvec_ok(in_dim)) return Q8_0_EINVAL;
-    if (variant == Q8_0_KERNEL_MFMA && !q8::gemm_supported(in_dim)) return Q8_0_EINVAL;
-    if (variant == Q8_0_KERNEL_SKINNY && !q8::skinny_supported(in_dim, n_tok)) return Q8_0_EINVAL;
-    if (variant != p.variant) p.split = 1;
-    p.variant = variant;
-  }
-  if (split_k > 0) {
-    if (p.variant != Q8_0_KERNEL_MFMA && p.variant != Q8_0_KERNEL_SKINNY && split_k != 1)
-      return Q8_0_EINVAL;
-    p.split = split_k;
-  }
-  if (p.variant == Q8_0_KERNEL_MFMA && p.split > 1 &&
-      q8::gemm_workspace_bytes(out_dim, n_tok, p.split) > workspace_bytes)
-    return Q8_0_EWORKSPACE;
-  if (p.variant == Q8_0_KERNEL_SKINNY && p.split > 1 &&
-      q8::skinny_workspace_bytes(out_dim, n_tok, p.split) > workspace_bytes)
-    return Q8_0_EWORKSPACE;
+  Plan p;
+  if ((st = forced_plan(in_dim, out_dim, n_tok, workspace_bytes, fast_align, variant, split_k, &p)) !=
+      Q8_0_OK)
+    return st;
+  if (plan_workspace_bytes(p, out_dim, n_tok) > workspace_bytes) return Q8_0_EWORKSPACE;
   if ((st = check_device()) != Q8_0_OK) return st;
   switch (p.variant) {
     case Q8_0_KERNEL_MFMA:
       return status_of(q8::launch_gemm(out, blocksums, w, in_dim, out_dim, x_q, n_tok, p.split,
-                                       static_cast<float *>(workspace), stream));
+                                       workspace, stream));
     case Q8_0_KERNEL_SKINNY:
       return status_of(q8::launch_skinny(out, blocksums, w, in_dim, out_dim, x_q, n_tok, p.split,
-                                         static_cast<float *>(workspace), stream));
+                                         workspace, stream));
     case Q8_0_KERNEL_MATVEC:
       return status_of(q8::launch_matvec(out, blocksums, w, in_dim, out_dim, x_q, n_tok, stream));
     default:
@@ -355,10 +368,15 @@ int q8_0_quantize_act(void *x_q, const float *x, int64_t n_tok, int64_t in_dim,
 }
 
 size_t q8_0_matmul_workspace_bytes(int64_t in_dim, int64_t out_dim, int64_t n_tok) {
+  return q8_0_matmul_debug_workspace_bytes(in_dim, out_dim, n_tok, Q8_0_KERNEL_AUTO, 0);
+}
+
+size_t q8_0_matmul_debug_workspace_bytes(int64_t in_dim, int64_t out_dim, int64_t n_tok,
+                                         int32_t variant, int32_t split_k) {
   if (in_dim <= 0 || out_dim <= 0 || n_tok <= 0 || in_dim % Q8_0_BLOCK_ELEMS != 0) return 0;
-  Plan p = make_plan(in_dim, out_dim, n_tok, SIZE_MAX, true);
-  if (p.variant == Q8_0_KERNEL_SKINNY) return q8::skinny_workspace_bytes(out_dim, n_tok, p.split);
-  return p.variant == Q8_0_KERNEL_MFMA ? q8::gemm_workspace_bytes(out_dim, n_tok, p.split) : 0;
+  Plan p;
+  if (forced_plan(in_dim, out_dim, n_tok, SIZE_MAX, true, variant, split_k, &p) != Q8_0_OK) return 0;
+  return plan_workspace_bytes(p, out_dim, n_tok);
 }
 
 int q8_0_matmul(float *out, const void *w, int64_t in_dim, int64_t out_dim, const void *x_q,

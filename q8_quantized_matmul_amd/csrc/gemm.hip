@@ -500,25 +500,12 @@ __global__ __launch_bounds__(512, 1) void gemm_lds_kernel(const GemmArgs a) {
 // spread over the current one (three after each of its first three blocks)
 // rather than issued together after the barrier.
 //
-// Operands.  A block dot sums qw_k * qx_k over k, so any permutation of k
-// applied to both operands gives the same S_b.  With the slice's pairs
-// d0..d16 and e0..e16 = d17..d33, a pair being
-//   [sA | qA0 qA1] [qA2 .. qA29] [qA30 qA31 | sB] [qB0 .. qB31],
-// the two 16-byte halves of each block's operand are
-//   block 0: {bfi(d0, d8), d1, d2, d3}   | {d4, d5, d6, d7}     slots 0 | 1
-//   block 1: {d16, d9, d10, d11}         | {d12, d13, d14, d15} slots 2 | 3
-//   block 2: {e7, bfi(e0, e8), e1, e2}   | {e3, e4, e5, e6}     slots 4 | 5
-//   block 3: {e11, e12, e9, e10}         | {e13, e14, e15, e16} slots 6 | 8
-// where bfi(a, b) takes a's high half (the block's first two quants) and b's
-// low half (its last two).  So every operand is one aligned 16-byte LDS read
-// (consecutive rows sit 9 slots apart, which keeps those reads free of bank
-// conflicts) plus, for half 0, one or two dwords of the next slot patched in
-// with v_bfi; half 1 reads the same patch address and keeps its own dwords.
-// The scales come out of the same reads: block 0's in d0's low half, block
-// 1's in d8's high half, block 2's in e0's low half, block 3's in e8's high
-// half.  (An earlier version realigned 24-byte windows with four v_alignbyte
-// per operand, from 8-byte reads that conflicted on every other row; this
-// one takes 1 instead of 4 VALU operations per operand and tile-block.)
+// Operands: K permuted the same way on both sides so that each is one
+// aligned 16-byte LDS read plus a v_bfi patch (perm_read / perm_prep in
+// q8_device.h, which states the permutation).  (An earlier version realigned
+// 24-byte windows with four v_alignbyte per operand, from 8-byte reads that
+// conflicted on every other row; this one takes 1 instead of 4 VALU
+// operations per operand and tile-block.)
 //
 // The MFMA's A operand is the token tile and B the weight tile, so a lane's
 // column of the result is an output column and the stores coalesce.  Only
@@ -593,14 +580,7 @@ __global__ __launch_bounds__(256, 2) void gemm_t4_kernel(const GemmArgs a) {
                         0x4B400000, 0x4B400000, 0x4B400000, 0x4B400000};
   const f16x4 unbias_a = h ? f16x4{0, 0, 0, 0} : f16x4{(_Float16)-3072.0f, 0, 0, 0};
   const f16x4 unbias_b = h ? f16x4{0, 0, 0, 0} : f16x4{(_Float16)4096.0f, 0, 0, 0};
-  // bfi masks (bits taken from the slot dword; the rest from the patch):
-  // keep the high half on half 0 / everything on half 1; keep nothing on
-  // half 0 / everything on half 1.
-  const uint32_t keep_hi = h ? 0xFFFFFFFFu : 0xFFFF0000u;
-  const uint32_t keep_h1 = h ? 0xFFFFFFFFu : 0u;
-  const uint32_t sel_lo = h ? 0x0C0C0C0Cu : 0x0C0C0100u;  // bytes 0, 1 (scale in the low half)
-  const uint32_t sel_hi = h ? 0x0C0C0C0Cu : 0x0C0C0302u;  // bytes 2, 3 (scale in the high half)
-  auto bfi = [](uint32_t keep, uint32_t x, uint32_t y) { return (x & keep) | (y & ~keep); };
+  const PermLane pl(h);
 
   struct TileOut {
     f32x16 S;
@@ -614,44 +594,9 @@ __global__ __launch_bounds__(256, 2) void gemm_t4_kernel(const GemmArgs a) {
     for (int r = 0; r < 16; ++r) acc[Q][r] = fmaf(o.S[r], o.C[r], acc[Q][r]);
   };
 
-  // Raw operand of block B for the row at `row`: the half's 16-byte slot and
-  // the patch dwords from the slot after half 0's.
-  struct Raw {
-    i32x4 v;
-    uint32_t p0, p1;
-  };
-  auto read_raw = [&]<int B>(const uint8_t *row, Raw &r) {
-    constexpr int S0 = B == 0 ? 0 : B == 1 ? 2 : B == 2 ? 4 : 6;   // half 0's slot
-    constexpr int S1 = B == 3 ? 8 : S0 + 1;                         // half 1's slot
-    constexpr int SP = B == 3 ? 7 : S0 + 2;                         // patch slot
-    r.v = *reinterpret_cast<const i32x4 *>(row + 16 * (h ? S1 : S0));
-    if constexpr (B < 2) {
-      r.p0 = *reinterpret_cast<const uint32_t *>(row + 16 * SP);
-    } else {
-      const u32x2 pp = *reinterpret_cast<const u32x2 *>(row + 16 * SP);
-      r.p0 = pp.x;
-      r.p1 = pp.y;
-    }
-  };
-  auto prep = [&]<int B>(const Raw &r, uint32_t &scale) -> i32x4 {
-    uint32_t v0 = (uint32_t)r.v.x, v1 = (uint32_t)r.v.y;
-    if constexpr (B == 0) {           // {bfi(d0, d8), d1, d2, d3}
-      scale = __builtin_amdgcn_perm(0u, v0, sel_lo);
-      v0 = bfi(keep_hi, v0, r.p0);
-    } else if constexpr (B == 1) {    // {d16, d9, d10, d11}
-      scale = __builtin_amdgcn_perm(0u, v0, sel_hi);
-      v0 = bfi(keep_h1, v0, r.p0);
-    } else if constexpr (B == 2) {    // {e7, bfi(e0, e8), e1, e2}
-      scale = __builtin_amdgcn_perm(0u, v1, sel_lo);
-      v1 = bfi(keep_hi, v1, r.p1);
-      v0 = bfi(keep_h1, v0, r.p0);
-    } else {                          // {e11, e12, e9, e10}
-      scale = __builtin_amdgcn_perm(0u, v1, sel_hi);
-      v0 = bfi(keep_h1, v0, r.p0);
-      v1 = bfi(keep_h1, v1, r.p1);
-    }
-    return i32x4{(int)v0, (int)v1, r.v.z, r.v.w};
-  };
+  using Raw = PermRaw;
+  auto read_raw = [&]<int B>(const uint8_t *row, Raw &r) { perm_read<B>(row, h, r); };
+  auto prep = [&]<int B>(const Raw &r, uint32_t &scale) -> i32x4 { return perm_prep<B>(r, pl, scale); };
 
   issue(b_begin, 0);
   for (int s = 0; s < nstages; ++s) {
@@ -793,8 +738,11 @@ int gemm_auto_split(int64_t in_dim, int64_t out_dim, int64_t n_tok) {
   return (int)std::max<int64_t>(split, 1);
 }
 
+// Partials [split][n_tok][out_dim] after the workspace's counter bytes (which
+// this kernel leaves untouched, so the skinny kernel's counters stay zero).
 size_t gemm_workspace_bytes(int64_t out_dim, int64_t n_tok, int split) {
-  return split > 1 ? (size_t)split * (size_t)out_dim * (size_t)n_tok * sizeof(float) : 0;
+  return split > 1 ? kWsCounterBytes + (size_t)split * (size_t)out_dim * (size_t)n_tok * sizeof(float)
+                   : 0;
 }
 
 static bool use_lds_kernel(int64_t nb, int64_t n_tok) { return nb % lds::KB == 0 && n_tok > 64; }
@@ -809,8 +757,11 @@ static bool use_t4_kernel(int64_t nb, int64_t out_dim, int64_t n_tok) {
 
 hipError_t launch_gemm(float *out, int32_t *blocksums, const void *w, int64_t in_dim,
                        int64_t out_dim, const void *x_q, int64_t n_tok, int split,
-                       float *partials, hipStream_t s) {
+                       void *workspace, hipStream_t s) {
   const int64_t nb = in_dim / kBlockElems;
+  float *partials =
+      workspace ? reinterpret_cast<float *>(static_cast<uint8_t *>(workspace) + kWsCounterBytes)
+                : nullptr;
   // The direct-to-LDS kernels copy 16-byte chunks; they take operands whose
   // bases are 16-byte aligned (torch allocations are), the register-staged
   // kernel the rest (it needs 4 bytes).

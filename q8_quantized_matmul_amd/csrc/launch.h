@@ -88,15 +88,22 @@ hipError_t launch_moe(float *out, int32_t *blocksums, const void *const *expert_
                       int32_t x_rows, int64_t n_tok, int32_t *workspace, bool fast,
                       hipStream_t s, int32_t *invalid_out = nullptr);
 
-// skinny.hip: matrix-core matmul for up to kSkinnyMaxTokens tokens, weights
-// streamed into registers, split-K through caller partials.
+// Caller workspace of q8_0_matmul split-K plans: arrival counters of the
+// skinny kernel's in-launch reduction (zero between calls) in the first
+// kWsCounterBytes, partial sums after them.
+constexpr size_t kWsCounterBytes = 4096;
+
+// skinny.hip: matrix-core matmul for up to kSkinnyMaxTokens tokens, token and
+// weight rows staged in LDS, split-K reduced inside the launch.
 constexpr int64_t kSkinnyMaxTokens = 64;
 bool skinny_supported(int64_t in_dim, int64_t n_tok);
-int skinny_auto_split(int64_t in_dim, int64_t out_dim);
+int skinny_auto_split(int64_t in_dim, int64_t out_dim, int64_t n_tok);
+// A split needs one counter per 32-row output tile.
+bool skinny_split_ok(int64_t out_dim, int split);
 size_t skinny_workspace_bytes(int64_t out_dim, int64_t n_tok, int split);
 hipError_t launch_skinny(float *out, int32_t *blocksums, const void *w, int64_t in_dim,
                          int64_t out_dim, const void *x_q, int64_t n_tok, int split,
-                         float *partials, hipStream_t s);
+                         void *workspace, hipStream_t s);
 
 // gemm.hip: int8 MFMA GEMM with per-block scales.
 bool gemm_supported(int64_t in_dim);
@@ -104,7 +111,7 @@ int gemm_auto_split(int64_t in_dim, int64_t out_dim, int64_t n_tok);
 size_t gemm_workspace_bytes(int64_t out_dim, int64_t n_tok, int split);
 hipError_t launch_gemm(float *out, int32_t *blocksums, const void *w, int64_t in_dim,
                        int64_t out_dim, const void *x_q, int64_t n_tok, int split,
-                       float *partials, hipStream_t s);
+                       void *workspace, hipStream_t s);
 // out[i] = sum over s = 0..n_split-1, in order, of partials[s * n + i].
 hipError_t launch_splitk_reduce(float *out, const float *partials, int64_t n, int n_split,
                                 hipStream_t s);

@@ -274,57 +274,92 @@ __device__ __forceinline__ void quantize_pair4(const float4 (&v)[4], int j, uint
   }
 }
 
-// Staged rows in LDS (8-byte-aligned rows of 4-block, 136-byte slices).
-// LDS words of one operand of block B of a slice: a 24-byte (16 for B = 3)
-// 8-byte-aligned window holding the 16 quant bytes of half h, and for B = 3
-// the block's scale, which lies before that window.  With SPLIT_TAIL the
-// slice's bytes 128..135 sit 8 bytes further on (at 136..143; the GEMM's
-// 144-byte pitch), which moves block 3's upper half.
-struct T4Raw {
-  uint32_t w[6];
-  uint32_t sc;
+// Staged rows of the matrix-core kernels: a row's 4 blocks (a 136-byte
+// slice, dwords d0..d33) as nine 16-byte slots at a 144-byte LDS pitch --
+// slice dwords 0..3, 4..7, ..., 28..31 and 30..33.
+//
+// A block dot sums qw_k * qx_k over k, so any permutation of k applied to
+// both operands gives the same S_b.  With the slice's pairs d0..d16 and
+// e0..e16 = d17..d33, a pair being
+//   [sA | qA0 qA1] [qA2 .. qA29] [qA30 qA31 | sB] [qB0 .. qB31],
+// the two 16-byte halves of each block's operand are
+//   block 0: {bfi(d0, d8), d1, d2, d3}   | {d4, d5, d6, d7}     slots 0 | 1
+//   block 1: {d16, d9, d10, d11}         | {d12, d13, d14, d15} slots 2 | 3
+//   block 2: {e7, bfi(e0, e8), e1, e2}   | {e3, e4, e5, e6}     slots 4 | 5
+//   block 3: {e11, e12, e9, e10}         | {e13, e14, e15, e16} slots 6 | 8
+// where bfi(a, b) takes a's high half (the block's first two quants) and b's
+// low half (its last two).  So every operand is one aligned 16-byte LDS read
+// (consecutive rows sit 9 slots apart, which keeps those reads free of bank
+// conflicts) plus, for half 0, one or two dwords of the next slot patched in
+// with v_bfi; half 1 reads the same patch address and keeps its own dwords.
+// The scales come out of the same reads: block 0's in d0's low half, block
+// 1's in d8's high half, block 2's in e0's low half, block 3's in e8's high
+// half.
+constexpr int kPermPitch = 144;  // LDS bytes per staged 4-block row
+constexpr int kPermSlots = kPermPitch / 16;
+
+// Raw operand of block B: the half's 16-byte slot and the patch dwords from
+// the slot after half 0's.
+struct PermRaw {
+  i32x4 v;
+  uint32_t p0, p1;
 };
 
-template <int B, bool SPLIT_TAIL = false>
-__device__ __forceinline__ void t4_read(const uint8_t *row, int h, T4Raw &r) {
-  constexpr int M = (2 * B + 2) % 8;  // quant start modulo 8 (rows are 8-aligned)
+template <int B>
+__device__ __forceinline__ void perm_read(const uint8_t *row, int h, PermRaw &r) {
   typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-  const u32x2 *q = reinterpret_cast<const u32x2 *>(row + B * kBlockBytes + 2 + 16 * h - M +
-                                                   (SPLIT_TAIL && B == 3 ? 8 * h : 0));
-  const u32x2 a = q[0], b = q[1];
-  r.w[0] = a.x;
-  r.w[1] = a.y;
-  r.w[2] = b.x;
-  r.w[3] = b.y;
-  if constexpr (M != 0) {
-    const u32x2 c = q[2];
-    r.w[4] = c.x;
-    r.w[5] = c.y;
+  constexpr int S0 = B == 0 ? 0 : B == 1 ? 2 : B == 2 ? 4 : 6;  // half 0's slot
+  constexpr int S1 = B == 3 ? 8 : S0 + 1;                        // half 1's slot
+  constexpr int SP = B == 3 ? 7 : S0 + 2;                        // patch slot
+  r.v = *reinterpret_cast<const i32x4 *>(row + 16 * (h ? S1 : S0));
+  if constexpr (B < 2) {
+    r.p0 = *reinterpret_cast<const uint32_t *>(row + 16 * SP);
   } else {
-    r.sc = *reinterpret_cast<const uint16_t *>(row + B * kBlockBytes);
+    const u32x2 pp = *reinterpret_cast<const u32x2 *>(row + 16 * SP);
+    r.p0 = pp.x;
+    r.p1 = pp.y;
   }
 }
 
-// The 16 quant bytes realigned for the MFMA, and the scale bits for half 0
-// (zero for half 1, which feeds the unused K slots of the scale MFMA).
+// Per-lane constants of perm_prep: bfi masks (bits taken from the slot
+// dword, the rest from the patch) and the byte selects of the scale.
+struct PermLane {
+  uint32_t keep_hi;  // the high half on half 0, everything on half 1
+  uint32_t keep_h1;  // nothing on half 0, everything on half 1
+  uint32_t sel_lo;   // scale bytes 0, 1 on half 0 (zero on half 1)
+  uint32_t sel_hi;   // scale bytes 2, 3 on half 0 (zero on half 1)
+  __device__ __forceinline__ explicit PermLane(int h)
+      : keep_hi(h ? 0xFFFFFFFFu : 0xFFFF0000u),
+        keep_h1(h ? 0xFFFFFFFFu : 0u),
+        sel_lo(h ? 0x0C0C0C0Cu : 0x0C0C0100u),
+        sel_hi(h ? 0x0C0C0C0Cu : 0x0C0C0302u) {}
+};
+
+__device__ __forceinline__ uint32_t perm_bfi(uint32_t keep, uint32_t x, uint32_t y) {
+  return (x & keep) | (y & ~keep);
+}
+
+// The operand of block B in the permuted order, and the scale bits for half
+// 0 (zero for half 1, which feeds the unused K slots of the scale MFMA).
 template <int B>
-__device__ __forceinline__ i32x4 t4_prep(const T4Raw &r, int h, uint32_t &scale) {
-  constexpr int M = (2 * B + 2) % 8;
-  const uint32_t *w = r.w;
-  if constexpr (M == 0) {
-    scale = h ? 0u : r.sc;
-    return i32x4{(int)w[0], (int)w[1], (int)w[2], (int)w[3]};
-  } else if constexpr (M == 4) {
-    scale = h ? 0u : (w[0] >> 16);
-    return i32x4{(int)w[1], (int)w[2], (int)w[3], (int)w[4]};
-  } else {
-    constexpr int K = M == 2 ? 0 : 1;
-    scale = h ? 0u : (M == 2 ? (w[0] & 0xFFFFu) : (w[1] & 0xFFFFu));
-    return i32x4{(int)__builtin_amdgcn_alignbyte(w[K + 1], w[K], 2),
-                 (int)__builtin_amdgcn_alignbyte(w[K + 2], w[K + 1], 2),
-                 (int)__builtin_amdgcn_alignbyte(w[K + 3], w[K + 2], 2),
-                 (int)__builtin_amdgcn_alignbyte(w[K + 4], w[K + 3], 2)};
+__device__ __forceinline__ i32x4 perm_prep(const PermRaw &r, const PermLane &pl, uint32_t &scale) {
+  uint32_t v0 = (uint32_t)r.v.x, v1 = (uint32_t)r.v.y;
+  if constexpr (B == 0) {           // {bfi(d0, d8), d1, d2, d3}
+    scale = __builtin_amdgcn_perm(0u, v0, pl.sel_lo);
+    v0 = perm_bfi(pl.keep_hi, v0, r.p0);
+  } else if constexpr (B == 1) {    // {d16, d9, d10, d11}
+    scale = __builtin_amdgcn_perm(0u, v0, pl.sel_hi);
+    v0 = perm_bfi(pl.keep_h1, v0, r.p0);
+  } else if constexpr (B == 2) {    // {e7, bfi(e0, e8), e1, e2}
+    scale = __builtin_amdgcn_perm(0u, v1, pl.sel_lo);
+    v1 = perm_bfi(pl.keep_hi, v1, r.p1);
+    v0 = perm_bfi(pl.keep_h1, v0, r.p0);
+  } else {                          // {e11, e12, e9, e10}
+    scale = __builtin_amdgcn_perm(0u, v1, pl.sel_hi);
+    v0 = perm_bfi(pl.keep_h1, v0, r.p0);
+    v1 = perm_bfi(pl.keep_h1, v1, r.p1);
   }
+  return i32x4{(int)v0, (int)v1, r.v.z, r.v.w};
 }
 
 // Direct global->LDS dword copy through a buffer resource: a 32-bit lane

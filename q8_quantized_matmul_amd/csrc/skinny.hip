@@ -8,21 +8,28 @@
 // narrow batches ("Part 6: GPU 加速", sections 4c and 4s).  Tokens are the
 // MFMA's M dimension (one or two 32-token tiles), output rows its N dimension.
 //
-//   * The workgroup's K range goes through LDS in stages of 4 block pairs
-//     (272 bytes of every token and weight row), double-buffered, filled by
-//     direct global->LDS copies in which consecutive lanes read consecutive
-//     bytes of a row (16-byte copies where rows are whole 16-byte chunks,
-//     dword copies otherwise).  Reading the MFMA operand layout straight from
-//     memory instead (each lane its own row) left the kernel bound by
-//     address processing, 1.2-2x slower depending on the split.
-//   * Wave w takes pair w of each stage.  One v_mfma_i32_32x32x32_i8 per
-//     (token tile, block) gives the exact S_b of the 32x32 tile; one
-//     v_mfma_f32_32x32x8_f16 with only K slot 0 populated gives the matching
-//     d_w * d_x outer product, exactly; the epilogue is acc += float(S_b) * scale.
-//   * The 4 waves are summed through LDS in wave order; K ranges of different
-//     workgroups (split-K) go to partials that the ordered reduce kernel sums.
-//     Every sum has a fixed order: results are deterministic.
+//   * The workgroup's K range is cut into steps of 2 block pairs (a 136-byte
+//     slice of every row).  Eight waves, two per SIMD: wave w takes token
+//     tile m = w / KQ and steps w % KQ, w % KQ + KQ, ... (KQ = 8 / MT waves
+//     per token tile), and streams them through a private LDS region with
+//     its own direct global->LDS copies of the 32 token rows of its tile and
+//     the 32 weight rows, staged at a 144-byte pitch with K permuted for
+//     aligned 16-byte operand reads (as in the tiled GEMM; q8_device.h
+//     perm_read).  Consecutive lanes copy consecutive bytes of a row: 16-byte
+//     copies where rows are whole 16-byte chunks, dword copies otherwise.  A
+//     wave waits for its own copies only: the K loop has no workgroup
+//     barrier, so the waves overlap one another's loads and matrix work.
+//   * Per block, one v_mfma_i32_32x32x32_i8 gives the exact S_b of the 32x32
+//     tile (converted to fp32 on the matrix core, as in the tiled GEMM) and
+//     one v_mfma_f32_32x32x8_f16 with only K slot 0 populated the matching
+//     d_w * d_x outer product, exactly; the epilogue is
+//     acc += float(S_b) * scale.
+//   * The waves of a token tile are summed through LDS in wave order.  With split-K,
+//     each workgroup leaves its sums in caller workspace and the last
+//     workgroup of an output tile to arrive adds them in split order.  Every
+//     sum has a fixed order: results are deterministic.
 #include <algorithm>
+#include <utility>
 
 #include "launch.h"
 #include "q8_device.h"
@@ -31,7 +38,9 @@ namespace q8 {
 namespace {
 
 struct SkinnyArgs {
-  float *out;            // [n_tok][out_dim], or partials [n_split][n_tok][out_dim]
+  float *out;            // [n_tok][out_dim]
+  float *partials;       // split-K: [n_split][tiles][MT][16][64 lanes], else null
+  uint32_t *arrivals;    // split-K: one arrival counter per output tile, else null
   int32_t *blocksums;    // debug: S_b [n_tok][out_dim][2 * n_pairs], or null
   const uint8_t *w;      // [out_dim][row_bytes]
   const uint8_t *x_q;    // [n_tok][row_bytes]
@@ -42,264 +51,390 @@ struct SkinnyArgs {
   int32_t pairs_per_split;
 };
 
-// A stage holds kStagePairs block pairs (one per wave) of every row of the
-// workgroup: 32 * MT token rows, then 32 weight rows, 272 bytes each.
-constexpr int kStagePairs = 4;
-constexpr int kStageRowBytes = kStagePairs * kPairBytes;  // 272
-constexpr int kStageRowDwords = kStageRowBytes / 4;       // 68
-constexpr int kCopyPeriod = 17;                           // 17 copies of 64 dwords = 16 rows
-static_assert(kCopyPeriod * 64 == 16 * kStageRowDwords, "copy pattern period");
+constexpr int kWaves = 8;
+constexpr int kStepPairs = 2;                          // pairs of a row per step
+constexpr int kSliceBytes = kStepPairs * kPairBytes;   // 136 bytes of a row per step
+constexpr int kPitch = kPermPitch;                     // 144 LDS bytes per staged row
+constexpr int kPitchDwords = kPitch / 4;               // 36
+constexpr int kGroupCopies = 9;                        // dword copies of 16 staged rows
+static_assert(kGroupCopies * 64 == 16 * kPitchDwords, "copy pattern period");
 
-template <int MT>
-struct SkinnyStage {
-  static constexpr int XROWS = 32 * MT;
-  static constexpr int ROWS = XROWS + 32;
-  static constexpr int BYTES = ROWS * kStageRowBytes;
-};
+// One wave's staged step: the 32 token rows of its tile, then the 32 weight
+// rows, 144 LDS bytes each.
+constexpr int kStepRows = 64;
+constexpr int kStepBytes = kStepRows * kPitch;  // 9216
 
-// One block of the wave's pair: operands from the staged rows, then per
-// token tile one int8 MFMA (S_b) and one scale MFMA (d_x * d_w), added as
-// acc += float(S_b) * scale.  STORE_S (debug) also writes S_b of block `blk`
-// for output column `o`.
-template <int B, int MT, bool STORE_S>
-__device__ __forceinline__ void skinny_block(const uint8_t *const (&xrow)[MT], const uint8_t *wrow,
-                                             int h, float (&acc)[MT][16], const SkinnyArgs &a,
-                                             int64_t blk, int64_t o) {
-  typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-  const i32x16 izero = {};
-  const f32x16 fzero = {};
-  T4Raw rw;
-  t4_read<B>(wrow, h, rw);
-  uint32_t sw;
-  const i32x4 Bop = t4_prep<B>(rw, h, sw);
-  const f16x4 SB = __builtin_bit_cast(f16x4, u32x2{sw, 0u});
-#pragma unroll
-  for (int m = 0; m < MT; ++m) {
-    T4Raw rx;
-    t4_read<B>(xrow[m], h, rx);
-    uint32_t sx;
-    const i32x4 Aop = t4_prep<B>(rx, h, sx);
-    const f16x4 SA = __builtin_bit_cast(f16x4, u32x2{sx, 0u});
-    const i32x16 S = __builtin_amdgcn_mfma_i32_32x32x32_i8(Aop, Bop, izero, 0, 0, 0);
-    const f32x16 C = __builtin_amdgcn_mfma_f32_32x32x8f16(SA, SB, fzero, 0, 0, 0);
-#pragma unroll
-    for (int r = 0; r < 16; ++r) acc[m][r] = fmaf((float)S[r], C[r], acc[m][r]);
-    if constexpr (STORE_S) {
-      // Element r: token 32 m + 8 (r / 4) + 4 h + r % 4.
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int64_t t = 32 * m + 8 * (r >> 2) + 4 * h + (r & 3);
-        if (t < a.n_tok && o < a.out_dim) a.blocksums[(t * a.out_dim + o) * 2 * a.n_pairs + blk] = S[r];
-      }
-    }
-  }
+// Byte of a row's slice that 16-byte slot j (0..8) of its staged row holds:
+// slots 0..7 the first 128 bytes, slot 8 bytes 120..135.
+__device__ __forceinline__ int slot_byte(int j) { return j < kPermSlots - 1 ? 16 * j : kSliceBytes - 16; }
+
+// s_waitcnt on the vector-memory counter alone (expcnt and lgkmcnt left at
+// their maxima): at most N of this wave's vector memory operations remain.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "the counter holds 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-// Stage copies, dword granularity (any in_dim % 64 == 0): waves 0 .. MT-1
-// move token rows 32 w + r, waves 2 and 3 weight rows o_tile + 16 (w - 2) + r
-// (stage rows XROWS + 16 (w - 2) + r).  Lane l of copy k moves flat dword
-// 64 k + l of a group of 16 rows.  Each group of 16 rows is read through a
-// buffer resource based at that group's first row plus the stage's byte
-// offset, whose range ends at the end of the wave's last valid row, and the
-// lane's whole offset is its 32-bit voffset: the hardware range check covers
-// voffset only (not the scalar offset), so everything a copy adds to the base
-// has to be in voffset or in the base.  Rows past the matrix, and the bytes
-// past the end of the last valid row (a short last stage), then lie outside
-// the range and read as zero; what lands in LDS for them feeds only outputs
-// that are not stored, or pairs past the split that no wave multiplies.
-template <int MT>
+// Step copies, dword granularity (any in_dim % 64 == 0): the step's rows in
+// groups of 16 (token rows 32 m + 16 g for g = 0, 1, then weight rows
+// o_tile + 16 (g - 2)), 9 copies per group: lane l of copy k moves staged
+// dword 64 k + l of the group (row r = that / 36 at LDS byte 4 (that % 36):
+// slice dwords 0..31, then 30..33).  Each group is read through a buffer
+// resource based at its first row plus the step's byte offset in the row,
+// whose range ends at the end of the group's last valid row, and the lane's
+// whole offset is its 32-bit voffset: the hardware range check covers
+// voffset only (not the scalar offset), so everything a copy adds to the
+// base has to be in voffset or in the base.  Rows past the matrix, and the
+// bytes past the end of the last valid row (an odd pair count's last step),
+// then lie outside the range and read as zero; what lands in LDS for them
+// feeds only outputs that are not stored, or a pair past the split that
+// runs with zero scales.
+template <int R>
 struct DwordCopies {
-  static constexpr int XROWS = 32 * MT;
-  const uint8_t *gbase = nullptr;
-  int64_t valid_bytes = 0;  // bytes of the wave's valid rows, from gbase
-  uint32_t off[kCopyPeriod];
-  int grp_rows = 0, first = 0, p_begin;
-  int64_t rows16;
+  static constexpr int NBUF = R;
+  static constexpr int GROUPS = kStepRows / 16;
+  static constexpr int PER_STEP = GROUPS * kGroupCopies;  // this wave's copies per step
+  const uint8_t *base[GROUPS];
+  int64_t valid_bytes[GROUPS];  // bytes of the group's valid rows, from base
+  uint32_t off[kGroupCopies];
 
-  __device__ __forceinline__ DwordCopies(const SkinnyArgs &a, int wave, int lane, int64_t o_tile,
-                                         int pb)
-      : p_begin(pb) {
-    int64_t valid = 0;
-    if (wave < MT) {
-      grp_rows = 32;
-      first = 32 * wave;
-      gbase = a.x_q + (int64_t)first * a.row_bytes;
-      valid = a.n_tok - first;
-    } else if (wave >= 2) {
-      grp_rows = 16;
-      first = XROWS + 16 * (wave - 2);
-      const int64_t o0 = o_tile + 16 * (wave - 2);
-      gbase = a.w + o0 * a.row_bytes;
-      valid = a.out_dim - o0;
-    }
-    valid = valid < 0 ? 0 : (valid > grp_rows ? grp_rows : valid);
-    valid_bytes = valid * a.row_bytes;
+  __device__ __forceinline__ DwordCopies(const SkinnyArgs &a, int lane, int m, int64_t o_tile) {
 #pragma unroll
-    for (int k = 0; k < kCopyPeriod; ++k) {
-      const int f = 64 * k + lane;
-      const int r = f / kStageRowDwords;
-      off[k] = (uint32_t)(r * (int)a.row_bytes + 4 * (f - r * kStageRowDwords));
+    for (int g = 0; g < GROUPS; ++g) {
+      int64_t valid;
+      if (g < 2) {
+        base[g] = a.x_q + (int64_t)(32 * m + 16 * g) * a.row_bytes;
+        valid = a.n_tok - (32 * m + 16 * g);
+      } else {
+        const int64_t o0 = o_tile + 16 * (g - 2);
+        base[g] = a.w + o0 * a.row_bytes;
+        valid = a.out_dim - o0;
+      }
+      valid = valid < 0 ? 0 : (valid > 16 ? 16 : valid);
+      valid_bytes[g] = valid * a.row_bytes;
     }
-    rows16 = 16 * a.row_bytes;
+#pragma unroll
+    for (int k = 0; k < kGroupCopies; ++k) {
+      const int f = 64 * k + lane;
+      const int r = f / kPitchDwords;
+      const int d = f - r * kPitchDwords;
+      off[k] = (uint32_t)(r * (int)a.row_bytes + (d < 32 ? 4 * d : kSliceBytes - 16 + 4 * (d - 32)));
+    }
   }
 
-  __device__ __forceinline__ void issue(uint8_t *stage, int s) const {
-    if (grp_rows == 0) return;
-    const uint32_t lds = (uint32_t)reinterpret_cast<uintptr_t>(stage + first * kStageRowBytes);
-    const int64_t sb = (int64_t)(p_begin + s * kStagePairs) * kPairBytes;
+  // Copies of the step whose first pair is pair0 into the staged rows at lds.
+  __device__ __forceinline__ void issue(uint8_t *lds_step, int pair0) const {
+    const int64_t start = (int64_t)pair0 * kPairBytes;
 #pragma unroll
-    for (int g = 0; g < 2; ++g) {
-      if (g == 1 && grp_rows == 16) break;
-      // Group g: rows 16 g .. 16 g + 15 of the wave, from byte sb of each row.
-      const int64_t start = sb + g * rows16;
-      const int64_t left = valid_bytes - start;
-      const rsrc_t rsrc = make_rsrc(gbase + start, (uint32_t)(left > 0 ? left : 0));
+    for (int g = 0; g < GROUPS; ++g) {
+      const int64_t left = valid_bytes[g] - start;
+      const rsrc_t rsrc = make_rsrc(base[g] + start, (uint32_t)(left > 0 ? left : 0));
+      const uint32_t lds = (uint32_t)reinterpret_cast<uintptr_t>(lds_step + 16 * g * kPitch);
 #pragma unroll
-      for (int k = 0; k < kCopyPeriod; ++k) {
+      for (int k = 0; k < kGroupCopies; ++k) {
         buffer_load_lds_raw(rsrc,
                             reinterpret_cast<__attribute__((address_space(3))) uint32_t *>(
-                                (uintptr_t)(lds + 256 * (k + kCopyPeriod * g))),
+                                (uintptr_t)(lds + 256 * k)),
                             4, (int)off[k], 0, 0, 0);
       }
     }
   }
 };
 
-// Stage copies, 16-byte granularity (in_dim % 256 == 0, so every row and
-// every stage is whole 16-byte chunks, and 16-byte-aligned operands): the
-// stage's ROWS * 17 chunks, x rows then weight rows, go out as 64-chunk wave
-// copies, copy i taken by wave i % 4.  Rows past the matrix re-read its last
-// row (their outputs are not stored).
-template <int MT>
+// Step copies, 16-byte granularity (in_dim % 256 == 0 and 16-byte-aligned
+// operands, so every step starts on an 8-byte boundary of a row): the step's
+// 64 * 9 slots (row, then slot) go out as 9 copies of 64.  Rows past the
+// matrix re-read its last row (their outputs are not stored).
+template <int R>
 struct ChunkCopies {
-  static constexpr int XROWS = 32 * MT;
-  static constexpr int CHUNKS = (XROWS + 32) * (kStageRowBytes / 16);
-  static constexpr int INSTS = (CHUNKS + 63) / 64;
-  static constexpr int PER_WAVE = (INSTS + 3) / 4;
-  const uint8_t *src[PER_WAVE];
-  int wave, lane, p_begin;
+  static constexpr int NBUF = R;
+  static constexpr int PER_STEP = kStepRows * kPermSlots / 64;  // this wave's copies per step
+  static_assert(PER_STEP * 64 == kStepRows * kPermSlots, "whole copies");
+  const uint8_t *src[PER_STEP];  // row base + slot byte
 
-  __device__ __forceinline__ ChunkCopies(const SkinnyArgs &a, int w, int l, int64_t o_tile, int pb)
-      : wave(w), lane(l), p_begin(pb) {
+  __device__ __forceinline__ ChunkCopies(const SkinnyArgs &a, int lane, int m, int64_t o_tile) {
 #pragma unroll
-    for (int j = 0; j < PER_WAVE; ++j) {
-      const int c = min(64 * (wave + 4 * j) + lane, CHUNKS - 1);
-      const int row = c / (kStageRowBytes / 16);
-      const int part = c - row * (kStageRowBytes / 16);
-      const int64_t g = row < XROWS ? min<int64_t>(row, a.n_tok - 1)
-                                    : min<int64_t>(o_tile + row - XROWS, a.out_dim - 1);
-      src[j] = (row < XROWS ? a.x_q : a.w) + g * a.row_bytes + 16 * part;
+    for (int k = 0; k < PER_STEP; ++k) {
+      const int c = 64 * k + lane;
+      const int row = c / kPermSlots;
+      const int slot = c - row * kPermSlots;
+      const uint8_t *rowp = row < 32 ? a.x_q + min<int64_t>(32 * m + row, a.n_tok - 1) * a.row_bytes
+                                     : a.w + min<int64_t>(o_tile + row - 32, a.out_dim - 1) * a.row_bytes;
+      src[k] = rowp + slot_byte(slot);
     }
   }
 
-  __device__ __forceinline__ void issue(uint8_t *stage, int s) const {
-    const int64_t sb = (int64_t)(p_begin + s * kStagePairs) * kPairBytes;
+  __device__ __forceinline__ void issue(uint8_t *lds_step, int pair0) const {
+    const int64_t start = (int64_t)pair0 * kPairBytes;
 #pragma unroll
-    for (int j = 0; j < PER_WAVE; ++j) {
-      const int inst = wave + 4 * j;
-      if (inst < INSTS && 64 * inst + lane < CHUNKS)
-        __builtin_amdgcn_global_load_lds(src[j] + sb, stage + 1024 * inst, 16, 0, 0);
-    }
+    for (int k = 0; k < PER_STEP; ++k)
+      __builtin_amdgcn_global_load_lds(
+          src[k] + start,
+          reinterpret_cast<__attribute__((address_space(3))) void *>((uintptr_t)(lds_step + 1024 * k)),
+          16, 0, 0);
   }
 };
 
+// Wait until this wave's oldest in-flight step has landed, with `behind`
+// later steps (PW copies each) still allowed in flight (behind < NBUF).
+template <int PW, int NBUF>
+__device__ __forceinline__ void wait_steps(int behind) {
+  static_assert(NBUF == 1 || NBUF == 2, "one or two steps in flight");
+  if constexpr (NBUF == 2) {
+    if (behind > 0) {
+      wait_vmcnt<PW>();
+      return;
+    }
+  }
+  wait_vmcnt<0>();
+}
+
+// The four blocks of one staged step.  Per block: the int8 MFMA accumulates
+// S_b onto the constant 0x4B400000 (1.5 * 2^23 as fp32 bits; |S_b| < 2^22,
+// so the int32 sum read as fp32 is exactly 1.5 * 2^23 + S_b), an f16 MFMA
+// adds the exact product (-3072) * 4096 = -1.5 * 2^23 in K slot 0 (so the
+// tile holds float(S_b) exactly, converted on the matrix core), and another
+// gives the d_x * d_w outer product; the VALU is left with one fma per
+// output: acc += float(S_b) * scale, in block order.  The next block's
+// operands are read before this block's matrix work.  Blocks of a pair at or
+// past `pair_end` (an odd pair count's last step) run with zero scales.
+// STORE_S (debug) also writes S_b of the valid blocks for output column o,
+// tokens of tile m.
+template <bool STORE_S>
+__device__ __forceinline__ void skinny_step(const uint8_t *st, int lrow, int h, const PermLane &pl,
+                                            float (&acc)[16], const SkinnyArgs &a, int pair0,
+                                            int pair_end, int m, int64_t o) {
+  typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+  const f32x16 fzero = {};
+  const i32x16 ibias = {0x4B400000, 0x4B400000, 0x4B400000, 0x4B400000, 0x4B400000, 0x4B400000,
+                        0x4B400000, 0x4B400000, 0x4B400000, 0x4B400000, 0x4B400000, 0x4B400000,
+                        0x4B400000, 0x4B400000, 0x4B400000, 0x4B400000};
+  const f16x4 unbias_a = h ? f16x4{0, 0, 0, 0} : f16x4{(_Float16)-3072.0f, 0, 0, 0};
+  const f16x4 unbias_b = h ? f16x4{0, 0, 0, 0} : f16x4{(_Float16)4096.0f, 0, 0, 0};
+  const uint8_t *xrow = st + lrow * kPitch;
+  const uint8_t *wrow = st + (32 + lrow) * kPitch;
+  const bool second = pair0 + 1 < pair_end;  // blocks 2, 3 are a valid pair
+
+  PermRaw rw[2], rx[2];
+  perm_read<0>(wrow, h, rw[0]);
+  perm_read<0>(xrow, h, rx[0]);
+  [&]<int... B>(std::integer_sequence<int, B...>) {
+    (([&] {
+       constexpr int cur = B & 1, nxt = cur ^ 1;
+       uint32_t sw, sx;
+       const i32x4 W = perm_prep<B>(rw[cur], pl, sw);
+       const i32x4 X = perm_prep<B>(rx[cur], pl, sx);
+       if constexpr (B + 1 < 4) {
+         perm_read<B + 1>(wrow, h, rw[nxt]);
+         perm_read<B + 1>(xrow, h, rx[nxt]);
+       }
+       if constexpr (B >= 2) {
+         if (!second) sw = sx = 0u;
+       }
+       const i32x16 biased = __builtin_amdgcn_mfma_i32_32x32x32_i8(X, W, ibias, 0, 0, 0);
+       const f32x16 S = __builtin_amdgcn_mfma_f32_32x32x8f16(unbias_a, unbias_b,
+                                                            __builtin_bit_cast(f32x16, biased), 0, 0, 0);
+       const f32x16 C = __builtin_amdgcn_mfma_f32_32x32x8f16(
+           __builtin_bit_cast(f16x4, u32x2{sx, 0u}), __builtin_bit_cast(f16x4, u32x2{sw, 0u}),
+           fzero, 0, 0, 0);
+#pragma unroll
+       for (int r = 0; r < 16; ++r) acc[r] = fmaf(S[r], C[r], acc[r]);
+       if constexpr (STORE_S) {
+         // Element r: token 32 m + 8 (r / 4) + 4 h + r % 4.
+         const int64_t blk = 2 * (int64_t)pair0 + B;
+         if (B < 2 || second) {
+#pragma unroll
+           for (int r = 0; r < 16; ++r) {
+             const int64_t t = 32 * m + 8 * (r >> 2) + 4 * h + (r & 3);
+             if (t < a.n_tok && o < a.out_dim)
+               a.blocksums[(t * a.out_dim + o) * 2 * a.n_pairs + blk] = (int32_t)S[r];
+           }
+         }
+       }
+     }()), ...);
+  }(std::make_integer_sequence<int, 4>{});
+}
+
 // MT token tiles of 32.  Grid: x = 32-row output tiles, y = K splits.
 template <int MT, class COPY, bool STORE_S>
-__global__ __launch_bounds__(256) void skinny_kernel(const SkinnyArgs a) {
-  using St = SkinnyStage<MT>;
-  __shared__ __attribute__((aligned(16))) uint8_t ring[2 * St::BYTES];
-  static_assert(4 * MT * 16 * 64 * sizeof(float) <= sizeof(ring), "reduction fits the ring");
+__global__ __launch_bounds__(512) void skinny_kernel(const SkinnyArgs a) {
+  constexpr int NBUF = COPY::NBUF;
+  constexpr int KQ = kWaves / MT;  // waves per token tile
+  constexpr int PER = 2 * MT;      // values of the workgroup's tile set a wave finishes
+  __shared__ __attribute__((aligned(16))) uint8_t ring[kWaves * NBUF * kStepBytes];
+  __shared__ uint32_t arrived_before;
+  static_assert(kWaves * 16 * 64 * sizeof(float) <= sizeof(ring), "reduction fits the ring");
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int m = wave / KQ;   // token tile
+  const int kq = wave % KQ;  // first step of this wave
   const int lrow = lane & 31;
   const int h = lane >> 5;
+  const PermLane pl(h);
   const int64_t o_tile = (int64_t)blockIdx.x * 32;
+  const int64_t o = o_tile + lrow;
   const int p_begin = blockIdx.y * a.pairs_per_split;
   const int p_end = min(p_begin + a.pairs_per_split, a.n_pairs);
-  const int nstages = (p_end - p_begin + kStagePairs - 1) / kStagePairs;
+  const int nsteps = (p_end - p_begin + kStepPairs - 1) / kStepPairs;
+  const int mine = nsteps > kq ? (nsteps - kq + KQ - 1) / KQ : 0;  // steps of this wave
 
-  COPY copies(a, wave, lane, o_tile, p_begin);
-  auto issue = [&](int st, int buf) { copies.issue(ring + buf * St::BYTES, st); };
+  COPY copies(a, lane, m, o_tile);
+  uint8_t *const region = ring + wave * NBUF * kStepBytes;
+  auto pair_of = [&](int i) { return p_begin + kStepPairs * (kq + KQ * i); };
 
-  float acc[MT][16];
+  float acc[16];
 #pragma unroll
-  for (int m = 0; m < MT; ++m)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) acc[m][r] = 0.0f;
+  for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
 
-  issue(0, 0);
-  for (int s = 0; s < nstages; ++s) {
-    __builtin_amdgcn_s_waitcnt(0);  // this wave's copies of stage s have landed
-    __syncthreads();                // ... and every wave's; buffer (s+1)&1 is free
-    if (s + 1 < nstages) issue(s + 1, (s + 1) & 1);
-    // Wave w takes pair w of the stage (blocks 2w, 2w+1), which starts 68 w
-    // bytes into each staged row: in the 136-byte slice w / 2, at block 0 or 2.
-    const int pair = p_begin + s * kStagePairs + wave;
-    if (pair < p_end) {
-      const uint8_t *st = ring + (s & 1) * St::BYTES + 136 * (wave >> 1);
-      const uint8_t *xrow[MT];
-#pragma unroll
-      for (int m = 0; m < MT; ++m) xrow[m] = st + (32 * m + lrow) * kStageRowBytes;
-      const uint8_t *wrow = st + (St::XROWS + lrow) * kStageRowBytes;
-      const int64_t blk = 2 * (int64_t)pair;  // the pair's first block
-      const int64_t o = o_tile + lrow;
-      if (wave & 1) {
-        skinny_block<2, MT, STORE_S>(xrow, wrow, h, acc, a, blk, o);
-        skinny_block<3, MT, STORE_S>(xrow, wrow, h, acc, a, blk + 1, o);
-      } else {
-        skinny_block<0, MT, STORE_S>(xrow, wrow, h, acc, a, blk, o);
-        skinny_block<1, MT, STORE_S>(xrow, wrow, h, acc, a, blk + 1, o);
-      }
+  // Step i of this wave lives in buffer i % NBUF of its region; the next
+  // step goes out as soon as the buffer it reuses has been read.
+  int issued = 0;
+  for (; issued < NBUF && issued < mine; ++issued)
+    copies.issue(region + issued * kStepBytes, pair_of(issued));
+  for (int i = 0; i < mine; ++i) {
+    wait_steps<COPY::PER_STEP, NBUF>(issued - i - 1);
+    const uint8_t *st = region + (NBUF == 2 ? (i & 1) : 0) * kStepBytes;
+    skinny_step<STORE_S>(st, lrow, h, pl, acc, a, pair_of(i), p_end, m, o);
+    if (issued < mine) {
+      // Every read of buffer i % NBUF has been consumed by the MFMAs above.
+      copies.issue(region + (issued % NBUF) * kStepBytes, pair_of(issued));
+      ++issued;
     }
   }
 
-  // Sum the four waves in wave order; wave w finishes values r = 4w .. 4w+3.
-  __syncthreads();  // every wave is done with the ring
-  float(*red)[MT][16][64] = reinterpret_cast<float(*)[MT][16][64]>(ring);
+  // Sum the KQ waves of each token tile in wave order; wave w finishes
+  // values v = PER w .. PER w + PER - 1 of the workgroup (tile v / 16,
+  // element v % 16).
+  __syncthreads();  // every wave is done with its region (no copy is in flight)
+  float(*red)[16][64] = reinterpret_cast<float(*)[16][64]>(ring);
 #pragma unroll
-  for (int m = 0; m < MT; ++m)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) red[wave][m][r][lane] = acc[m][r];
+  for (int r = 0; r < 16; ++r) red[wave][r][lane] = acc[r];
   __syncthreads();
-  const int64_t o = o_tile + lrow;
-  float *dst = a.out + (int64_t)blockIdx.y * a.n_tok * a.out_dim;
+  float v[PER];
 #pragma unroll
-  for (int m = 0; m < MT; ++m) {
+  for (int k = 0; k < PER; ++k) {
+    const int val = PER * wave + k;
+    const int tm = val >> 4, r = val & 15;
+    float sum = red[KQ * tm][r][lane];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int r = 4 * wave + k;
-      const float v = ((red[0][m][r][lane] + red[1][m][r][lane]) + red[2][m][r][lane]) +
-                      red[3][m][r][lane];
-      // Element r of a lane: token 32 m + 8 (r / 4) + 4 h + r % 4, column lrow.
-      const int64_t t = 32 * m + 8 * (r >> 2) + 4 * h + (r & 3);
-      if (t < a.n_tok && o < a.out_dim) dst[t * a.out_dim + o] = v;
+    for (int j = 1; j < KQ; ++j) sum += red[KQ * tm + j][r][lane];
+    v[k] = sum;
+  }
+
+  if (gridDim.y > 1) {
+    // Split-K: every workgroup of an output tile leaves its sums in the
+    // partials (one coalesced slot per value), then counts itself in.  The
+    // last to arrive adds the tile's partials in split order, 0 first, as the
+    // ordered reduce would, stores the result and re-arms the counter for the
+    // next call.  Nobody waits for anybody.
+    //
+    // Coherence without cache-wide fences: the partials are stored and
+    // loaded with device-scope (agent) atomic accesses, which the L2 of every
+    // XCD treats as coherent, and every wave waits for its stores to complete
+    // before the barrier that precedes the arrival.  A fence at device scope
+    // would write back and invalidate the whole L2 of the XCD in every
+    // workgroup instead.
+    const int64_t tiles = gridDim.x;
+    constexpr int VALS = MT * 16 * 64;  // floats per workgroup
+    const int64_t slot = (int64_t)(PER * wave) * 64 + lane;
+    const int64_t mine_off = ((int64_t)blockIdx.y * tiles + blockIdx.x) * VALS + slot;
+#pragma unroll
+    for (int k = 0; k < PER; ++k)
+      __hip_atomic_store(a.partials + mine_off + k * 64, v[k], __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+    wait_vmcnt<0>();  // this wave's partials are visible at device scope
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();  // ... and every wave's
+    asm volatile("" ::: "memory");
+    if (threadIdx.x == 0)
+      arrived_before = __hip_atomic_fetch_add(a.arrivals + blockIdx.x, 1u, __ATOMIC_RELAXED,
+                                              __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    if (arrived_before != gridDim.y - 1) return;  // uniform: one LDS value
+    float sum[PER];
+    const int64_t first = (int64_t)blockIdx.x * VALS + slot;
+    for (int s0 = 0; s0 < (int)gridDim.y; s0 += 4) {
+      float p[4][PER];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int sp = min(s0 + j, (int)gridDim.y - 1);  // past the last split: re-read, unused
+#pragma unroll
+        for (int k = 0; k < PER; ++k)
+          p[j][k] = sp == (int)blockIdx.y
+                        ? v[k]
+                        : __hip_atomic_load(a.partials + first + sp * tiles * VALS + k * 64,
+                                            __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int k = 0; k < PER; ++k)
+          if (s0 + j < (int)gridDim.y) sum[k] = s0 + j == 0 ? p[j][k] : sum[k] + p[j][k];
     }
+    if (threadIdx.x == 0)
+      __hip_atomic_store(a.arrivals + blockIdx.x, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+    for (int k = 0; k < PER; ++k) v[k] = sum[k];
+  }
+
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+    // Value v = PER w + k: tile m = v / 16, element r = v % 16 of a lane:
+    // token 32 m + 8 (r / 4) + 4 h + r % 4, column lrow.
+    const int val = PER * wave + k;
+    const int tm = val >> 4, r = val & 15;
+    const int64_t t = 32 * tm + 8 * (r >> 2) + 4 * h + (r & 3);
+    if (t < a.n_tok && o < a.out_dim) a.out[t * a.out_dim + o] = v[k];
   }
 }
 
 // Every variant explicitly instantiated: without this the host side of the
-// front end dropped two of them (the host stubs were referenced but never
+// front end dropped some of them (the host stubs were referenced but never
 // emitted).
 template __global__ void skinny_kernel<1, ChunkCopies<1>, false>(const SkinnyArgs);
+template __global__ void skinny_kernel<1, ChunkCopies<2>, false>(const SkinnyArgs);
+template __global__ void skinny_kernel<2, ChunkCopies<1>, false>(const SkinnyArgs);
 template __global__ void skinny_kernel<2, ChunkCopies<2>, false>(const SkinnyArgs);
-template __global__ void skinny_kernel<1, ChunkCopies<1>, true>(const SkinnyArgs);
-template __global__ void skinny_kernel<2, ChunkCopies<2>, true>(const SkinnyArgs);
 template __global__ void skinny_kernel<1, DwordCopies<1>, false>(const SkinnyArgs);
+template __global__ void skinny_kernel<1, DwordCopies<2>, false>(const SkinnyArgs);
+template __global__ void skinny_kernel<2, DwordCopies<1>, false>(const SkinnyArgs);
 template __global__ void skinny_kernel<2, DwordCopies<2>, false>(const SkinnyArgs);
+template __global__ void skinny_kernel<1, ChunkCopies<1>, true>(const SkinnyArgs);
+template __global__ void skinny_kernel<1, ChunkCopies<2>, true>(const SkinnyArgs);
+template __global__ void skinny_kernel<2, ChunkCopies<1>, true>(const SkinnyArgs);
+template __global__ void skinny_kernel<2, ChunkCopies<2>, true>(const SkinnyArgs);
 template __global__ void skinny_kernel<1, DwordCopies<1>, true>(const SkinnyArgs);
+template __global__ void skinny_kernel<1, DwordCopies<2>, true>(const SkinnyArgs);
+template __global__ void skinny_kernel<2, DwordCopies<1>, true>(const SkinnyArgs);
 template __global__ void skinny_kernel<2, DwordCopies<2>, true>(const SkinnyArgs);
 
-template <int MT, bool STORE_S>
-void launch_skinny_variant(bool wide, dim3 grid, const SkinnyArgs &a, hipStream_t s) {
+template <int MT, int R, bool STORE_S>
+void launch_skinny_copies(bool wide, dim3 grid, const SkinnyArgs &a, hipStream_t s) {
   if (wide) {
-    auto k = skinny_kernel<MT, ChunkCopies<MT>, STORE_S>;
-    hipLaunchKernelGGL(k, grid, dim3(256), 0, s, a);
+    auto k = skinny_kernel<MT, ChunkCopies<R>, STORE_S>;
+    hipLaunchKernelGGL(k, grid, dim3(64 * kWaves), 0, s, a);
   } else {
-    auto k = skinny_kernel<MT, DwordCopies<MT>, STORE_S>;
-    hipLaunchKernelGGL(k, grid, dim3(256), 0, s, a);
+    auto k = skinny_kernel<MT, DwordCopies<R>, STORE_S>;
+    hipLaunchKernelGGL(k, grid, dim3(64 * kWaves), 0, s, a);
   }
 }
+
+// Two steps in flight per wave when a wave has more than one step.
+template <bool STORE_S>
+void launch_skinny_variant(int mt, bool two_steps, bool wide, dim3 grid, const SkinnyArgs &a,
+                           hipStream_t s) {
+  if (mt == 2) {
+    if (two_steps) launch_skinny_copies<2, 2, STORE_S>(wide, grid, a, s);
+    else launch_skinny_copies<2, 1, STORE_S>(wide, grid, a, s);
+  } else {
+    if (two_steps) launch_skinny_copies<1, 2, STORE_S>(wide, grid, a, s);
+    else launch_skinny_copies<1, 1, STORE_S>(wide, grid, a, s);
+  }
+}
+
+int skinny_mt(int64_t n_tok) { return n_tok > 32 ? 2 : 1; }
 
 }  // namespace
 
@@ -308,31 +443,44 @@ bool skinny_supported(int64_t in_dim, int64_t n_tok) {
          n_tok <= kSkinnyMaxTokens;
 }
 
-// Splits: enough workgroups for the chip (about 256), at least one pair per
-// wave, at most 16.
-int skinny_auto_split(int64_t in_dim, int64_t out_dim) {
+// Splits: enough workgroups for the chip (about 256), a step for every wave
+// of a token tile per split where the row allows, at most 16.
+int skinny_auto_split(int64_t in_dim, int64_t out_dim, int64_t n_tok) {
   const int64_t tiles = (out_dim + 31) / 32;
   const int64_t pairs = in_dim / 64;
   int64_t split = (256 + tiles - 1) / tiles;
-  split = std::min<int64_t>(split, std::max<int64_t>(pairs / 4, 1));
+  split = std::min<int64_t>(
+      split, std::max<int64_t>(pairs / (kStepPairs * (kWaves / skinny_mt(n_tok))), 1));
   split = std::min<int64_t>(split, 16);
   return (int)std::max<int64_t>(split, 1);
 }
 
+// Workspace of a split-K launch: the arrival counters (zero between calls)
+// in the first kWsCounterBytes, then the partials, MT * 4 KiB per workgroup.
 size_t skinny_workspace_bytes(int64_t out_dim, int64_t n_tok, int split) {
-  return split > 1 ? (size_t)split * (size_t)out_dim * (size_t)n_tok * sizeof(float) : 0;
+  if (split <= 1) return 0;
+  const int64_t tiles = (out_dim + 31) / 32;
+  return kWsCounterBytes + (size_t)split * (size_t)tiles * (size_t)skinny_mt(n_tok) * 4096;
+}
+
+bool skinny_split_ok(int64_t out_dim, int split) {
+  return split <= 1 || (out_dim + 31) / 32 <= (int64_t)(kWsCounterBytes / 4);
 }
 
 hipError_t launch_skinny(float *out, int32_t *blocksums, const void *w, int64_t in_dim,
                          int64_t out_dim, const void *x_q, int64_t n_tok, int split,
-                         float *partials, hipStream_t s) {
+                         void *workspace, hipStream_t s) {
   SkinnyArgs a{};
+  a.out = out;
   a.blocksums = blocksums;
   a.n_pairs = (int32_t)(in_dim / 64);
-  // Splits are whole stages (the last one may be short).
-  const int pps = (((a.n_pairs + split - 1) / split + kStagePairs - 1) / kStagePairs) * kStagePairs;
+  // Splits are whole steps (the last one may be short).
+  const int pps = ((a.n_pairs + split - 1) / split + kStepPairs - 1) / kStepPairs * kStepPairs;
   const int n_split = (a.n_pairs + pps - 1) / pps;
-  a.out = n_split > 1 ? partials : out;
+  if (n_split > 1) {
+    a.arrivals = static_cast<uint32_t *>(workspace);
+    a.partials = reinterpret_cast<float *>(static_cast<uint8_t *>(workspace) + kWsCounterBytes);
+  }
   a.w = static_cast<const uint8_t *>(w);
   a.x_q = static_cast<const uint8_t *>(x_q);
   a.out_dim = out_dim;
@@ -340,20 +488,14 @@ hipError_t launch_skinny(float *out, int32_t *blocksums, const void *w, int64_t 
   a.row_bytes = (in_dim / 32) * 34;
   a.pairs_per_split = pps;
   const dim3 grid((uint32_t)((out_dim + 31) / 32), (uint32_t)n_split);
-  // 16-byte copies need whole 16-byte chunks: rows of 8k blocks, 16-aligned bases.
+  // 16-byte copies need rows of 8k blocks and 16-aligned bases.
   const bool wide = in_dim % 256 == 0 && (reinterpret_cast<uintptr_t>(w) & 15) == 0 &&
                     (reinterpret_cast<uintptr_t>(x_q) & 15) == 0;
-  const bool two = n_tok > 32;
-  if (blocksums) {
-    if (two) launch_skinny_variant<2, true>(wide, grid, a, s);
-    else launch_skinny_variant<1, true>(wide, grid, a, s);
-  } else {
-    if (two) launch_skinny_variant<2, false>(wide, grid, a, s);
-    else launch_skinny_variant<1, false>(wide, grid, a, s);
-  }
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess || n_split == 1) return err;
-  return launch_splitk_reduce(out, partials, n_tok * out_dim, n_split, s);
+  const int mt = skinny_mt(n_tok);
+  const bool two_steps = pps > kStepPairs * (kWaves / mt);
+  if (blocksums) launch_skinny_variant<true>(mt, two_steps, wide, grid, a, s);
+  else launch_skinny_variant<false>(mt, two_steps, wide, grid, a, s);
+  return hipGetLastError();
 }
 
 }  // namespace q8

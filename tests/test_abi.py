@@ -27,7 +27,7 @@ def q8():
 def test_exports_every_declared_symbol(q8):
     lib = ctypes.CDLL(q8.LIB_PATH)
     declared = _declared()
-    assert len(declared) == 16
+    assert len(declared) == 17
     for name in declared:
         assert hasattr(lib, name), name
     assert set(declared) == set(q8.EXPORTED)
@@ -212,13 +212,24 @@ def test_plan_regimes(q8):
     assert q8.q8_0_matmul_plan(32768, 1024, 1, 0) == (q8.KERNEL_MATVEC, 1)
     assert q8.q8_0_matmul_plan(4096, 2048, 15, 0) == (q8.KERNEL_MATVEC, 1)
     # From 16 to 64 tokens the skinny matrix-core kernel, split for about
-    # 256 workgroups of 32 rows (at least one block pair per wave).
+    # 256 workgroups of 32 rows, each split at least one 2-pair step for
+    # every wave of a token tile (8 waves for one tile, 4 each for two).
     assert q8.q8_0_matmul_plan(4096, 2048, 16, 1 << 40) == (q8.KERNEL_SKINNY, 4)
     assert q8.q8_0_matmul_plan(4096, 2048, 64, 1 << 40) == (q8.KERNEL_SKINNY, 4)
     assert q8.q8_0_matmul_plan(4096, 2048, 64, 0) == (q8.KERNEL_SKINNY, 1)
     assert q8.q8_0_matmul_plan(1024, 32768, 64, 1 << 40) == (q8.KERNEL_SKINNY, 1)
-    assert q8.q8_0_matmul_plan(4096, 256, 48, 1 << 40) == (q8.KERNEL_SKINNY, 16)
-    assert q8.q8_0_matmul_workspace_bytes(4096, 2048, 64) == 4 * 2048 * 64 * 4
+    assert q8.q8_0_matmul_plan(4096, 256, 48, 1 << 40) == (q8.KERNEL_SKINNY, 8)
+    assert q8.q8_0_matmul_plan(4096, 256, 20, 1 << 40) == (q8.KERNEL_SKINNY, 4)
+    # Split-K workspace: 4096 bytes of arrival counters, then 4 KiB of
+    # partials per 32-token tile for each workgroup (64 tiles x 4 splits).
+    assert q8.q8_0_matmul_workspace_bytes(4096, 2048, 64) == 4096 + 4 * 64 * 2 * 4096
+    assert q8.q8_0_matmul_workspace_bytes(4096, 2048, 16) == 4096 + 4 * 64 * 1 * 4096
+    assert q8.q8_0_matmul_debug_workspace_bytes(4096, 2048, 64, q8.KERNEL_SKINNY, 2) == \
+        4096 + 2 * 64 * 2 * 4096
+    assert q8.q8_0_matmul_debug_workspace_bytes(4096, 2048, 64, q8.KERNEL_SKINNY, 1) == 0
+    # A skinny split needs one counter per 32-row tile: at most 1024 tiles.
+    assert q8.q8_0_matmul_debug_workspace_bytes(1024, 32768, 64, q8.KERNEL_SKINNY, 2) > 0
+    assert q8.q8_0_matmul_debug_workspace_bytes(1024, 32800, 64, q8.KERNEL_SKINNY, 2) == 0
     # Above 64 tokens the tiled GEMM; split-K aims for 256 workgroups.
     assert q8.q8_0_matmul_plan(4096, 2048, 65, 1 << 40)[0] == q8.KERNEL_MFMA
     assert q8.q8_0_matmul_plan(1024, 32768, 128, 1 << 40) == (q8.KERNEL_MFMA, 1)
@@ -226,10 +237,12 @@ def test_plan_regimes(q8):
     v, s = q8.q8_0_matmul_plan(32768, 1024, 2048, 1 << 40)
     assert v == q8.KERNEL_MFMA and s == 8
     need = q8.q8_0_matmul_workspace_bytes(32768, 1024, 2048)
-    assert need == 8 * 1024 * 2048 * 4
+    assert need == 4096 + 8 * 1024 * 2048 * 4
     # Without workspace the split falls back to 1; with some, to what fits.
     assert q8.q8_0_matmul_plan(32768, 1024, 2048, 0) == (q8.KERNEL_MFMA, 1)
-    assert q8.q8_0_matmul_plan(32768, 1024, 2048, 3 * 1024 * 2048 * 4) == (q8.KERNEL_MFMA, 3)
+    assert q8.q8_0_matmul_plan(32768, 1024, 2048, 4096 + 3 * 1024 * 2048 * 4) == (q8.KERNEL_MFMA, 3)
+    assert q8.q8_0_matmul_debug_workspace_bytes(32768, 1024, 2048, q8.KERNEL_MFMA, 3) == \
+        4096 + 3 * 1024 * 2048 * 4
     # Block counts that are not whole pairs take the generic kernel.
     assert q8.q8_0_matmul_plan(96, 64, 1, 0) == (q8.KERNEL_GENERIC, 1)
     assert q8.q8_0_matmul_plan(96, 64, 100, 0) == (q8.KERNEL_GENERIC, 1)

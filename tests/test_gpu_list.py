@@ -172,6 +172,35 @@ def test_list_special_values_fused():
           dict(in_dim=1024, out_dim=64, mode="x", x=x)], 1, "special")
 
 
+def _special_pattern(tag):
+    """1024 values: a zero block, NaN, Inf, binary16-overflowing, subnormal
+    and tiny-scale blocks, signed zeros and a tie in the quotient x/d."""
+    x = workloads.normal((1, 1024), 1.0, "cpu", "list_special", tag)
+    x[0, 0:32] = 0.0
+    x[0, 40] = float("nan")
+    x[0, 70] = float("inf")
+    x[0, 128:160] = 8321040.0
+    x[0, 160:192] = 2.0 ** -149
+    x[0, 200] = 127 * 2.0 ** -20
+    x[0, 256:288:2] = -0.0
+    d = np.float32(np.float32(3.3) / np.float32(127.0))
+    x[0, 300] = 3.3
+    x[0, 301] = float(np.float32(2.5 * np.float64(d)))    # tie in the quotient
+    x[0, 520] = -float("inf")
+    x[0, 600:632] = -8321040.0
+    x[0, 800] = -3.3
+    x[0, 801] = -float(np.float32(2.5 * np.float64(d)))   # negative tie
+    return x
+
+
+@pytest.mark.parametrize("in_dim,n_tok", [(1024, 1), (512, 2), (256, 4)])
+def test_list_special_values_one_item_wave(in_dim, n_tok):
+    """The same special values through the one-item fused kernel whose waves
+    each quantize the whole x (at most 16 pairs): the headline decode path."""
+    x = _special_pattern("wave").reshape(n_tok, in_dim).contiguous()
+    _run([dict(in_dim=in_dim, out_dim=200, mode="x+xq", x=x)], n_tok, f"special_wave{in_dim}")
+
+
 def test_list_graph_replay_matches_eager():
     """The call is capturable: replays equal the eager result every time."""
     q8 = _q8()

@@ -37,8 +37,7 @@ def _run_and_check(wq, xq, wq_o, xq_o, in_dim, out_dim, n_tok, variant, split=0,
     q8 = _q8()
     say(f"[matmul] {where} in={in_dim} out={out_dim} n_tok={n_tok} variant={variant} split={split}")
     out = torch.full((n_tok, out_dim), float("nan"), device="cuda")   # poisoned
-    ws = torch.empty(max(q8.q8_0_matmul_workspace_bytes(in_dim, out_dim, n_tok),
-                         16 * out_dim * n_tok * 4 if split else 1), dtype=torch.uint8, device="cuda")
+    ws = q8.matmul_workspace(in_dim, out_dim, n_tok, variant=variant, split_k=split)
     got, bs = q8.q8_0_matmul_debug(wq, xq, in_dim, out_dim, n_tok, variant=variant, split_k=split,
                                    out=out, workspace=ws)
     torch.cuda.synchronize()
@@ -115,12 +114,13 @@ def _run_skinny(wq, xq, wq_o, xq_o, in_dim, out_dim, n_tok, split, where):
     q8 = _q8()
     say(f"[matmul] {where} in={in_dim} out={out_dim} n_tok={n_tok} skinny split={split}")
     out = torch.full((n_tok, out_dim), float("nan"), device="cuda")
-    ws = torch.empty(max(4 * split * out_dim * n_tok, 1), dtype=torch.uint8, device="cuda")
+    ws = q8.matmul_workspace(in_dim, out_dim, n_tok, variant=q8.KERNEL_SKINNY, split_k=split)
     got, bs = q8.q8_0_matmul_debug(wq, xq, in_dim, out_dim, n_tok, variant=q8.KERNEL_SKINNY,
                                    split_k=split, blocksums=True, out=out, workspace=ws)
     plain, _ = q8.q8_0_matmul_debug(wq, xq, in_dim, out_dim, n_tok, variant=q8.KERNEL_SKINNY,
                                     split_k=split, blocksums=False, workspace=ws)
     torch.cuda.synchronize()
+    assert not ws[:4096].any(), f"{where}: split-K arrival counters not re-armed"
     ref, mag, rbs = oracle.matmul(wq_o, xq_o, in_dim, want_blocksums=True)
     assert np.array_equal(bs.cpu().numpy(), rbs), f"{where}: block sums differ"
     assert torch.equal(plain.view(torch.int32), got.view(torch.int32)), f"{where}: debug build differs"
@@ -132,15 +132,66 @@ def _run_skinny(wq, xq, wq_o, xq_o, in_dim, out_dim, n_tok, split, where):
 @pytest.mark.parametrize("in_dim,out_dim,n_tok,split", [
     (4096, 2048, 64, 4), (4096, 2048, 32, 4), (2048, 4096, 33, 2), (4096, 1000, 40, 1),
     (1024, 300, 17, 2), (64, 50, 64, 1), (192, 65, 31, 1), (128, 33, 5, 1), (4096, 64, 48, 16),
-    (1024, 32768, 64, 1), (8192, 96, 1, 3), (2048, 4096, 64, 2), (4096, 2048, 64, 0)])
+    (1024, 32768, 64, 1), (8192, 96, 1, 3), (2048, 4096, 64, 2), (4096, 2048, 64, 0),
+    (16384, 2048, 64, 4), (4160, 2048, 64, 4), (4160, 300, 20, 3), (1024, 32768, 64, 2)])
 def test_skinny_shapes(in_dim, out_dim, n_tok, split):
     # Ragged rows and token counts, one or two token tiles, waves with no
-    # block pair (192 values = 3 pairs), and split-K with uneven splits.
+    # block pair (192 values = 3 pairs), and split-K with uneven splits; K
+    # ranges longer than the resident stages (16384, 8192), dword copies
+    # (4160 values: 65 pairs) with split-K, and a split over 1024 tiles.
     w = workloads.normal((out_dim, in_dim), 0.02, "cuda", "sk", out_dim, in_dim, "w")
     x = workloads.normal((n_tok, in_dim), 1.0, "cuda", "sk", n_tok, in_dim, "x")
     x[min(3, n_tok - 1), 40:50] *= 30.0  # outlier block
     wq, xq, wq_o, xq_o = _prep(w, x)
     _run_skinny(wq, xq, wq_o, xq_o, in_dim, out_dim, n_tok, split, "skinny")
+
+
+def test_skinny_workspace_reuse_and_graph():
+    """One zero-filled workspace serves calls of different shapes and splits:
+    the in-launch split-K arrival counters are back at zero after every call,
+    so later calls and graph replays find them armed."""
+    q8 = _q8()
+    shapes = [(4096, 2048, 64, 4), (2048, 256, 20, 8), (4160, 2048, 64, 4), (4096, 2048, 64, 4)]
+    need = max(q8.q8_0_matmul_debug_workspace_bytes(k, n, t, q8.KERNEL_SKINNY, sp)
+               for k, n, t, sp in shapes)
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    data, firsts = {}, {}
+    for k, n, t, sp in shapes:
+        if (k, n, t) not in data:
+            w = workloads.normal((n, k), 0.02, "cuda", "skr", n, k, "w")
+            x = workloads.normal((t, k), 1.0, "cuda", "skr", t, k, "x")
+            data[(k, n, t)] = _prep(w, x)
+        wq, xq, wq_o, xq_o = data[(k, n, t)]
+        say(f"[matmul] skinny reuse in={k} out={n} n_tok={t} split={sp}")
+        out = torch.full((t, n), float("nan"), device="cuda")
+        q8.q8_0_matmul_debug(wq, xq, k, n, t, variant=q8.KERNEL_SKINNY, split_k=sp,
+                             blocksums=False, out=out, workspace=ws)
+        torch.cuda.synchronize()
+        assert not ws[:4096].any(), "arrival counters not re-armed"
+        ref, mag, _ = oracle.matmul(wq_o, xq_o, k)
+        assert_close(out.cpu().numpy(), ref, mag, f"skinny reuse {k}x{n}x{t}")
+        if (k, n, t) in firsts:
+            assert torch.equal(out.view(torch.int32), firsts[(k, n, t)].view(torch.int32))
+        firsts[(k, n, t)] = out
+    # Graph capture of a split-K call; every replay equals the eager result.
+    k, n, t, sp = shapes[0]
+    wq, xq, _, _ = data[(k, n, t)]
+    out = torch.empty((t, n), device="cuda")
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            q8.q8_0_matmul_debug(wq, xq, k, n, t, variant=q8.KERNEL_SKINNY, split_k=sp,
+                                 blocksums=False, out=out, workspace=ws)
+    torch.cuda.current_stream().wait_stream(s)
+    for rep in range(3):
+        out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int32), firsts[(k, n, t)].view(torch.int32)), rep
+        assert not ws[:4096].any()
 
 
 @pytest.mark.parametrize("only_block", [None, 0, 1, 2, 3, 6, 7])
@@ -203,7 +254,7 @@ def _run_outputs(wq, xq, wq_o, xq_o, in_dim, out_dim, n_tok, split, where):
     q8 = _q8()
     say(f"[matmul] {where} in={in_dim} out={out_dim} n_tok={n_tok} split={split}")
     out = torch.full((n_tok, out_dim), float("nan"), device="cuda")
-    ws = torch.empty(16 * out_dim * n_tok * 4, dtype=torch.uint8, device="cuda")
+    ws = q8.matmul_workspace(in_dim, out_dim, n_tok, variant=3, split_k=split)
     got, _ = q8.q8_0_matmul_debug(wq, xq, in_dim, out_dim, n_tok, variant=3, split_k=split,
                                   blocksums=False, out=out, workspace=ws)
     torch.cuda.synchronize()
@@ -385,7 +436,7 @@ def test_prefill_whole_tile_blocksums(name, rows, tokens, split):
     k = d["in_dim"]
     got = _run_and_check(wq, xq, wq_o, xq_o, k, rows, tokens, q8.KERNEL_MFMA, split,
                          where=f"{name} whole tiles")
-    ws = torch.empty(max(16 * rows * tokens * 4, 1), dtype=torch.uint8, device="cuda")
+    ws = q8.matmul_workspace(k, rows, tokens, variant=q8.KERNEL_MFMA, split_k=split)
     plain, _ = q8.q8_0_matmul_debug(wq, xq, k, rows, tokens, variant=q8.KERNEL_MFMA, split_k=split,
                                     blocksums=False, workspace=ws)
     torch.cuda.synchronize()
