@@ -151,12 +151,14 @@ def bench_attn_q_b(torch, q8, wl, steps, warmup):
     # Measured ceiling: a coalesced non-temporal streaming read of the same weight copies.
     sink = torch.zeros(1, dtype=torch.int32, device="cuda")
     read_us = time_kernel(torch, lambda i: q8.q8_0_probe_read(ws[i % ROT], sink), ROT)
+    # The fixed part of any launch: an empty kernel of 1024 workgroups, timed the same way.
+    launch_us = time_kernel(torch, lambda i: q8.q8_0_probe_launch(1024, sink), ROT)
     fused_bytes = n * row_bytes(k) + 4 * k + 4 * n       # W + fp32 x + out
     mv_bytes = n * row_bytes(k) + row_bytes(k) + 4 * n   # W + x_q + out
     return dict(sec=sec, steps=done, step_bytes=fused_bytes, kernel_bytes=fused_bytes,
                 kernel_us=kern_us, sec_separate=sec_sep, matvec_us=mv_us, matvec_bytes=mv_bytes,
                 quant_us=quant_us, plan=q8.q8_0_matmul_plan(k, n, 1, 0),
-                read_us=read_us, read_bytes=n * row_bytes(k))
+                read_us=read_us, read_bytes=n * row_bytes(k), launch_us=launch_us)
 
 
 def bench_decode5(torch, q8, wl, steps, warmup):
@@ -502,7 +504,10 @@ def main():
                      "measured_ceiling": {
                          "kind": "coalesced non-temporal streaming read of the same weight copies (q8_0_probe_read)",
                          "GBs": round(h["read_bytes"] / (h["read_us"] * 1e-6) / 1e9, 1),
-                         "frac": round(ach / (h["read_bytes"] / (h["read_us"] * 1e-6) / 1e9), 4)},
+                         "frac": round(ach / (h["read_bytes"] / (h["read_us"] * 1e-6) / 1e9), 4),
+                         "read_us": round(h["read_us"], 3),
+                         "launch_floor_us": round(h["launch_us"], 3),
+                         "launch_floor_kind": "empty kernel, 1024 workgroups (q8_0_probe_launch)"},
                      "traffic": profiled_traffic("matvec_list_attn_q_b.md"),
                      "kernel": "matvec_fused_kernel (the one-item q8_0_matmul_list launch: in-launch quantize + matvec)",
                      "kernel_us": round(h["kernel_us"], 3), "bytes_per_launch": h["kernel_bytes"]},

@@ -314,6 +314,13 @@ int q8_0_matmul_plan(int64_t in_dim, int64_t out_dim, int64_t n_tok,
  * Errors: bad size or alignment, null pointers -> Q8_0_EINVAL. */
 int q8_0_probe_read(const void *buf, size_t bytes, uint32_t *sink, hipStream_t stream);
 
+/* Measurement probe (the fixed cost of a launch, part of the decode ceiling:
+ * a token's work is a chain of short dispatches, "Part 6: GPU 加速",
+ * section 4n): an empty kernel of `workgroups` workgroups of 256 lanes that
+ * exits at once.  sink: device uint32, never written.
+ * Errors: workgroups outside [1, 65536], null sink -> Q8_0_EINVAL. */
+int q8_0_probe_launch(int32_t workgroups, uint32_t *sink, hipStream_t stream);
+
 /* Measurement probe (the matrix-core ceiling that the int8 GEMM kernels are
  * reported against beside the 5 POPS peak): 512 workgroups of 4 waves, each
  * wave `iters` rounds of 4 independent v_mfma_i32_32x32x32_i8, i.e.

@@ -82,6 +82,7 @@ _sig = {
     "q8_0_moe_ffn_workspace_bytes": ([_i64, _i32, _i32, _i64, _i64], _sz),
     "q8_0_moe_ffn": ([ctypes.POINTER(MoeFfnArgs), _vp, _sz, _vp], ctypes.c_int),
     "q8_0_probe_read": ([_vp, _sz, _vp, _vp], ctypes.c_int),
+    "q8_0_probe_launch": ([_i32, _vp, _vp], ctypes.c_int),
     "q8_0_probe_mfma_i8": ([_i32, _vp, _vp], ctypes.c_int),
     "q8_0_probe_mfma_mix": ([_i32, _i32, _vp, _vp], ctypes.c_int),
     "q8_0_strerror": ([ctypes.c_int], ctypes.c_char_p),
@@ -326,6 +327,12 @@ def q8_0_probe_read(buf: torch.Tensor, sink: torch.Tensor) -> None:
     """Streaming read of the whole (contiguous, 16-byte aligned) device tensor."""
     _check(_lib.q8_0_probe_read(_dev(buf, "buf"), buf.numel() * buf.element_size(),
                                 _dev(sink, "sink"), _stream()), "q8_0_probe_read")
+
+
+def q8_0_probe_launch(workgroups: int, sink: torch.Tensor) -> None:
+    """An empty launch of `workgroups` workgroups: the fixed cost of a launch."""
+    _check(_lib.q8_0_probe_launch(int(workgroups), _dev(sink, "sink"), _stream()),
+           "q8_0_probe_launch")
 
 
 def q8_0_probe_mfma_i8(iters: int, sink: torch.Tensor) -> None:

@@ -461,6 +461,13 @@ int q8_0_probe_read(const void *buf, size_t bytes, uint32_t *sink, hipStream_t s
   return status_of(q8::launch_probe_read(buf, (int64_t)bytes, sink, stream));
 }
 
+int q8_0_probe_launch(int32_t workgroups, uint32_t *sink, hipStream_t stream) {
+  if (workgroups < 1 || workgroups > 65536 || !sink || !aligned(sink, 4)) return Q8_0_EINVAL;
+  int st = check_device();
+  if (st != Q8_0_OK) return st;
+  return status_of(q8::launch_probe_launch(workgroups, sink, stream));
+}
+
 int q8_0_probe_mfma_i8(int32_t iters, uint32_t *sink, hipStream_t stream) {
   if (iters < 1 || !sink || !aligned(sink, 4)) return Q8_0_EINVAL;
   int st = check_device();

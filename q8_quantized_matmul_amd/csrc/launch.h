@@ -116,10 +116,11 @@ hipError_t launch_gemm(float *out, int32_t *blocksums, const void *w, int64_t in
 hipError_t launch_splitk_reduce(float *out, const float *partials, int64_t n, int n_split,
                                 hipStream_t s);
 
-// probe.hip: measured ceilings (a streaming read, an int8 MFMA loop).
+// probe.hip: measured ceilings (a streaming read, an empty launch, int8 MFMA loops).
 constexpr int kProbeWorkgroups = 512;  // 2 per CU, 4 waves each
 constexpr int kProbeChains = 4;        // independent MFMA chains per wave
 hipError_t launch_probe_read(const void *buf, int64_t bytes, uint32_t *sink, hipStream_t s);
+hipError_t launch_probe_launch(int32_t workgroups, uint32_t *sink, hipStream_t s);
 hipError_t launch_probe_mfma(int32_t iters, uint32_t *sink, hipStream_t s);
 hipError_t launch_probe_mix(int32_t iters, int32_t mix, uint32_t *sink, hipStream_t s);
 

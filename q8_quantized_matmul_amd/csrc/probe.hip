@@ -1,6 +1,7 @@
 // probe.hip -- measured ceilings that the hot-path kernels are reported
 // against beside the published peaks: a plain coalesced streaming read (the
-// HBM ceiling of the matvec kernels) and a loop of independent int8 MFMAs
+// HBM ceiling of the matvec kernels), an empty launch (the fixed cost every
+// launch pays before a byte moves) and a loop of independent int8 MFMAs
 // (the matrix-core ceiling of the GEMM kernels).  Neither computes anything
 // of the method; each keeps its work alive through a checksum that is stored
 // only if it takes one impossible value.
@@ -30,6 +31,12 @@ __global__ __launch_bounds__(256) void probe_read_kernel(const u32x4 *__restrict
 #pragma unroll
   for (int u = 0; u < kReadUnroll; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
   if (acc == kNever) sink[0] = acc;
+}
+
+// Nothing but the launch: every lane exits at once (the store never happens:
+// no workgroup index equals the workgroup count).
+__global__ __launch_bounds__(256) void probe_launch_kernel(uint32_t *sink) {
+  if (blockIdx.x == gridDim.x) sink[0] = kNever;
 }
 
 // Four independent accumulating chains per wave; operands change every round
@@ -155,6 +162,11 @@ hipError_t launch_probe_read(const void *buf, int64_t bytes, uint32_t *sink, hip
   const int64_t grid = (n16 + 256 * kReadUnroll - 1) / (256 * kReadUnroll);
   hipLaunchKernelGGL(probe_read_kernel, dim3((uint32_t)grid), dim3(256), 0, s,
                      static_cast<const u32x4 *>(buf), n16, sink);
+  return hipGetLastError();
+}
+
+hipError_t launch_probe_launch(int32_t workgroups, uint32_t *sink, hipStream_t s) {
+  hipLaunchKernelGGL(probe_launch_kernel, dim3((uint32_t)workgroups), dim3(256), 0, s, sink);
   return hipGetLastError();
 }
 

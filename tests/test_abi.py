@@ -27,7 +27,7 @@ def q8():
 def test_exports_every_declared_symbol(q8):
     lib = ctypes.CDLL(q8.LIB_PATH)
     declared = _declared()
-    assert len(declared) == 17
+    assert len(declared) == 18
     for name in declared:
         assert hasattr(lib, name), name
     assert set(declared) == set(q8.EXPORTED)
@@ -282,3 +282,6 @@ def test_probe_validation(q8):
     assert lib.q8_0_probe_mfma_mix(0, 1, FAKE, None) == q8.Q8_0_EINVAL
     assert lib.q8_0_probe_mfma_mix(10, 3, FAKE, None) == q8.Q8_0_EINVAL
     assert lib.q8_0_probe_mfma_mix(10, 1, None, None) == q8.Q8_0_EINVAL
+    assert lib.q8_0_probe_launch(0, FAKE, None) == q8.Q8_0_EINVAL
+    assert lib.q8_0_probe_launch(65537, FAKE, None) == q8.Q8_0_EINVAL
+    assert lib.q8_0_probe_launch(16, None, None) == q8.Q8_0_EINVAL

@@ -66,3 +66,16 @@ def test_probe_mfma_mix_runs_and_scales(mix):
     assert int(sink.item()) == 0
     assert t8 > 4 * t1
 
+
+
+def test_probe_launch_runs():
+    """The empty launch leaves the sink alone and costs far less than a
+    launch that streams memory (it is the fixed part of every launch)."""
+    q8 = _q8()
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    big = torch.empty(64 << 20, dtype=torch.uint8, device="cuda")
+    t_empty = _time_us(lambda: q8.q8_0_probe_launch(1024, sink), reps=50)
+    t_read = _time_us(lambda: q8.q8_0_probe_read(big, sink), reps=20)
+    say(f"[probe] empty launch {t_empty:.2f} us, 64 MiB read {t_read:.1f} us")
+    assert int(sink.item()) == 0
+    assert t_empty < t_read
