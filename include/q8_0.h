@@ -66,7 +66,7 @@ enum {
     Q8_0_KERNEL_GENERIC = 1, /* one block per lane, any shape           */
     Q8_0_KERNEL_MATVEC = 2,  /* weight-streaming matvec, small n_tok     */
     Q8_0_KERNEL_MFMA = 3,    /* int8 MFMA GEMM, large n_tok              */
-    Q8_0_KERNEL_SKINNY = 4   /* int8 MFMA, weights streamed, n_tok <= 64 */
+    Q8_0_KERNEL_SKINNY = 4   /* int8 MFMA, rows staged in LDS, n_tok <= 64 */
 };
 
 /* Quantize activations to Q8_0 ("Part 3: 模型架构", section 2 rule, per
@@ -251,7 +251,7 @@ typedef struct q8_0_matmul_item {
  * For each item: if x is set, x_q_i = q8_0_quantize_act(x); then
  * out = q8_0_matmul(w, x_q_i) with no workspace.  Every output and every
  * x_q byte is bit-identical to those separate calls.
- * Items on the weight-streaming path with n_tok < 16 share one launch.  An item
+ * Items on the weight-streaming path (n_tok < 12) share one launch.  An item
  * with x set whose in_dim is one of 64, 128, ..., 4096 with n_tok * in_dim <=
  * 4096 (and x 16-byte, x_q 4-byte aligned) is quantized inside that launch,
  * so a list of such decode projections is a single kernel launch; x_q may

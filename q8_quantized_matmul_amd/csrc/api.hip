@@ -17,14 +17,16 @@ static_assert(Q8_0_MOE_STATIC_SCRATCH_BYTES == q8::kMoeStaticScratchBytes,
 
 namespace {
 
-// Regimes by token count (measured on 4096->2048, 2048->4096, 4096->1024 and
-// 1024->32768): the weight-streaming matvec below 16 tokens, the skinny
-// matrix-core kernel (weight and token rows staged in LDS) from 16 to 64,
-// the LDS-tiled GEMM above.
-constexpr int64_t kSkinnyMinTokens = 16;
-// The shared list launch reads each token's x row per wave from global
-// memory; from 16 tokens an item runs as its own (LDS-staged) matvec launch.
-constexpr int64_t kListMaxTokens = 15;
+// Regimes by token count (measured on 4096->2048, 2048->4096, 4096->1024,
+// 4096->512 and 1024->32768, graph-replayed calls): the weight-streaming
+// matvec below 12 tokens, the skinny matrix-core kernel (one launch, split-K
+// inside it) from 12 to 64, the LDS-tiled GEMM above.  Rows the matvec
+// cannot take (pair counts that are neither a power of two below 64 nor a
+// multiple of 64, e.g. in_dim 1536 or 7168) go to the skinny kernel from two
+// tokens: the generic kernel's cost grows by 3-4 us per token there.
+constexpr int64_t kSkinnyMinTokens = 12;
+// The shared list launch takes the matvec items, so below the skinny regime.
+constexpr int64_t kListMaxTokens = kSkinnyMinTokens - 1;
 constexpr int32_t kMaxExperts = 8192;
 constexpr int kMaxDevices = 64;
 
@@ -59,7 +61,8 @@ bool matvec_ok(int64_t in_dim) { return q8::matvec_shape(in_dim, nullptr); }
 Plan make_plan(int64_t in_dim, int64_t out_dim, int64_t n_tok, size_t ws_bytes, bool fast_align) {
   Plan p{Q8_0_KERNEL_GENERIC, 1};
   if (!fast_align) return p;
-  if (n_tok >= kSkinnyMinTokens && q8::skinny_supported(in_dim, n_tok)) {
+  const bool skinny_regime = n_tok >= kSkinnyMinTokens || (n_tok >= 2 && !matvec_ok(in_dim));
+  if (skinny_regime && q8::skinny_supported(in_dim, n_tok)) {
     p.variant = Q8_0_KERNEL_SKINNY;
     int split = q8::skinny_split_ok(out_dim, 2) ? q8::skinny_auto_split(in_dim, out_dim, n_tok) : 1;
     while (split > 1 && q8::skinny_workspace_bytes(out_dim, n_tok, split) > ws_bytes) --split;

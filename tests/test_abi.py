@@ -210,8 +210,14 @@ def test_plan_regimes(q8):
     # Decode shapes stream weights through the matvec kernel.
     assert q8.q8_0_matmul_plan(1024, 32768, 1, 0) == (q8.KERNEL_MATVEC, 1)
     assert q8.q8_0_matmul_plan(32768, 1024, 1, 0) == (q8.KERNEL_MATVEC, 1)
-    assert q8.q8_0_matmul_plan(4096, 2048, 15, 0) == (q8.KERNEL_MATVEC, 1)
-    # From 16 to 64 tokens the skinny matrix-core kernel, split for about
+    assert q8.q8_0_matmul_plan(4096, 2048, 11, 0) == (q8.KERNEL_MATVEC, 1)
+    assert q8.q8_0_matmul_plan(4096, 2048, 12, 0) == (q8.KERNEL_SKINNY, 1)
+    # Rows the matvec cannot take: the generic kernel at one token, the
+    # skinny kernel from two.
+    assert q8.q8_0_matmul_plan(7168, 2048, 1, 0) == (q8.KERNEL_GENERIC, 1)
+    assert q8.q8_0_matmul_plan(7168, 2048, 2, 0) == (q8.KERNEL_SKINNY, 1)
+    assert q8.q8_0_matmul_plan(1536, 4096, 4, 1 << 40)[0] == q8.KERNEL_SKINNY
+    # From 12 to 64 tokens the skinny matrix-core kernel, split for about
     # 256 workgroups of 32 rows, each split at least one 2-pair step for
     # every wave of a token tile (8 waves for one tile, 4 each for two).
     assert q8.q8_0_matmul_plan(4096, 2048, 16, 1 << 40) == (q8.KERNEL_SKINNY, 4)
