@@ -443,14 +443,18 @@ bool skinny_supported(int64_t in_dim, int64_t n_tok) {
          n_tok <= kSkinnyMaxTokens;
 }
 
-// Splits: enough workgroups for the chip (about 256), a step for every wave
-// of a token tile per split where the row allows, at most 16.
-int skinny_auto_split(int64_t in_dim, int64_t out_dim, int64_t n_tok) {
+// Splits.  The split-K completion (partials out, an arrival counter, the
+// last arrival's sum) puts about 1.5 us of serial memory round trips on the
+// critical path, so a split has to buy more than that: with 128 or more
+// tiles half the chip is already busy and one split is fastest; below that,
+// enough workgroups for the chip (about 256), at least 16 block pairs per
+// split (a full step for each of the eight waves), at most 16 splits.
+int skinny_auto_split(int64_t in_dim, int64_t out_dim) {
   const int64_t tiles = (out_dim + 31) / 32;
   const int64_t pairs = in_dim / 64;
+  if (tiles >= 128) return 1;
   int64_t split = (256 + tiles - 1) / tiles;
-  split = std::min<int64_t>(
-      split, std::max<int64_t>(pairs / (kStepPairs * (kWaves / skinny_mt(n_tok))), 1));
+  split = std::min<int64_t>(split, std::max<int64_t>(pairs / (kStepPairs * kWaves), 1));
   split = std::min<int64_t>(split, 16);
   return (int)std::max<int64_t>(split, 1);
 }

@@ -217,15 +217,19 @@ def test_plan_regimes(q8):
     assert q8.q8_0_matmul_plan(7168, 2048, 1, 0) == (q8.KERNEL_GENERIC, 1)
     assert q8.q8_0_matmul_plan(7168, 2048, 2, 0) == (q8.KERNEL_SKINNY, 1)
     assert q8.q8_0_matmul_plan(1536, 4096, 4, 1 << 40)[0] == q8.KERNEL_SKINNY
-    # From 12 to 64 tokens the skinny matrix-core kernel, split for about
-    # 256 workgroups of 32 rows, each split at least one 2-pair step for
-    # every wave of a token tile (8 waves for one tile, 4 each for two).
+    # From 12 to 64 tokens the skinny matrix-core kernel.  Split-K only
+    # below 128 tiles of 32 rows: about 256 workgroups, at least 16 block
+    # pairs per split, at most 16 splits.
     assert q8.q8_0_matmul_plan(4096, 2048, 16, 1 << 40) == (q8.KERNEL_SKINNY, 4)
     assert q8.q8_0_matmul_plan(4096, 2048, 64, 1 << 40) == (q8.KERNEL_SKINNY, 4)
     assert q8.q8_0_matmul_plan(4096, 2048, 64, 0) == (q8.KERNEL_SKINNY, 1)
+    assert q8.q8_0_matmul_plan(2048, 4096, 16, 1 << 40) == (q8.KERNEL_SKINNY, 1)
+    assert q8.q8_0_matmul_plan(2048, 4064, 16, 1 << 40) == (q8.KERNEL_SKINNY, 2)
     assert q8.q8_0_matmul_plan(1024, 32768, 64, 1 << 40) == (q8.KERNEL_SKINNY, 1)
-    assert q8.q8_0_matmul_plan(4096, 256, 48, 1 << 40) == (q8.KERNEL_SKINNY, 8)
-    assert q8.q8_0_matmul_plan(4096, 256, 20, 1 << 40) == (q8.KERNEL_SKINNY, 4)
+    assert q8.q8_0_matmul_plan(4096, 1024, 64, 1 << 40) == (q8.KERNEL_SKINNY, 4)
+    assert q8.q8_0_matmul_plan(7168, 2048, 32, 1 << 40) == (q8.KERNEL_SKINNY, 4)
+    assert q8.q8_0_matmul_plan(4096, 256, 48, 1 << 40) == (q8.KERNEL_SKINNY, 4)
+    assert q8.q8_0_matmul_plan(65536, 256, 20, 1 << 40) == (q8.KERNEL_SKINNY, 16)
     # Split-K workspace: 4096 bytes of arrival counters, then 4 KiB of
     # partials per 32-token tile for each workgroup (64 tiles x 4 splits).
     assert q8.q8_0_matmul_workspace_bytes(4096, 2048, 64) == 4096 + 4 * 64 * 2 * 4096
