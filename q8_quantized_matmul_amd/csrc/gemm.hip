@@ -1,5 +1,5 @@
 // gemm.hip -- Q8_0 x Q8_0 GEMM on gfx950 matrix cores for many tokens
-// (prefill, and any call with more than 64 tokens; 20..64 go to the skinny
+// (prefill, and any call with more than 64 tokens; 12..64 go to the skinny
 // kernel).
 //
 // Same arithmetic as the matvec ("Part 6: 代码走读", trace 3): per output

@@ -1,5 +1,6 @@
 // skinny.hip -- Q8_0 matmul for up to 64 tokens on the matrix cores (the
-// plan uses it from 16 tokens), a 32-row output tile per workgroup.
+// plan uses it from 12 tokens, from 2 for rows the matvec cannot take), a
+// 32-row output tile per workgroup.
 //
 // The method is the same as everywhere (ds4-learning "Part 6: 代码走读",
 // trace 3: out[t][o] = sum over blocks of d_w * d_x * S_b); this kernel
