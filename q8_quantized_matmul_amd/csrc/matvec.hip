@@ -25,7 +25,8 @@
 //     staged there by direct copies (StagedX: grouped launches and two or
 //     more tokens), or quantized there from fp32 by the workgroup itself
 //     (LdsX: the list launch); single-token launches read it per wave from
-//     global memory (GlobalX).
+//     global memory (GlobalX), rows of 64 or more pairs as coalesced chunks
+//     issued ahead of the weights.
 #include <algorithm>
 #include <type_traits>
 
@@ -83,8 +84,9 @@ struct GlobalX {
 
 // The same x source for the single-token matvec kernel, whose body loads
 // item 0's x pairs before the weights (attn_q_b separate matvec 7.78 -> 7.65
-// us on one box).  The list kernel keeps GlobalX: there the early load cost
-// decode5 15.0 -> 16.1 us.
+// us on one box).  The list kernel keeps GlobalX, which loads early only in
+// rows of 64 or more pairs (coalesced chunk loads, decode5 15.3 -> 14.4 us):
+// there lane-strided early loads of the short rows cost decode5 15.0 -> 16.1 us.
 struct GlobalXFirst : GlobalX {};
 
 // StagedX: the x_q rows of the workgroup's items, XT at a time, copied into
@@ -279,6 +281,27 @@ constexpr int kCoalLdsDwords = 4 * kCoalRegions * kCoalDwords;
 // of every region (a 16-byte load is then wholly inside or wholly past it).
 constexpr bool coal_body(int lpr, int rg, int cpw) { return rg * cpw <= kCoalRegions && lpr >= 4; }
 
+// One wave's 64-pair chunk (4352 contiguous bytes) from coalesced registers
+// to the pair layout: lane l holds the chunk's 16-byte pieces l, l + 64,
+// l + 128, l + 192 and its dword 1024 + l; they are written to the wave's LDS
+// region `reg` (kCoalDwords dwords) in byte order, and lane l reads back pair
+// l at dword 17 l.  LDS operations of one wave run in order; the fences keep
+// the compiler from moving them past each other or past the region's next use.
+__device__ __forceinline__ void coal_to_pair(uint32_t *reg, const u32x4_a4 (&piece)[4],
+                                             uint32_t tail, int lane,
+                                             uint32_t (&d)[kPairDwords]) {
+  u32x4_a4 *dst = reinterpret_cast<u32x4_a4 *>(reg);
+#pragma unroll
+  for (int k = 0; k < 4; ++k) dst[64 * k + lane] = piece[k];
+  reg[1024 + lane] = tail;
+  __builtin_amdgcn_wave_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+#pragma unroll
+  for (int i = 0; i < kPairDwords; ++i) d[i] = reg[kPairDwords * lane + i];
+  __builtin_amdgcn_wave_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
 // One workgroup tile of the matvec: TILE_ROWS weight rows against n_items x
 // rows.  `tile` is the tile index within the matrix; `w` and `items` the
 // (possibly per-expert) weights and item list.
@@ -288,7 +311,9 @@ constexpr bool coal_body(int lpr, int rg, int cpw) { return rg * cpw <= kCoalReg
 // COAL: the weight rows come in through whole coalesced 16-byte non-temporal
 // loads, passed through a per-wave LDS region from which each lane reads its
 // pair, instead of per-lane 68-byte pair loads (wst: kCoalDwords dwords per
-// region, (RG * CPW) regions per wave).
+// region, (RG * CPW) regions per wave).  Single-token bodies of rows of 64 or
+// more pairs also pass item 0's x chunks through the wave's first region
+// (without COAL, wst holds one region per wave for that).
 template <int LPR, int WPR, int CPW, int RG, bool GROUPED, bool STORE_S, class XS,
           bool PAIR = false, bool COAL = false>
 __device__ __forceinline__ void matvec_body(const MatvecArgs &a, int64_t tile, const uint8_t *w,
@@ -312,15 +337,42 @@ __device__ __forceinline__ void matvec_body(const MatvecArgs &a, int64_t tile, c
     pair_of[c] = (LPR < 64) ? (int64_t)(lane % LPR) : (int64_t)(c * WPR + part) * 64 + lane;
 
   // A global x row is otherwise loaded only once the weights have landed:
-  // with GlobalXFirst (the single-token matvec kernel) item 0's pairs are
-  // loaded first here, so their latency overlaps the weight stream.  Callers
-  // launch with at least one item, and pair_of stays inside the row.
-  constexpr bool XPRE = std::is_same_v<XS, GlobalXFirst> && !GROUPED && CPW <= 2;
+  // item 0's pairs are loaded first here, so their latency overlaps the
+  // weight stream, with GlobalXFirst (the single-token matvec kernel) and
+  // for the list kernel's rows of 64 or more pairs.  In those rows a wave's x
+  // pairs are one contiguous chunk: they come in through coalesced 16-byte
+  // loads (8 cache lines per instruction instead of 34 for lane-strided pair
+  // loads), turned into the pair layout through LDS once the weight loads
+  // are issued.  Callers launch with at least one item, and pair_of stays
+  // inside the row.
+  constexpr bool XPRE =
+      (std::is_same_v<XS, GlobalXFirst> || (std::is_same_v<XS, GlobalX> && LPR == 64 && COAL)) &&
+      !GROUPED && CPW <= 2;
+  constexpr bool XCOAL = XPRE && LPR == 64;
   uint32_t xpre[CPW][kPairDwords];
-  if constexpr (XPRE) {
+  u32x4_a4 xpiece[XCOAL ? CPW : 1][4];
+  uint32_t xtail[XCOAL ? CPW : 1];
+  if constexpr (XCOAL) {
+#pragma unroll
+    for (int c = 0; c < CPW; ++c) {
+      const uint8_t *src = xs.x_q + (int64_t)(c * WPR + part) * 64 * kPairBytes;
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        xpiece[c][k] = *reinterpret_cast<const u32x4_a4 *>(src + 16 * (64 * k + lane));
+      xtail[c] = *reinterpret_cast<const uint32_t *>(src + 4096 + 4 * lane);
+    }
+  } else if constexpr (XPRE) {
 #pragma unroll
     for (int c = 0; c < CPW; ++c) xs.load(0, 0, pair_of[c], xpre[c]);
   }
+  auto x_from_pieces = [&]() {
+    if constexpr (XCOAL) {
+      const int wave_u = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+      uint32_t *reg = wst + wave_u * (COAL ? kCoalRegions : 1) * kCoalDwords;
+#pragma unroll
+      for (int c = 0; c < CPW; ++c) coal_to_pair(reg, xpiece[c], xtail[c], lane, xpre[c]);
+    }
+  };
   // Every lane issues the same loads (rows past the end re-read the last row,
   // whose results are never stored), so the wait for the prefetched x rows
   // can leave the weight loads in flight.
@@ -361,6 +413,7 @@ __device__ __forceinline__ void matvec_body(const MatvecArgs &a, int64_t tile, c
       }
     }
     xs.publish();
+    x_from_pieces();
     // Through this wave's LDS regions: write the region back in byte order,
     // then lane l reads its pair at byte 68 l.  LDS operations of one wave
     // run in order, so no barrier is needed.
@@ -391,6 +444,7 @@ __device__ __forceinline__ void matvec_body(const MatvecArgs &a, int64_t tile, c
       }
     }
     xs.publish();
+    x_from_pieces();
   }
 
   for (int64_t it = 0; it < n_items; ++it) {
@@ -508,8 +562,11 @@ __global__ __launch_bounds__(256) void matvec_kernel(const MatvecArgs a) {
     matvec_body<LPR, WPR, CPW, RG, GROUPED, STORE_S, GlobalXFirst, false, true>(
         a, blockIdx.x, w, items, n_items, xs, nullptr, wst);
   } else {
+    // one LDS region per wave for the x chunks of rows of 64 or more pairs
+    __shared__ __attribute__((aligned(16))) uint32_t xst[LPR == 64 ? 4 * kCoalDwords : 1];
     GlobalXFirst xs{{a.x_q, a.row_bytes}};
-    matvec_body<LPR, WPR, CPW, RG, GROUPED, STORE_S>(a, blockIdx.x, w, items, n_items, xs);
+    matvec_body<LPR, WPR, CPW, RG, GROUPED, STORE_S>(a, blockIdx.x, w, items, n_items, xs,
+                                                     nullptr, xst);
   }
 }
 
