@@ -157,16 +157,22 @@ def matmul_workspace(in_dim: int, out_dim: int, n_tok: int, device="cuda", varia
     return torch.zeros(max(n, 1), dtype=torch.uint8, device=device)
 
 
+def _nbytes(t: torch.Tensor) -> int:
+    return 0 if t is None else t.numel() * t.element_size()
+
+
 def q8_0_matmul(w: torch.Tensor, x_q: torch.Tensor, in_dim: int, out_dim: int, n_tok: int,
                 out: torch.Tensor = None, workspace: torch.Tensor = None) -> torch.Tensor:
-    """out fp32 [n_tok][out_dim] = Q8_0 weights [out_dim][in_dim] x Q8_0 x_q [n_tok][in_dim]."""
+    """out fp32 [n_tok][out_dim] = Q8_0 weights [out_dim][in_dim] x Q8_0 x_q [n_tok][in_dim].
+    Without a workspace, one is allocated (and zero-filled) only for plans that
+    need it; plans that need none (the matvec) get a null pointer."""
     if out is None:
         out = torch.empty((n_tok, out_dim), dtype=torch.float32, device=w.device)
-    if workspace is None:
+    if workspace is None and q8_0_matmul_workspace_bytes(in_dim, out_dim, n_tok) > 0:
         workspace = matmul_workspace(in_dim, out_dim, n_tok, w.device)
     _check(_lib.q8_0_matmul(_dev(out, "out", torch.float32), _dev(w, "w"), in_dim, out_dim,
                             _dev(x_q, "x_q"), n_tok, _dev(workspace, "workspace"),
-                            workspace.numel() * workspace.element_size(), _stream()),
+                            _nbytes(workspace), _stream()),
            "q8_0_matmul")
     return out
 
@@ -180,13 +186,14 @@ def q8_0_matmul_debug(w, x_q, in_dim, out_dim, n_tok, variant=KERNEL_AUTO, split
     if blocksums:
         bs = torch.empty((n_tok, out_dim, in_dim // BLOCK_ELEMS), dtype=torch.int32,
                          device=w.device)
-    if workspace is None:
+    if workspace is None and q8_0_matmul_debug_workspace_bytes(in_dim, out_dim, n_tok, variant,
+                                                               split_k) > 0:
         workspace = matmul_workspace(in_dim, out_dim, n_tok, w.device, variant, split_k)
     _check(_lib.q8_0_matmul_debug(_dev(out, "out", torch.float32),
                                   _dev(bs, "blocksums") if bs is not None else None,
                                   _dev(w, "w"), in_dim, out_dim, _dev(x_q, "x_q"), n_tok,
                                   _dev(workspace, "workspace"),
-                                  workspace.numel() * workspace.element_size(), variant, split_k,
+                                  _nbytes(workspace), variant, split_k,
                                   _stream()), "q8_0_matmul_debug")
     return out, bs
 

@@ -276,10 +276,17 @@ constexpr int kWaveXPairs = 16;
 constexpr int kCoalDwords = 64 * kPairDwords;
 constexpr int kCoalRegions = 2;
 constexpr int kCoalLdsDwords = 4 * kCoalRegions * kCoalDwords;
-// Bodies that stage their weights this way: at most two regions per wave, and
-// rows of at least four pairs, so that the matrix ends on a 16-byte boundary
-// of every region (a 16-byte load is then wholly inside or wholly past it).
+// Bodies that stage their weights this way: rows of at least four pairs, so
+// that the matrix ends on a 16-byte boundary of every region (a 16-byte load
+// is then wholly inside or wholly past it), and at most two (row group, chunk)
+// regions per wave.  The list kernel's two-row-group body of 32768-wide rows
+// (four chunks per wave) also takes it, its chunks passing through the two
+// regions in turn: 8.6 -> 8.2 us for that row as a one-item list, where the
+// same body in the single-token kernel gained nothing.
 constexpr bool coal_body(int lpr, int rg, int cpw) { return rg * cpw <= kCoalRegions && lpr >= 4; }
+constexpr bool coal_list_body(int lpr, int wpr, int rg, int cpw) {
+  return coal_body(lpr, rg, cpw) || (lpr == 64 && wpr == 4 && cpw == 2 && rg == 2);
+}
 
 // One wave's 64-pair chunk (4352 contiguous bytes) from coalesced registers
 // to the pair layout: lane l holds the chunk's 16-byte pieces l, l + 64,
@@ -379,7 +386,7 @@ __device__ __forceinline__ void matvec_body(const MatvecArgs &a, int64_t tile, c
   xs.prefetch();
   uint32_t wr[NM][RG][CPW][kPairDwords];
   if constexpr (COAL) {
-    static_assert(!PAIR && coal_body(LPR, RG, CPW), "coalesced weight staging");
+    static_assert(!PAIR && coal_list_body(LPR, WPR, RG, CPW), "coalesced weight staging");
     // A wave's 64 pairs of one (row group, chunk) are 4352 contiguous bytes:
     // RPW whole rows, or one 64-pair chunk of a row.  Lane l loads 16-byte
     // chunks l, l + 64, l + 128, l + 192 and then dword 1024 + l, so every
@@ -388,7 +395,8 @@ __device__ __forceinline__ void matvec_body(const MatvecArgs &a, int64_t tile, c
     // feeds only outputs that are not stored, and nothing is read outside the
     // matrix.  The loads go to registers (not direct to LDS) and nothing
     // branches between them and the earlier x loads, so waiting for x does
-    // not wait for the weights.
+    // not wait for the weights.  Region (g * CPW + c) mod kCoalRegions takes
+    // the chunk; a region is rewritten only after the wave's reads of it.
     const int wave_u = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     const int64_t rb0 = tile * TILE_ROWS + (wave_u / WPR) * ROWS_PER_SLOT;
     uint32_t *mine = wst + wave_u * (kCoalRegions * kCoalDwords);
@@ -416,12 +424,13 @@ __device__ __forceinline__ void matvec_body(const MatvecArgs &a, int64_t tile, c
     x_from_pieces();
     // Through this wave's LDS regions: write the region back in byte order,
     // then lane l reads its pair at byte 68 l.  LDS operations of one wave
-    // run in order, so no barrier is needed.
+    // run in order, so no barrier is needed; the fences keep the compiler
+    // from moving a region's next writes above its reads.
 #pragma unroll
     for (int g = 0; g < RG; ++g) {
 #pragma unroll
       for (int c = 0; c < CPW; ++c) {
-        uint32_t *reg = mine + (g * CPW + c) * kCoalDwords;
+        uint32_t *reg = mine + ((g * CPW + c) % kCoalRegions) * kCoalDwords;
         u32x4_a4 *dst = reinterpret_cast<u32x4_a4 *>(reg);
 #pragma unroll
         for (int k = 0; k < 4; ++k) dst[64 * k + lane] = ch[g][c][k];
@@ -751,20 +760,20 @@ struct ListArgs {
 template <int LPR, int WPR, int CPW, int RG, class XS>
 __device__ __forceinline__ void list_tile(const MatvecArgs &m, int64_t tile, XS &xs,
                                           uint32_t *wst) {
-  if constexpr (coal_body(LPR, RG, CPW))
+  if constexpr (coal_list_body(LPR, WPR, RG, CPW))
     matvec_body<LPR, WPR, CPW, RG, false, false, XS, false, true>(m, tile, m.w, nullptr,
                                                                   m.n_items, xs, nullptr, wst);
   else
     matvec_body<LPR, WPR, CPW, RG, false, false>(m, tile, m.w, nullptr, m.n_items, xs);
 }
 
-// Row shapes with one 64-pair chunk per wave take one or two row groups per
-// wave slot; two-chunk rows take one, which keeps every body within two
-// coalesced-staging regions per wave.
+// Row shapes with one 64-pair chunk per wave, and 32768-wide rows (four
+// waves of two chunks), take one or two row groups per wave slot; the other
+// two-chunk shapes take one.
 template <int LPR, int WPR, int CPW, class XS>
 __device__ __forceinline__ void list_tile_rg(int rg, const MatvecArgs &m, int64_t tile, XS &xs,
                                              uint32_t *wst) {
-  if constexpr (CPW == 1) {
+  if constexpr (CPW == 1 || (CPW == 2 && WPR == 4)) {
     if (rg == 2) {
       list_tile<LPR, WPR, CPW, 2>(m, tile, xs, wst);
       return;
@@ -797,7 +806,11 @@ __device__ __forceinline__ void list_dispatch(int code, int rg, const MatvecArgs
   }
 }
 
-__global__ __launch_bounds__(256) void matvec_list_kernel(const ListArgs a) {
+// Held to 128 VGPRs, four waves per SIMD, as many as its LDS allows: the
+// two-row-group body of 32768-wide rows would otherwise take 146 and cost
+// every item of the launch a wave (decode5 from x_q 11.0 -> 10.75 us with it).
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8))) void matvec_list_kernel(
+    const ListArgs a) {
   __shared__ uint32_t xbuf[kFusePairs * kPairDwords];
   __shared__ __attribute__((aligned(16))) uint32_t wst[kCoalLdsDwords];
   // The item of this workgroup: the last one whose first tile is at or below
@@ -1112,11 +1125,10 @@ hipError_t launch_matvec_list(const ListItem *items, int n_items, int64_t n_tok,
     d.out_dim = src.out_dim;
     d.nb = src.in_dim / kBlockElems;
     // Two row groups per wave slot where the item alone still fills 1024
-    // workgroups: fewer, fuller workgroups stay resident in one round.  Rows
-    // of two chunks per wave (in_dim 32768) keep one row group, so that their
-    // weights take the coalesced staging (at most two regions per wave):
-    // decode5 17.1 -> 15.1 us against two row groups with per-lane loads.
-    const bool two = sh.chunks_per_wave == 1;
+    // workgroups (256 for 32768-wide rows): fewer, fuller workgroups stay
+    // resident in one round, and a 32768-wide x row is read once per two
+    // weight rows instead of once per row (decode5 from x_q 11.0 -> 10.75 us).
+    const bool two = sh.chunks_per_wave == 1 || (sh.chunks_per_wave == 2 && sh.waves_per_row == 4);
     const int rg = (two && choose_rg(sh, src.out_dim, 1) >= 2) ? 2 : 1;
     d.shape = code;
     d.rg = rg;

@@ -147,6 +147,16 @@ def test_list_ragged_rows_every_shape(out_dim):
     _run(specs[8:], 1, f"ragged{out_dim}b")
 
 
+@pytest.mark.parametrize("out_dim,n_tok", [(513, 1), (1023, 2), (1024, 5)])
+def test_list_wide_rows_two_row_groups(out_dim, n_tok):
+    # 32768-wide rows take two row groups per workgroup from 511 rows on, their
+    # four chunks per wave passing through the wave's two staging regions in
+    # turn; an odd row count leaves the last workgroup's second row past the end.
+    specs = [dict(in_dim=32768, out_dim=out_dim, mode="xq"),
+             dict(in_dim=4096, out_dim=300, mode="x+xq")]
+    _run(specs, n_tok, f"wide{out_dim}x{n_tok}")
+
+
 def test_list_sixteen_items():
     dims = [64, 128, 256, 512, 1024, 2048, 4096, 4096, 1024, 512, 256, 128, 64, 2048, 1024, 8192]
     specs = [dict(in_dim=k, out_dim=37 + 5 * i, mode=("x", "x+xq", "xq")[i % 3] if k <= 4096 else "xq")
