@@ -186,6 +186,22 @@ def bench_decode5(torch, q8, wl, steps, warmup):
 
     sec, done = time_steps(torch, step, steps, warmup, per_graph=rot)
     sec_sep, _ = time_steps(torch, step_separate, steps, warmup, per_graph=rot)
+
+    # The five matmuls from x_q in one list launch, the quantizer reported
+    # separately (five launches, one per x row).
+    for j in range(len(dims)):
+        q8.q8_0_quantize_act(xs[j], out=xqs[j])
+    qlists = [[dict(out=outs[j], w=wq[c][j], x_q=xqs[j], in_dim=k, out_dim=n)
+               for j, (k, n) in enumerate(dims)] for c in range(rot)]
+    sec_xq, _ = time_steps(torch, lambda i: q8.q8_0_matmul_list(qlists[i % rot], 1), steps, warmup,
+                           per_graph=rot)
+    list_xq_us = time_kernel(torch, lambda i: q8.q8_0_matmul_list(qlists[i % rot], 1), rot)
+
+    def quantize_all(i):
+        for j in range(len(dims)):
+            q8.q8_0_quantize_act(xs[j], out=xqs[j])
+
+    quant_us = time_kernel(torch, quantize_all, rot)
     per = []
     for j, (k, n) in enumerate(dims):
         us = time_kernel(torch, lambda i, j=j, k=k, n=n: q8.q8_0_matmul(wq[i % rot][j], xqs[j], k, n, 1,
@@ -194,8 +210,10 @@ def bench_decode5(torch, q8, wl, steps, warmup):
                         kernel_bytes=n * row_bytes(k) + row_bytes(k) + 4 * n))
     w_bytes = sum(n * row_bytes(k) for k, n in dims)
     step_bytes = w_bytes + sum(4 * k + 4 * n for k, n in dims)  # W + fp32 x + out
+    xq_bytes = w_bytes + sum(row_bytes(k) + 4 * n for k, n in dims)  # W + x_q + out
     return dict(sec=sec, sec_separate=sec_sep, step_bytes=step_bytes, w_bytes=w_bytes,
-                per_matrix=per)
+                per_matrix=per, sec_xq=sec_xq, list_xq_us=list_xq_us, xq_bytes=xq_bytes,
+                quant_us=quant_us)
 
 
 def bench_router_shared(torch, q8, wl, steps, warmup):
@@ -528,6 +546,16 @@ def main():
             "ms_per_step": round(d5["sec"] * 1e3, 5),
             "frac_hbm": round(d5["step_bytes"] / d5["sec"] / 1e9 / HBM_PEAK_GBS, 4),
             "separate_calls_ms_per_step": round(d5["sec_separate"] * 1e3, 5),
+            "from_x_q": {
+                "what": "the five matmuls from x_q in one list launch (quantizer below, separately)",
+                "GBs": round(d5["xq_bytes"] / d5["sec_xq"] / 1e9, 1),
+                "ms_per_step": round(d5["sec_xq"] * 1e3, 5),
+                "frac_hbm": round(d5["xq_bytes"] / d5["sec_xq"] / 1e9 / HBM_PEAK_GBS, 4),
+                "list_kernel_us": round(d5["list_xq_us"], 3),
+                "list_kernel_frac_hbm": round(d5["xq_bytes"] / (d5["list_xq_us"] * 1e-6) / 1e9
+                                              / HBM_PEAK_GBS, 4),
+                "bytes": d5["xq_bytes"],
+                "quantize_five_rows_us": round(d5["quant_us"], 3)},
             "per_matrix_q8_0_matmul": [
                 {"name": p["name"], "kernel_us": round(p["kernel_us"], 3),
                  "GBs": round(p["kernel_bytes"] / (p["kernel_us"] * 1e-6) / 1e9, 1)}
