@@ -265,6 +265,39 @@ def _run_outputs(wq, xq, wq_o, xq_o, in_dim, out_dim, n_tok, split, where):
     return got.cpu().numpy(), ref
 
 
+def _at_offset(t, off):
+    """A copy of uint8 tensor t whose data starts `off` bytes into a larger buffer."""
+    buf = torch.zeros(t.numel() + 64, dtype=torch.uint8, device=t.device)
+    v = buf[off:off + t.numel()].view(t.shape)
+    v.copy_(t)
+    return v
+
+
+@pytest.mark.parametrize("out_dim,n_tok,in_dim", [
+    (256, 256, 512),     # whole tiles: the four-tile kernel when 16-byte aligned
+    (300, 150, 1152),    # ragged: the direct-copy tiled kernel when aligned
+    (512, 40, 1024),     # the skinny kernel (16-byte or dword copies)
+    (1024, 1, 32768),    # single-token matvec, coalesced x chunks
+    (1024, 5, 4096)])    # several tokens, staged x rows
+def test_operands_at_4_byte_offsets(out_dim, n_tok, in_dim):
+    # w and x_q 4 bytes into larger buffers: the kernels that copy 16-byte
+    # chunks must not take them.  The auto plan's result is checked against
+    # the oracle, and against the same call on the aligned copies.
+    q8 = _q8()
+    w = workloads.normal((out_dim, in_dim), 0.02, "cuda", "off4", out_dim, in_dim, "w")
+    x = workloads.normal((n_tok, in_dim), 1.0, "cuda", "off4", n_tok, in_dim, "x")
+    wq, xq, wq_o, xq_o = _prep(w, x)
+    wq4, xq4 = _at_offset(wq, 4), _at_offset(xq, 4)
+    assert wq4.data_ptr() % 16 == 4 and xq4.data_ptr() % 16 == 4
+    say(f"[matmul] offset4 in={in_dim} out={out_dim} n_tok={n_tok}")
+    got = q8.q8_0_matmul(wq4, xq4, in_dim, out_dim, n_tok)
+    aligned = q8.q8_0_matmul(wq, xq, in_dim, out_dim, n_tok)
+    torch.cuda.synchronize()
+    ref, mag, _ = oracle.matmul(wq_o, xq_o, in_dim)
+    assert_close(got.cpu().numpy(), ref, mag, f"offset4 {out_dim}x{n_tok}x{in_dim}")
+    assert_close(aligned.cpu().numpy(), ref, mag, f"aligned {out_dim}x{n_tok}x{in_dim}")
+
+
 @pytest.mark.parametrize("out_dim,n_tok,in_dim,split", [
     (256, 256, 512, 1), (384, 128, 1152, 3), (128, 384, 4096, 1), (256, 128, 2048, 4),
     (512, 128, 128, 1), (768, 256, 384, 1), (1024, 128, 640, 1), (256, 256, 1024, 2)])
