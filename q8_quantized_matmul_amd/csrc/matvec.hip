@@ -448,8 +448,13 @@ __device__ __forceinline__ void matvec_body(const MatvecArgs &a, int64_t tile, c
       const int64_t lrow = row < a.out_dim ? row : a.out_dim - 1;
 #pragma unroll
       for (int c = 0; c < CPW; ++c) {
-        load_pair(w + lrow * a.row_bytes + pair_of[c] * kPairBytes, wr[0][g][c]);
-        if constexpr (PAIR) load_pair(w2 + lrow * a.row_bytes + pair_of[c] * kPairBytes, wr[NM - 1][g][c]);
+        if constexpr (GROUPED) {
+          load_pair_global(w + lrow * a.row_bytes + pair_of[c] * kPairBytes, wr[0][g][c]);
+          if constexpr (PAIR)
+            load_pair_global(w2 + lrow * a.row_bytes + pair_of[c] * kPairBytes, wr[NM - 1][g][c]);
+        } else {
+          load_pair(w + lrow * a.row_bytes + pair_of[c] * kPairBytes, wr[0][g][c]);
+        }
       }
     }
     xs.publish();

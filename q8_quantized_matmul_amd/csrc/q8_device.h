@@ -25,13 +25,28 @@ __device__ __forceinline__ float f16_bits_to_f32(uint32_t bits) {
   return (float)__builtin_bit_cast(_Float16, (uint16_t)(bits & 0xFFFFu));
 }
 
-// Load the 17 dwords of a block pair (68 bytes, dword aligned) from global
-// memory.  The pointer is taken as a global one explicitly: a base read from a
-// device table (the grouped kernels' expert weights) would otherwise load
-// with flat instructions, which also count on the LDS/scalar wait counter.
+// Load the 17 dwords of a block pair (68 bytes, dword aligned).
+__device__ __forceinline__ void load_pair(const uint8_t *p, uint32_t (&d)[kPairDwords]) {
+  const u32x4_a4 *v = reinterpret_cast<const u32x4_a4 *>(p);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    u32x4_a4 t = v[i];
+    d[4 * i + 0] = t.x;
+    d[4 * i + 1] = t.y;
+    d[4 * i + 2] = t.z;
+    d[4 * i + 3] = t.w;
+  }
+  d[16] = reinterpret_cast<const uint32_t *>(p)[16];
+}
+
+// The same through a pointer taken as global memory explicitly.  For bases
+// read from a device table (the grouped kernels' expert weights) the compiler
+// would otherwise emit flat loads, which also count on the LDS/scalar wait
+// counter.  Only the grouped kernels use it: elsewhere the pointers are kernel
+// arguments, already known to be global.
 typedef __attribute__((address_space(1))) const u32x4_a4 global_u32x4_a4;
 typedef __attribute__((address_space(1))) const uint32_t global_u32;
-__device__ __forceinline__ void load_pair(const uint8_t *p, uint32_t (&d)[kPairDwords]) {
+__device__ __forceinline__ void load_pair_global(const uint8_t *p, uint32_t (&d)[kPairDwords]) {
   global_u32x4_a4 *v = (global_u32x4_a4 *)p;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
