@@ -74,15 +74,29 @@ __global__ __launch_bounds__(256) void quantize_pair_kernel(const float *__restr
         __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(x + row * in_dim + p * 64 + sub * 4));
     v[u] = make_float4(t.x, t.y, t.z, t.w);
   }
+  // The workgroup's 16 U pairs are consecutive bytes of x_q: they are
+  // gathered in LDS and written with one coalesced dword per lane and store
+  // (256 contiguous bytes per wave instruction) instead of one 64-byte run
+  // per pair and store.  On the prefill_b input the fastest launch went from
+  // 55.2 to 52.9 us (rocprofv3, one box).  Pairs past the end are quantized
+  // (their loads re-read the last pair) but not stored.
+  constexpr int NP = 16 * U;
+  __shared__ uint32_t stage[NP * kPairDwords];
 #pragma unroll
   for (int u = 0; u < U; ++u) {
-    const int64_t pair = first + 16 * u;
+    const int lp = (int)(threadIdx.x >> 4) + 16 * u;  // pair within the workgroup
     const PairWords pw = quantize_pair16(v[u], sub);  // every lane takes part (DPP)
-    if (pair < total_pairs) {                          // uniform over the 16 lanes
-      uint32_t *dst = reinterpret_cast<uint32_t *>(xq + pair * kPairBytes);
-      __builtin_nontemporal_store(pw.hi, dst + sub + 1);
-      if (sub == 0) __builtin_nontemporal_store(pw.lo, dst);
-    }
+    stage[lp * kPairDwords + sub + 1] = pw.hi;
+    if (sub == 0) stage[lp * kPairDwords] = pw.lo;
+  }
+  __syncthreads();
+  const int64_t p0 = (int64_t)blockIdx.x * NP;
+  const int64_t valid = min((int64_t)NP, total_pairs - p0) * kPairDwords;  // dwords to store
+  uint32_t *dst = reinterpret_cast<uint32_t *>(xq + p0 * kPairBytes);
+#pragma unroll
+  for (int k = 0; k < (NP * kPairDwords + 255) / 256; ++k) {
+    const int d = 256 * k + (int)threadIdx.x;
+    if (d < valid) __builtin_nontemporal_store(stage[d], dst + d);
   }
 }
 
