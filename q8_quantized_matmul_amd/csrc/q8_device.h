@@ -136,6 +136,8 @@ struct PairWords {
 constexpr int kDppXor1 = 0xB1;
 constexpr int kDppXor2 = 0x4E;
 constexpr int kDppHalfMirror = 0x141;
+constexpr int kDppRowRor4 = 0x124;  // the 16-lane row rotated by 4 lanes
+constexpr int kDppRowRor8 = 0x128;  // ... and by 8 lanes
 constexpr int kDppNext = 0x101;
 constexpr int kDppMirror = 0x140;    // lane 15-i of the same 16-lane row
 constexpr int kDppBcast15 = 0x142;   // lane 15 of the previous row
