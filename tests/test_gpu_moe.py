@@ -65,6 +65,28 @@ def test_moe_small(in_dim, out_dim, n_expert, n_tok, n_used, x_rows):
     assert torch.equal(got, got2)
 
 
+@pytest.mark.parametrize("in_dim,out_dim,n_expert,x_rows", [(4096, 1029, 16, 0), (2048, 2051, 16, 1)])
+def test_moe_four_row_groups_ragged(in_dim, out_dim, n_expert, x_rows):
+    # Enough tiles for four row groups per wave slot, whose four row sums per
+    # lane are reduced together (64-lane rows at in_dim 4096, 32-lane rows at
+    # 2048); the row counts leave a ragged last tile.
+    q8 = _q8()
+    n_tok, n_used = 8, 4
+    wq, sel, xq, wq_o, xq_o = _small_case(in_dim, out_dim, n_expert, n_tok, n_used, in_dim + out_dim,
+                                          x_rows)
+    table = q8.expert_table(wq)
+    say(f"[moe] four row groups in={in_dim} out={out_dim} E={n_expert} x_rows={x_rows}")
+    out = torch.full((n_tok, n_used, out_dim), float("nan"), device="cuda")
+    got, _ = q8.q8_0_moe_grouped(table, n_expert, sel.cuda(), xq, in_dim, out_dim, x_rows, out=out)
+    torch.cuda.synchronize()
+    ref, mag, bad = oracle.moe_grouped(wq_o, sel.numpy(), xq_o, in_dim, out_dim, x_rows)
+    assert bad == 0
+    assert_close(got.cpu().numpy(), ref, mag, "moe four row groups")
+    got2, _ = q8.q8_0_moe_grouped(table, n_expert, sel.cuda(), xq, in_dim, out_dim, x_rows)
+    torch.cuda.synchronize()
+    assert torch.equal(got, got2)
+
+
 def test_moe_invalid_ids_and_duplicates():
     q8 = _q8()
     in_dim, out_dim, n_expert, n_tok, n_used = 512, 48, 6, 7, 3
