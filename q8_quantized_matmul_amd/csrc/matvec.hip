@@ -159,12 +159,14 @@ struct StagedX {
   }
 };
 
-// x rows per staging buffer: as many as fit in about 20 KB of LDS, 1 to 16.
-template <int LPR, int WPR, int CPW>
+// x rows per staging buffer: as many as fit in about 20 KB of LDS, 1 to 16;
+// with SMALL (the grouped kernels, which also stage their weights through
+// 17 KB of LDS) about 8.5 KB, so that four workgroups fit a CU.
+template <int LPR, int WPR, int CPW, bool SMALL = false>
 struct StagedShape {
   static constexpr int ROW_DW = kPairDwords * (LPR < 64 ? LPR : 64 * WPR * CPW);
   static constexpr int STRIDE = (ROW_DW + 63) / 64 * 64;
-  static constexpr int XT_RAW = 20480 / (4 * STRIDE);
+  static constexpr int XT_RAW = (SMALL ? 8704 : 20480) / (4 * STRIDE);
   static constexpr int XT = XT_RAW < 1 ? 1 : (XT_RAW > 16 ? 16 : XT_RAW);
   using X = StagedX<ROW_DW, XT>;
 };
@@ -386,38 +388,52 @@ __device__ __forceinline__ void matvec_body(const MatvecArgs &a, int64_t tile, c
   xs.prefetch();
   uint32_t wr[NM][RG][CPW][kPairDwords];
   if constexpr (COAL) {
-    static_assert(!PAIR && coal_list_body(LPR, WPR, RG, CPW), "coalesced weight staging");
-    // A wave's 64 pairs of one (row group, chunk) are 4352 contiguous bytes:
-    // RPW whole rows, or one 64-pair chunk of a row.  Lane l loads 16-byte
-    // chunks l, l + 64, l + 128, l + 192 and then dword 1024 + l, so every
-    // lane issues the same five loads.  Loads of a region that reaches past
-    // the last row are clamped to the matrix's last bytes: what they bring
-    // feeds only outputs that are not stored, and nothing is read outside the
-    // matrix.  The loads go to registers (not direct to LDS) and nothing
-    // branches between them and the earlier x loads, so waiting for x does
-    // not wait for the weights.  Region (g * CPW + c) mod kCoalRegions takes
-    // the chunk; a region is rewritten only after the wave's reads of it.
+    static_assert(GROUPED || (!PAIR && coal_list_body(LPR, WPR, RG, CPW)), "coalesced weight staging");
+    // A wave's 64 pairs of one (matrix, row group, chunk) are 4352 contiguous
+    // bytes: RPW whole rows, or one 64-pair chunk of a row.  Lane l loads
+    // 16-byte chunks l, l + 64, l + 128, l + 192 and then dword 1024 + l, so
+    // every lane issues the same five loads.  Loads of a region that reaches
+    // past the last row are clamped to the matrix's last bytes: what they
+    // bring feeds only outputs that are not stored, and nothing is read
+    // outside the matrix.  The loads go to registers (not direct to LDS) and
+    // nothing branches between them and the earlier x loads, so waiting for x
+    // does not wait for the weights.  The chunks pass through the wave's
+    // NREG regions in turn (one per wave in the grouped kernels, which also
+    // stage their x rows in LDS); a region is rewritten only after the
+    // wave's reads of it.  The grouped kernels' weight bases come from the
+    // device table, so their loads go through global pointers explicitly.
+    constexpr int NREG = GROUPED ? 1 : kCoalRegions;
     const int wave_u = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     const int64_t rb0 = tile * TILE_ROWS + (wave_u / WPR) * ROWS_PER_SLOT;
-    uint32_t *mine = wst + wave_u * (kCoalRegions * kCoalDwords);
-    const uint8_t *wend = w + a.out_dim * a.row_bytes;
-    u32x4_a4 ch[RG][CPW][4];
-    uint32_t tail[RG][CPW];
+    uint32_t *mine = wst + wave_u * (NREG * kCoalDwords);
+    u32x4_a4 ch[NM][RG][CPW][4];
+    uint32_t tail[NM][RG][CPW];
 #pragma unroll
-    for (int g = 0; g < RG; ++g) {
+    for (int m = 0; m < NM; ++m) {
+      const uint8_t *wm = m == 0 ? w : w2;
+      const uint8_t *wend = wm + a.out_dim * a.row_bytes;
 #pragma unroll
-      for (int c = 0; c < CPW; ++c) {
-        const int64_t chunk0 = LPR < 64 ? 0 : (int64_t)(c * WPR + (wave_u % WPR)) * 64;
-        const uint8_t *src = w + (rb0 + g * RPW) * a.row_bytes + chunk0 * kPairBytes;
+      for (int g = 0; g < RG; ++g) {
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const uint8_t *p = src + 16 * (64 * k + lane);
-          ch[g][c][k] = __builtin_nontemporal_load(
-              reinterpret_cast<const u32x4_a4 *>(p < wend - 16 ? p : wend - 16));
+        for (int c = 0; c < CPW; ++c) {
+          const int64_t chunk0 = LPR < 64 ? 0 : (int64_t)(c * WPR + (wave_u % WPR)) * 64;
+          const uint8_t *src = wm + (rb0 + g * RPW) * a.row_bytes + chunk0 * kPairBytes;
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            const uint8_t *q = src + 16 * (64 * k + lane);
+            q = q < wend - 16 ? q : wend - 16;
+            if constexpr (GROUPED)
+              ch[m][g][c][k] = __builtin_nontemporal_load((global_u32x4_a4 *)q);
+            else
+              ch[m][g][c][k] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_a4 *>(q));
+          }
+          const uint8_t *q = src + 4096 + 4 * lane;
+          q = q < wend - 4 ? q : wend - 4;
+          if constexpr (GROUPED)
+            tail[m][g][c] = __builtin_nontemporal_load((global_u32 *)q);
+          else
+            tail[m][g][c] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t *>(q));
         }
-        const uint8_t *p = src + 4096 + 4 * lane;
-        tail[g][c] = __builtin_nontemporal_load(
-            reinterpret_cast<const uint32_t *>(p < wend - 4 ? p : wend - 4));
       }
     }
     xs.publish();
@@ -427,18 +443,21 @@ __device__ __forceinline__ void matvec_body(const MatvecArgs &a, int64_t tile, c
     // run in order, so no barrier is needed; the fences keep the compiler
     // from moving a region's next writes above its reads.
 #pragma unroll
-    for (int g = 0; g < RG; ++g) {
+    for (int m = 0; m < NM; ++m) {
 #pragma unroll
-      for (int c = 0; c < CPW; ++c) {
-        uint32_t *reg = mine + ((g * CPW + c) % kCoalRegions) * kCoalDwords;
-        u32x4_a4 *dst = reinterpret_cast<u32x4_a4 *>(reg);
+      for (int g = 0; g < RG; ++g) {
 #pragma unroll
-        for (int k = 0; k < 4; ++k) dst[64 * k + lane] = ch[g][c][k];
-        reg[1024 + lane] = tail[g][c];
-        __builtin_amdgcn_wave_barrier();
-        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        for (int c = 0; c < CPW; ++c) {
+          uint32_t *reg = mine + (((m * RG + g) * CPW + c) % NREG) * kCoalDwords;
+          u32x4_a4 *dst = reinterpret_cast<u32x4_a4 *>(reg);
 #pragma unroll
-        for (int i = 0; i < kPairDwords; ++i) wr[0][g][c][i] = reg[kPairDwords * lane + i];
+          for (int k = 0; k < 4; ++k) dst[64 * k + lane] = ch[m][g][c][k];
+          reg[1024 + lane] = tail[m][g][c];
+          __builtin_amdgcn_wave_barrier();
+          __atomic_signal_fence(__ATOMIC_SEQ_CST);
+#pragma unroll
+          for (int i = 0; i < kPairDwords; ++i) wr[m][g][c][i] = reg[kPairDwords * lane + i];
+        }
       }
     }
   } else {
@@ -605,10 +624,21 @@ __global__ __launch_bounds__(256) void matvec_kernel(const MatvecArgs a) {
     items = a.pairs + a.offsets[e];
   }
   if constexpr (STAGED) {
-    using SX = typename StagedShape<LPR, WPR, CPW>::X;
+    // Grouped launches stage their weights coalesced too, through one LDS
+    // region per wave, beside a smaller x buffer (four workgroups per CU):
+    // moe gate projection 335 -> 305 us, down 328 -> 302 us against per-lane
+    // pair loads (one box).
+    constexpr bool GCOAL = GROUPED && LPR >= 4;
+    using SX = typename StagedShape<LPR, WPR, CPW, GCOAL>::X;
     __shared__ __attribute__((aligned(16))) uint32_t xbuf[2 * SX::BUF];
     SX xs{xbuf, a.x_q, a.row_bytes, items, n_items, (uint32_t)a.n_used, a.x_rows};
-    matvec_body<LPR, WPR, CPW, RG, GROUPED, STORE_S>(a, blockIdx.x, w, items, n_items, xs);
+    if constexpr (GCOAL) {
+      __shared__ __attribute__((aligned(16))) uint32_t wst[4 * kCoalDwords];
+      matvec_body<LPR, WPR, CPW, RG, GROUPED, STORE_S, SX, false, true>(a, blockIdx.x, w, items,
+                                                                       n_items, xs, nullptr, wst);
+    } else {
+      matvec_body<LPR, WPR, CPW, RG, GROUPED, STORE_S>(a, blockIdx.x, w, items, n_items, xs);
+    }
   } else if constexpr (!GROUPED && coal_body(LPR, RG, CPW)) {
     __shared__ __attribute__((aligned(16))) uint32_t wst[kCoalLdsDwords];
     GlobalXFirst xs{{a.x_q, a.row_bytes}};
@@ -630,12 +660,19 @@ __global__ __launch_bounds__(256) void matvec_pair_kernel(const MatvecArgs a) {
   const int e = blockIdx.y;
   const int64_t n_items = a.counts[e];
   if (n_items == 0) return;  // uniform across the workgroup
-  using SX = typename StagedShape<LPR, WPR, CPW>::X;
+  constexpr bool GCOAL = LPR >= 4;  // weights staged coalesced, as in the grouped kernel
+  using SX = typename StagedShape<LPR, WPR, CPW, GCOAL>::X;
   __shared__ __attribute__((aligned(16))) uint32_t xbuf[2 * SX::BUF];
   const int32_t *items = a.pairs + a.offsets[e];
   SX xs{xbuf, a.x_q, a.row_bytes, items, n_items, (uint32_t)a.n_used, a.x_rows};
-  matvec_body<LPR, WPR, CPW, RG, true, false, SX, true>(a, blockIdx.x, a.expert_w[e], items,
-                                                        n_items, xs, a.expert_w2[e]);
+  if constexpr (GCOAL) {
+    __shared__ __attribute__((aligned(16))) uint32_t wst[4 * kCoalDwords];
+    matvec_body<LPR, WPR, CPW, RG, true, false, SX, true, true>(a, blockIdx.x, a.expert_w[e], items,
+                                                                n_items, xs, a.expert_w2[e], wst);
+  } else {
+    matvec_body<LPR, WPR, CPW, RG, true, false, SX, true>(a, blockIdx.x, a.expert_w[e], items,
+                                                          n_items, xs, a.expert_w2[e]);
+  }
 }
 
 // ---- generic fallback: one wave per (token, row), lanes stride over blocks.
