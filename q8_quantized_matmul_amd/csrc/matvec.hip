@@ -100,6 +100,7 @@ struct GlobalXFirst : GlobalX {};
 // dwords, the lanes past a row's end re-read its last dword into the padding.
 template <int ROW_DW, int XT>
 struct StagedX {
+  static constexpr bool kStaged = true;  // weights, if coalesced, use one region per wave
   static constexpr int STRIDE = (ROW_DW + 63) / 64 * 64;
   static constexpr int NI = STRIDE / 64;
   static constexpr int BUF = XT * STRIDE;  // dwords per buffer
@@ -388,7 +389,8 @@ __device__ __forceinline__ void matvec_body(const MatvecArgs &a, int64_t tile, c
   xs.prefetch();
   uint32_t wr[NM][RG][CPW][kPairDwords];
   if constexpr (COAL) {
-    static_assert(GROUPED || (!PAIR && coal_list_body(LPR, WPR, RG, CPW)), "coalesced weight staging");
+    static_assert(GROUPED || requires { XS::kStaged; } || (!PAIR && coal_list_body(LPR, WPR, RG, CPW)),
+                  "coalesced weight staging");
     // A wave's 64 pairs of one (matrix, row group, chunk) are 4352 contiguous
     // bytes: RPW whole rows, or one 64-pair chunk of a row.  Lane l loads
     // 16-byte chunks l, l + 64, l + 128, l + 192 and then dword 1024 + l, so
@@ -398,11 +400,11 @@ __device__ __forceinline__ void matvec_body(const MatvecArgs &a, int64_t tile, c
     // outside the matrix.  The loads go to registers (not direct to LDS) and
     // nothing branches between them and the earlier x loads, so waiting for x
     // does not wait for the weights.  The chunks pass through the wave's
-    // NREG regions in turn (one per wave in the grouped kernels, which also
-    // stage their x rows in LDS); a region is rewritten only after the
+    // NREG regions in turn (one per wave where the x rows are staged in LDS
+    // too); a region is rewritten only after the
     // wave's reads of it.  The grouped kernels' weight bases come from the
     // device table, so their loads go through global pointers explicitly.
-    constexpr int NREG = GROUPED ? 1 : kCoalRegions;
+    constexpr int NREG = (GROUPED || requires { XS::kStaged; }) ? 1 : kCoalRegions;
     const int wave_u = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     const int64_t rb0 = tile * TILE_ROWS + (wave_u / WPR) * ROWS_PER_SLOT;
     uint32_t *mine = wst + wave_u * (NREG * kCoalDwords);
@@ -627,9 +629,12 @@ __global__ __launch_bounds__(256) void matvec_kernel(const MatvecArgs a) {
     // Grouped launches stage their weights coalesced too, through one LDS
     // region per wave, beside a smaller x buffer (four workgroups per CU):
     // moe gate projection 335 -> 305 us, down 328 -> 302 us against per-lane
-    // pair loads (one box).
-    constexpr bool GCOAL = GROUPED && LPR >= 4;
-    using SX = typename StagedShape<LPR, WPR, CPW, GCOAL>::X;
+    // pair loads (one box).  Plain staged launches (2..11 tokens) do so for
+    // 32768-wide rows, whose x buffer holds one row either way: 32768 -> 1024
+    // at 2 / 4 / 8 tokens 13.4 / 17.5 / 25.6 -> 12.6 / 16.5 / 24.7 us; at
+    // in_dim 1024 and 4096 it measured slower from four tokens on.
+    constexpr bool GCOAL = LPR >= 4 && (GROUPED || (LPR == 64 && WPR == 4 && CPW == 2));
+    using SX = typename StagedShape<LPR, WPR, CPW, GROUPED && GCOAL>::X;
     __shared__ __attribute__((aligned(16))) uint32_t xbuf[2 * SX::BUF];
     SX xs{xbuf, a.x_q, a.row_bytes, items, n_items, (uint32_t)a.n_used, a.x_rows};
     if constexpr (GCOAL) {
