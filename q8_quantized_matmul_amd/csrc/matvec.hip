@@ -1214,8 +1214,12 @@ hipError_t launch_matvec_list(const ListItem *items, int n_items, int64_t n_tok,
     // workgroups (256 for 32768-wide rows): fewer, fuller workgroups stay
     // resident in one round, and a 32768-wide x row is read once per two
     // weight rows instead of once per row (decode5 from x_q 11.0 -> 10.75 us).
+    // Items quantized in the launch take two from 256 rows on: every
+    // workgroup reads the whole fp32 row, so fuller workgroups halve those
+    // reads (router + shared gate/up 7.87 -> 7.42 us; decode5 unchanged).
     const bool two = sh.chunks_per_wave == 1 || (sh.chunks_per_wave == 2 && sh.waves_per_row == 4);
-    const int rg = (two && choose_rg(sh, src.out_dim, 1) >= 2) ? 2 : 1;
+    const bool fused_two = src.x && sh.chunks_per_wave == 1 && src.out_dim >= 256;
+    const int rg = (two && (fused_two || choose_rg(sh, src.out_dim, 1) >= 2)) ? 2 : 1;
     d.shape = code;
     d.rg = rg;
     d.first_tile = (int32_t)tiles;
