@@ -342,6 +342,28 @@ int q8_0_probe_mfma_i8(int32_t iters, uint32_t *sink, hipStream_t stream);
  * Q8_0_EINVAL. */
 int q8_0_probe_mfma_mix(int32_t iters, int32_t mix, uint32_t *sink, hipStream_t stream);
 
+/* Debug aid of the race tests (a kernel that reads LDS it has not written,
+ * or reads it before the barrier that publishes it, computes from whatever
+ * the LDS held; the pages record such bugs -- a barrier of too narrow a scope,
+ * "Part 6: GPU 加速", section 4n, and threadgroup memory allocated too small,
+ * caught by a debug layer, section 4p): fills the whole LDS of every compute
+ * unit with `pattern`, so that the next launch on `stream` starts with every
+ * LDS byte holding it.  Running a kernel after two different patterns and
+ * comparing its outputs bit for bit shows whether it reads unwritten LDS.
+ * Stream-ordered; allocates nothing.  Errors: no device -> Q8_0_ENODEV. */
+int q8_0_debug_poison_lds(uint32_t pattern, hipStream_t stream);
+
+/* LDS dwords each workgroup of q8_0_debug_read_lds copies out. */
+#define Q8_0_DEBUG_LDS_DWORDS 8192
+
+/* The check that q8_0_debug_poison_lds reaches later launches: `workgroups`
+ * workgroups each copy the Q8_0_DEBUG_LDS_DWORDS dwords of LDS they were
+ * given, without writing them first, to seen[w * Q8_0_DEBUG_LDS_DWORDS ...].
+ *   seen      : device uint32, workgroups * Q8_0_DEBUG_LDS_DWORDS, written.
+ *   workgroups: 1 .. 4096.
+ * Errors: null or unaligned seen, workgroups out of range -> Q8_0_EINVAL. */
+int q8_0_debug_read_lds(uint32_t *seen, int32_t workgroups, hipStream_t stream);
+
 /* Static description of a status code. */
 const char *q8_0_strerror(int status);
 

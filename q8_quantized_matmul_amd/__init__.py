@@ -85,6 +85,8 @@ _sig = {
     "q8_0_probe_launch": ([_i32, _vp, _vp], ctypes.c_int),
     "q8_0_probe_mfma_i8": ([_i32, _vp, _vp], ctypes.c_int),
     "q8_0_probe_mfma_mix": ([_i32, _i32, _vp, _vp], ctypes.c_int),
+    "q8_0_debug_poison_lds": ([ctypes.c_uint32, _vp], ctypes.c_int),
+    "q8_0_debug_read_lds": ([_vp, _i32, _vp], ctypes.c_int),
     "q8_0_strerror": ([ctypes.c_int], ctypes.c_char_p),
 }
 for _name, (_args, _res) in _sig.items():
@@ -224,7 +226,8 @@ def q8_0_moe_workspace_bytes(n_tok: int, n_used: int, n_expert: int) -> int:
 
 def expert_table(mats) -> torch.Tensor:
     """Device int64 table of expert weight base pointers from a list of tensors
-    (or from one stacked [n_expert, ...] tensor)."""
+    (or from one stacked [n_expert, ...] tensor).  The table holds raw device
+    addresses: the tensors must stay alive as long as the table is used."""
     if isinstance(mats, torch.Tensor):
         base = mats.data_ptr()
         stride = mats[0].numel() * mats.element_size()
@@ -353,3 +356,20 @@ def q8_0_probe_mfma_mix(iters: int, mix: int, sink: torch.Tensor) -> None:
     PROBE_MFMA_OPS_PER_ITER."""
     _check(_lib.q8_0_probe_mfma_mix(int(iters), int(mix), _dev(sink, "sink"), _stream()),
            "q8_0_probe_mfma_mix")
+
+
+DEBUG_LDS_DWORDS = 8192  # Q8_0_DEBUG_LDS_DWORDS
+
+
+def q8_0_debug_poison_lds(pattern: int) -> None:
+    """Fill every compute unit's LDS with the 32-bit pattern (race tests)."""
+    _check(_lib.q8_0_debug_poison_lds(int(pattern) & 0xFFFFFFFF, _stream()),
+           "q8_0_debug_poison_lds")
+
+
+def q8_0_debug_read_lds(seen: torch.Tensor, workgroups: int) -> None:
+    """Copy the unwritten LDS of `workgroups` workgroups into seen (int32,
+    workgroups * DEBUG_LDS_DWORDS elements)."""
+    assert seen.numel() * seen.element_size() >= workgroups * DEBUG_LDS_DWORDS * 4
+    _check(_lib.q8_0_debug_read_lds(_dev(seen, "seen"), int(workgroups), _stream()),
+           "q8_0_debug_read_lds")

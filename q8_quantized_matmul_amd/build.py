@@ -12,7 +12,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libq8_0.so")
-SOURCES = ["api.hip", "quantize.hip", "matvec.hip", "moe.hip", "gemm.hip", "skinny.hip", "probe.hip"]
+SOURCES = ["api.hip", "quantize.hip", "matvec.hip", "moe.hip", "gemm.hip", "skinny.hip", "probe.hip",
+           "debug.hip"]
 
 # -packed-fp32-ops: keep the compiler from emitting packed fp32 VALU forms.
 # No fast-math: the quantizer relies on IEEE division and roundf.

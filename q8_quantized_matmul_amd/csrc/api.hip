@@ -14,6 +14,8 @@
 
 static_assert(Q8_0_MOE_STATIC_SCRATCH_BYTES == q8::kMoeStaticScratchBytes,
               "header and library agree on the static routing scratch");
+static_assert(Q8_0_DEBUG_LDS_DWORDS == q8::kDebugLdsDwords,
+              "header and library agree on the LDS read-back size");
 
 namespace {
 
@@ -483,6 +485,19 @@ int q8_0_probe_mfma_mix(int32_t iters, int32_t mix, uint32_t *sink, hipStream_t 
   int st = check_device();
   if (st != Q8_0_OK) return st;
   return status_of(q8::launch_probe_mix(iters, mix, sink, stream));
+}
+
+int q8_0_debug_poison_lds(uint32_t pattern, hipStream_t stream) {
+  int st = check_device();
+  if (st != Q8_0_OK) return st;
+  return status_of(q8::launch_debug_poison_lds(pattern, stream));
+}
+
+int q8_0_debug_read_lds(uint32_t *seen, int32_t workgroups, hipStream_t stream) {
+  if (!seen || !aligned(seen, 4) || workgroups < 1 || workgroups > 4096) return Q8_0_EINVAL;
+  int st = check_device();
+  if (st != Q8_0_OK) return st;
+  return status_of(q8::launch_debug_read_lds(seen, workgroups, stream));
 }
 
 const char *q8_0_strerror(int status) {

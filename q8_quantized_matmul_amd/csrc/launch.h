@@ -123,5 +123,11 @@ hipError_t launch_probe_read(const void *buf, int64_t bytes, uint32_t *sink, hip
 hipError_t launch_probe_launch(int32_t workgroups, uint32_t *sink, hipStream_t s);
 hipError_t launch_probe_mfma(int32_t iters, uint32_t *sink, hipStream_t s);
 hipError_t launch_probe_mix(int32_t iters, int32_t mix, uint32_t *sink, hipStream_t s);
+// debug.hip: LDS poisoning for the race tests: kDebugLdsDwords of LDS per workgroup (five
+// workgroups fill a compute unit's 160 KB), four rounds of them per compute unit.
+constexpr int kDebugLdsDwords = 8192;
+constexpr int kDebugPoisonWorkgroups = 256 * 5 * 4;
+hipError_t launch_debug_poison_lds(uint32_t pattern, hipStream_t s);
+hipError_t launch_debug_read_lds(uint32_t *seen, int32_t workgroups, hipStream_t s);
 
 }  // namespace q8

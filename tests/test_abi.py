@@ -27,7 +27,7 @@ def q8():
 def test_exports_every_declared_symbol(q8):
     lib = ctypes.CDLL(q8.LIB_PATH)
     declared = _declared()
-    assert len(declared) == 18
+    assert len(declared) == 20
     for name in declared:
         assert hasattr(lib, name), name
     assert set(declared) == set(q8.EXPORTED)
@@ -269,6 +269,8 @@ def test_valid_call_without_device_reports_nodev(q8):
     items = (q8.MatmulItem * 2)(q8.MatmulItem(FAKE, FAKE, FAKE, None, 1024, 256),
                                 q8.MatmulItem(FAKE, FAKE, None, FAKE, 8192, 64))
     assert lib.q8_0_matmul_list(items, 2, 1, None) == q8.Q8_0_ENODEV
+    assert lib.q8_0_debug_poison_lds(0xFFFFFFFF, None) == q8.Q8_0_ENODEV
+    assert lib.q8_0_debug_read_lds(FAKE, 4, None) == q8.Q8_0_ENODEV
 
 
 def test_oracle_is_not_imported_by_the_product():
@@ -295,3 +297,7 @@ def test_probe_validation(q8):
     assert lib.q8_0_probe_launch(0, FAKE, None) == q8.Q8_0_EINVAL
     assert lib.q8_0_probe_launch(65537, FAKE, None) == q8.Q8_0_EINVAL
     assert lib.q8_0_probe_launch(16, None, None) == q8.Q8_0_EINVAL
+    assert lib.q8_0_debug_read_lds(None, 4, None) == q8.Q8_0_EINVAL
+    assert lib.q8_0_debug_read_lds(FAKE + 2, 4, None) == q8.Q8_0_EINVAL
+    assert lib.q8_0_debug_read_lds(FAKE, 0, None) == q8.Q8_0_EINVAL
+    assert lib.q8_0_debug_read_lds(FAKE, 4097, None) == q8.Q8_0_EINVAL
