@@ -66,7 +66,7 @@ Plan make_plan(int64_t in_dim, int64_t out_dim, int64_t n_tok, size_t ws_bytes, 
   const bool skinny_regime = n_tok >= kSkinnyMinTokens || (n_tok >= 2 && !matvec_ok(in_dim));
   if (skinny_regime && q8::skinny_supported(in_dim, n_tok)) {
     p.variant = Q8_0_KERNEL_SKINNY;
-    int split = q8::skinny_split_ok(out_dim, 2) ? q8::skinny_auto_split(in_dim, out_dim) : 1;
+    int split = q8::skinny_split_ok(out_dim, 2) ? q8::skinny_auto_split(in_dim, out_dim, n_tok) : 1;
     while (split > 1 && q8::skinny_workspace_bytes(out_dim, n_tok, split) > ws_bytes) --split;
     p.split = split;
   } else if (n_tok > q8::kSkinnyMaxTokens && q8::gemm_supported(in_dim)) {

@@ -97,7 +97,7 @@ constexpr size_t kWsCounterBytes = 4096;
 // weight rows staged in LDS, split-K reduced inside the launch.
 constexpr int64_t kSkinnyMaxTokens = 64;
 bool skinny_supported(int64_t in_dim, int64_t n_tok);
-int skinny_auto_split(int64_t in_dim, int64_t out_dim);
+int skinny_auto_split(int64_t in_dim, int64_t out_dim, int64_t n_tok);
 // A split needs one counter per 32-row output tile.
 bool skinny_split_ok(int64_t out_dim, int split);
 size_t skinny_workspace_bytes(int64_t out_dim, int64_t n_tok, int split);

@@ -29,6 +29,8 @@
 //     each workgroup leaves its sums in caller workspace and the last
 //     workgroup of an output tile to arrive adds them in split order.  Every
 //     sum has a fixed order: results are deterministic.
+//   * From 33 tokens with 64 to 128 output tiles, the two token tiles go to
+//     separate workgroups (grid z) instead of a K split (skinny_token_split).
 #include <algorithm>
 #include <utility>
 
@@ -257,9 +259,19 @@ __device__ __forceinline__ void skinny_step(const uint8_t *st, int lrow, int h, 
   }(std::make_integer_sequence<int, 4>{});
 }
 
-// MT token tiles of 32.  Grid: x = 32-row output tiles, y = K splits.
+// MT token tiles of 32.  Grid: x = 32-row output tiles, y = K splits, z =
+// 32-token tiles taken by separate workgroups (only with one split): the
+// workgroup at z reads and writes the rows from 32 z on.
 template <int MT, class COPY, bool STORE_S>
-__global__ __launch_bounds__(512) void skinny_kernel(const SkinnyArgs a) {
+__global__ __launch_bounds__(512) void skinny_kernel(const SkinnyArgs a0) {
+  SkinnyArgs a = a0;
+  if (blockIdx.z > 0) {
+    const int64_t t0 = 32 * (int64_t)blockIdx.z;
+    a.x_q += t0 * a.row_bytes;
+    a.out += t0 * a.out_dim;
+    if (a.blocksums) a.blocksums += t0 * a.out_dim * 2 * a.n_pairs;
+    a.n_tok -= t0;
+  }
   constexpr int NBUF = COPY::NBUF;
   constexpr int KQ = kWaves / MT;  // waves per token tile
   constexpr int PER = 2 * MT;      // values of the workgroup's tile set a wave finishes
@@ -444,13 +456,30 @@ bool skinny_supported(int64_t in_dim, int64_t n_tok) {
          n_tok <= kSkinnyMaxTokens;
 }
 
+// Token tiles in separate workgroups: from 33 tokens, with 64 to 128 output
+// tiles of 32 rows, one split and a workgroup per (row tile, token tile)
+// instead of one per row tile with both token tiles (and, below 128 tiles,
+// a K split with its in-launch completion).  Every weight row is then read
+// by two workgroups.  Graph replays at 64 tokens, one box: 4096 -> 2048
+// 8.63 -> 7.97 us (against split 4), 2048 -> 4096 8.14 -> 6.15 us (against
+// 128 workgroups); 7168 -> 2048 the same (11.1 us); with 32 tiles (4096 ->
+// 1024: 7.5 -> 7.65 us) too few workgroups remain, and with 1024 tiles
+// (1024 -> 32768 at 40 tokens: 20.7 -> 25.8 us) the second read of the
+// weights costs more than it saves.
+bool skinny_token_split(int64_t out_dim, int64_t n_tok) {
+  const int64_t tiles = (out_dim + 31) / 32;
+  return n_tok > 32 && tiles >= 64 && tiles <= 128;
+}
+
 // Splits.  The split-K completion (partials out, an arrival counter, the
 // last arrival's sum) puts about 1.5 us of serial memory round trips on the
 // critical path, so a split has to buy more than that: with 128 or more
 // tiles half the chip is already busy and one split is fastest; below that,
 // enough workgroups for the chip (about 256), at least 16 block pairs per
-// split (a full step for each of the eight waves), at most 16 splits.
-int skinny_auto_split(int64_t in_dim, int64_t out_dim) {
+// split (a full step for each of the eight waves), at most 16 splits; none
+// where the token tiles go to separate workgroups.
+int skinny_auto_split(int64_t in_dim, int64_t out_dim, int64_t n_tok) {
+  if (skinny_token_split(out_dim, n_tok)) return 1;
   const int64_t tiles = (out_dim + 31) / 32;
   const int64_t pairs = in_dim / 64;
   if (tiles >= 128) return 1;
@@ -492,11 +521,13 @@ hipError_t launch_skinny(float *out, int32_t *blocksums, const void *w, int64_t 
   a.n_tok = n_tok;
   a.row_bytes = (in_dim / 32) * 34;
   a.pairs_per_split = pps;
-  const dim3 grid((uint32_t)((out_dim + 31) / 32), (uint32_t)n_split);
+  const bool tsplit = n_split == 1 && skinny_token_split(out_dim, n_tok);
+  const dim3 grid((uint32_t)((out_dim + 31) / 32), (uint32_t)n_split,
+                  tsplit ? (uint32_t)((n_tok + 31) / 32) : 1u);
   // 16-byte copies need rows of 8k blocks and 16-aligned bases.
   const bool wide = in_dim % 256 == 0 && (reinterpret_cast<uintptr_t>(w) & 15) == 0 &&
                     (reinterpret_cast<uintptr_t>(x_q) & 15) == 0;
-  const int mt = skinny_mt(n_tok);
+  const int mt = tsplit ? 1 : skinny_mt(n_tok);
   const bool two_steps = pps > kStepPairs * (kWaves / mt);
   if (blocksums) launch_skinny_variant<true>(mt, two_steps, wide, grid, a, s);
   else launch_skinny_variant<false>(mt, two_steps, wide, grid, a, s);

@@ -221,7 +221,11 @@ def test_plan_regimes(q8):
     # below 128 tiles of 32 rows: about 256 workgroups, at least 16 block
     # pairs per split, at most 16 splits.
     assert q8.q8_0_matmul_plan(4096, 2048, 16, 1 << 40) == (q8.KERNEL_SKINNY, 4)
-    assert q8.q8_0_matmul_plan(4096, 2048, 64, 1 << 40) == (q8.KERNEL_SKINNY, 4)
+    # From 33 tokens with 64 to 128 row tiles the token tiles go to separate
+    # workgroups instead: one split, no workspace.
+    assert q8.q8_0_matmul_plan(4096, 2048, 64, 1 << 40) == (q8.KERNEL_SKINNY, 1)
+    assert q8.q8_0_matmul_plan(4096, 2048, 32, 1 << 40) == (q8.KERNEL_SKINNY, 4)
+    assert q8.q8_0_matmul_plan(4096, 1024, 33, 1 << 40) == (q8.KERNEL_SKINNY, 4)
     assert q8.q8_0_matmul_plan(4096, 2048, 64, 0) == (q8.KERNEL_SKINNY, 1)
     assert q8.q8_0_matmul_plan(2048, 4096, 16, 1 << 40) == (q8.KERNEL_SKINNY, 1)
     assert q8.q8_0_matmul_plan(2048, 4064, 16, 1 << 40) == (q8.KERNEL_SKINNY, 2)
@@ -232,7 +236,8 @@ def test_plan_regimes(q8):
     assert q8.q8_0_matmul_plan(65536, 256, 20, 1 << 40) == (q8.KERNEL_SKINNY, 16)
     # Split-K workspace: 4096 bytes of arrival counters, then 4 KiB of
     # partials per 32-token tile for each workgroup (64 tiles x 4 splits).
-    assert q8.q8_0_matmul_workspace_bytes(4096, 2048, 64) == 4096 + 4 * 64 * 2 * 4096
+    assert q8.q8_0_matmul_workspace_bytes(4096, 2048, 64) == 0
+    assert q8.q8_0_matmul_workspace_bytes(4096, 1024, 64) == 4096 + 4 * 32 * 2 * 4096
     assert q8.q8_0_matmul_workspace_bytes(4096, 2048, 16) == 4096 + 4 * 64 * 1 * 4096
     assert q8.q8_0_matmul_debug_workspace_bytes(4096, 2048, 64, q8.KERNEL_SKINNY, 2) == \
         4096 + 2 * 64 * 2 * 4096
