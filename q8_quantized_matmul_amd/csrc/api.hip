@@ -22,7 +22,8 @@ namespace {
 // Regimes by token count (measured on 4096->2048, 2048->4096, 4096->1024,
 // 4096->512 and 1024->32768, graph-replayed calls): the weight-streaming
 // matvec below 12 tokens, the skinny matrix-core kernel (one launch, split-K
-// inside it) from 12 to 64, the LDS-tiled GEMM above.  Rows the matvec
+// inside it) from 12 to 64 and, for shapes skinny_many_tokens accepts, up to
+// 256; the LDS-tiled GEMM above.  Rows the matvec
 // cannot take (pair counts that are neither a power of two below 64 nor a
 // multiple of 64, e.g. in_dim 1536 or 7168) go to the skinny kernel from two
 // tokens: the generic kernel's cost grows by 3-4 us per token there.
@@ -63,7 +64,9 @@ bool matvec_ok(int64_t in_dim) { return q8::matvec_shape(in_dim, nullptr); }
 Plan make_plan(int64_t in_dim, int64_t out_dim, int64_t n_tok, size_t ws_bytes, bool fast_align) {
   Plan p{Q8_0_KERNEL_GENERIC, 1};
   if (!fast_align) return p;
-  const bool skinny_regime = n_tok >= kSkinnyMinTokens || (n_tok >= 2 && !matvec_ok(in_dim));
+  const bool skinny_regime =
+      (n_tok <= q8::kSkinnyMaxTokens && (n_tok >= kSkinnyMinTokens || (n_tok >= 2 && !matvec_ok(in_dim)))) ||
+      q8::skinny_many_tokens(in_dim, out_dim, n_tok);
   if (skinny_regime && q8::skinny_supported(in_dim, n_tok)) {
     p.variant = Q8_0_KERNEL_SKINNY;
     int split = q8::skinny_split_ok(out_dim, 2) ? q8::skinny_auto_split(in_dim, out_dim, n_tok) : 1;
@@ -99,6 +102,9 @@ int forced_plan(int64_t in_dim, int64_t out_dim, int64_t n_tok, size_t ws_bytes,
     p.split = split_k;
   }
   if (p.variant == Q8_0_KERNEL_SKINNY && !q8::skinny_split_ok(out_dim, p.split)) return Q8_0_EINVAL;
+  // Above kSkinnyMaxTokens the skinny kernel runs one split only.
+  if (p.variant == Q8_0_KERNEL_SKINNY && n_tok > q8::kSkinnyMaxTokens && p.split > 1)
+    return Q8_0_EINVAL;
   *out = p;
   return Q8_0_OK;
 }

@@ -93,10 +93,16 @@ hipError_t launch_moe(float *out, int32_t *blocksums, const void *const *expert_
 // kWsCounterBytes, partial sums after them.
 constexpr size_t kWsCounterBytes = 4096;
 
-// skinny.hip: matrix-core matmul for up to kSkinnyMaxTokens tokens, token and
-// weight rows staged in LDS, split-K reduced inside the launch.
+// skinny.hip: matrix-core matmul, token and weight rows staged in LDS.  Up to
+// kSkinnyMaxTokens tokens a workgroup may hold both token tiles and split-K
+// is reduced inside the launch; up to kSkinnyWideMaxTokens every 32-token
+// tile has workgroups of its own and there is one split.
 constexpr int64_t kSkinnyMaxTokens = 64;
+constexpr int64_t kSkinnyWideMaxTokens = 256;
 bool skinny_supported(int64_t in_dim, int64_t n_tok);
+// Shapes for which the plan prefers the skinny kernel to the tiled GEMM from
+// kSkinnyMaxTokens + 1 to kSkinnyWideMaxTokens tokens.
+bool skinny_many_tokens(int64_t in_dim, int64_t out_dim, int64_t n_tok);
 int skinny_auto_split(int64_t in_dim, int64_t out_dim, int64_t n_tok);
 // A split needs one counter per 32-row output tile.
 bool skinny_split_ok(int64_t out_dim, int split);

@@ -1,6 +1,7 @@
-// skinny.hip -- Q8_0 matmul for up to 64 tokens on the matrix cores (the
-// plan uses it from 12 tokens, from 2 for rows the matvec cannot take), a
-// 32-row output tile per workgroup.
+// skinny.hip -- Q8_0 matmul for up to 256 tokens on the matrix cores (the
+// plan uses it from 12 to 64 tokens, from 2 for rows the matvec cannot take,
+// and up to 256 for moderate shapes, skinny_many_tokens), a 32-row output
+// tile per workgroup.
 //
 // The method is the same as everywhere (ds4-learning "Part 6: 代码走读",
 // trace 3: out[t][o] = sum over blocks of d_w * d_x * S_b); this kernel
@@ -30,7 +31,8 @@
 //     workgroup of an output tile to arrive adds them in split order.  Every
 //     sum has a fixed order: results are deterministic.
 //   * From 33 tokens with 64 to 128 output tiles, the two token tiles go to
-//     separate workgroups (grid z) instead of a K split (skinny_token_split).
+//     separate workgroups (grid z) instead of a K split (skinny_token_split);
+//     above 64 tokens (up to 256) every token tile does, with one split.
 #include <algorithm>
 #include <utility>
 
@@ -453,7 +455,22 @@ int skinny_mt(int64_t n_tok) { return n_tok > 32 ? 2 : 1; }
 
 bool skinny_supported(int64_t in_dim, int64_t n_tok) {
   return in_dim > 0 && in_dim % 64 == 0 && (in_dim / 32) * kBlockBytes <= (1 << 24) && n_tok >= 1 &&
-         n_tok <= kSkinnyMaxTokens;
+         n_tok <= kSkinnyWideMaxTokens;
+}
+
+// Above 64 tokens, graph replays on one box (tiled GEMM with its own split
+// -> this kernel, one workgroup per (32-row tile, 32-token tile), one split):
+// 4096 -> 2048 at 65 / 128 / 256 tokens 19.0 / 18.6 / 21.6 -> 8.4 / 9.0 /
+// 15.9 us, 2048 -> 4096 18.0 / 18.9 / 21.5 -> 9.8 / 10.5 / 18.4, 4096 -> 1024
+// 14.1 / 13.5 / 17.9 -> 7.7 / 7.9 / 8.7, 7168 -> 2048 20.4 / 19.7 / 24.2 ->
+// 11.3 / 12.0 / 22.0.  The GEMM stays ahead where every token tile would
+// re-read many weights (1024 -> 32768: 24.2 against 37.1 us at 65 tokens)
+// and where long rows leave too few workgroups without a K split (32768 ->
+// 1024: 37.4 against 43.6 us); at 512 tokens 4096 -> 2048 is even (28.9 /
+// 29.3 us).  Hence: rows of at most 128 block pairs, at most 128 row tiles.
+bool skinny_many_tokens(int64_t in_dim, int64_t out_dim, int64_t n_tok) {
+  return n_tok > kSkinnyMaxTokens && n_tok <= kSkinnyWideMaxTokens && in_dim / 64 <= 128 &&
+         (out_dim + 31) / 32 <= 128;
 }
 
 // Token tiles in separate workgroups: from 33 tokens, with 64 to 128 output
@@ -479,7 +496,7 @@ bool skinny_token_split(int64_t out_dim, int64_t n_tok) {
 // split (a full step for each of the eight waves), at most 16 splits; none
 // where the token tiles go to separate workgroups.
 int skinny_auto_split(int64_t in_dim, int64_t out_dim, int64_t n_tok) {
-  if (skinny_token_split(out_dim, n_tok)) return 1;
+  if (n_tok > kSkinnyMaxTokens || skinny_token_split(out_dim, n_tok)) return 1;
   const int64_t tiles = (out_dim + 31) / 32;
   const int64_t pairs = in_dim / 64;
   if (tiles >= 128) return 1;
@@ -511,6 +528,7 @@ hipError_t launch_skinny(float *out, int32_t *blocksums, const void *w, int64_t 
   // Splits are whole steps (the last one may be short).
   const int pps = ((a.n_pairs + split - 1) / split + kStepPairs - 1) / kStepPairs * kStepPairs;
   const int n_split = (a.n_pairs + pps - 1) / pps;
+  if (n_tok > kSkinnyMaxTokens && n_split > 1) return hipErrorInvalidValue;
   if (n_split > 1) {
     a.arrivals = static_cast<uint32_t *>(workspace);
     a.partials = reinterpret_cast<float *>(static_cast<uint8_t *>(workspace) + kWsCounterBytes);
@@ -521,7 +539,8 @@ hipError_t launch_skinny(float *out, int32_t *blocksums, const void *w, int64_t 
   a.n_tok = n_tok;
   a.row_bytes = (in_dim / 32) * 34;
   a.pairs_per_split = pps;
-  const bool tsplit = n_split == 1 && skinny_token_split(out_dim, n_tok);
+  const bool tsplit =
+      n_tok > kSkinnyMaxTokens || (n_split == 1 && skinny_token_split(out_dim, n_tok));
   const dim3 grid((uint32_t)((out_dim + 31) / 32), (uint32_t)n_split,
                   tsplit ? (uint32_t)((n_tok + 31) / 32) : 1u);
   // 16-byte copies need rows of 8k blocks and 16-aligned bases.

@@ -245,8 +245,21 @@ def test_plan_regimes(q8):
     # A skinny split needs one counter per 32-row tile: at most 1024 tiles.
     assert q8.q8_0_matmul_debug_workspace_bytes(1024, 32768, 64, q8.KERNEL_SKINNY, 2) > 0
     assert q8.q8_0_matmul_debug_workspace_bytes(1024, 32800, 64, q8.KERNEL_SKINNY, 2) == 0
-    # Above 64 tokens the tiled GEMM; split-K aims for 256 workgroups.
-    assert q8.q8_0_matmul_plan(4096, 2048, 65, 1 << 40)[0] == q8.KERNEL_MFMA
+    # From 65 to 256 tokens the skinny kernel for rows of at most 128 block
+    # pairs and at most 128 row tiles (every token tile in workgroups of its
+    # own, one split, no workspace); the GEMM otherwise.
+    assert q8.q8_0_matmul_plan(4096, 2048, 65, 1 << 40) == (q8.KERNEL_SKINNY, 1)
+    assert q8.q8_0_matmul_plan(8192, 4096, 256, 1 << 40) == (q8.KERNEL_SKINNY, 1)
+    assert q8.q8_0_matmul_workspace_bytes(4096, 1024, 200) == 0
+    assert q8.q8_0_matmul_plan(4096, 2048, 257, 1 << 40)[0] == q8.KERNEL_MFMA
+    assert q8.q8_0_matmul_plan(8256, 2048, 128, 1 << 40)[0] == q8.KERNEL_MFMA
+    assert q8.q8_0_matmul_plan(4096, 4128, 128, 1 << 40)[0] == q8.KERNEL_MFMA
+    assert q8.q8_0_matmul_plan(32768, 1024, 128, 1 << 40)[0] == q8.KERNEL_MFMA
+    # A forced K split above 64 tokens is refused.
+    lib = q8.raw_library()
+    assert lib.q8_0_matmul_debug(FAKE, None, FAKE, 4096, 2048, FAKE, 100, FAKE, 1 << 30,
+                                 q8.KERNEL_SKINNY, 2, None) == q8.Q8_0_EINVAL
+    # Above that the tiled GEMM; split-K aims for 256 workgroups.
     assert q8.q8_0_matmul_plan(1024, 32768, 128, 1 << 40) == (q8.KERNEL_MFMA, 1)
     assert q8.q8_0_matmul_plan(4096, 2048, 4096, 1 << 40) == (q8.KERNEL_MFMA, 1)
     v, s = q8.q8_0_matmul_plan(32768, 1024, 2048, 1 << 40)

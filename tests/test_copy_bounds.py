@@ -5,8 +5,9 @@ The hardware range check on those loads covers the lane's voffset (plus the
 instruction offset) against the resource's num_records; the scalar offset is
 not part of the check.  These tests restate the kernel's address arithmetic
 (DwordCopies and ChunkCopies, and the launcher's split of the block pairs)
-and check, for every token count 1..64, several ragged out_dims, every
-n_pairs % 4 case and every split the launcher can pick:
+and check, for every token count 1..64 (and, for token tiles in workgroups
+of their own, counts up to 256), several ragged out_dims, every n_pairs % 4
+case and every split the launcher can pick:
   * every copy that passes the range check reads inside the operand buffer;
   * every byte the kernel multiplies (a valid row, a pair below the split's
     end) passes the range check and lands at the LDS byte the operand reads
@@ -65,8 +66,9 @@ def dword_groups(m, o_tile, n_tok, out_dim):
     return out
 
 
-def check_shape(n_tok, in_dim, out_dim, split):
-    mt = 2 if n_tok > 32 else 1
+def check_shape(n_tok, in_dim, out_dim, split, mt=None):
+    if mt is None:
+        mt = 2 if n_tok > 32 else 1
     nb = in_dim // 32
     row_bytes = nb * 34
     n_pairs = in_dim // 64
@@ -163,6 +165,23 @@ def test_skinny_dword_copies_stay_in_bounds(n_pairs):
         for out_dim in (32, 48, 67):
             for split in sorted({1, 2, 3, max(1, n_pairs // 4), 16}):
                 check_shape(n_tok, in_dim, out_dim, split)
+
+
+def test_skinny_token_tiles_in_separate_workgroups_stay_in_bounds():
+    """From 33 tokens the launcher may give every 32-token tile workgroups of
+    its own (grid z, one split; always above 64 tokens, up to 256): the
+    workgroup at z reads the x rows from 32 z on, n_tok - 32 z of them, with
+    one token tile.  Its copies are those of a one-tile call on that slice."""
+    for n_pairs in (1, 3, 5, 13, 64):
+        for n_tok in (33, 40, 63, 64, 65, 100, 128, 200, 255, 256):
+            for out_dim in (32, 67):
+                for z in range((n_tok + 31) // 32):
+                    rest = n_tok - 32 * z
+                    if n_pairs <= 13:
+                        check_shape(rest, 64 * n_pairs, out_dim, 1, mt=1)
+                    if n_pairs % 4 == 0:
+                        for pair0 in (0, n_pairs - STEP_PAIRS):
+                            check_chunk_copies(1, rest, out_dim, n_pairs, 0, pair0)
 
 
 def test_skinny_dword_copies_model_catches_an_unchecked_offset():
