@@ -32,7 +32,8 @@
 //     sum has a fixed order: results are deterministic.
 //   * From 33 tokens with 64 to 128 output tiles, the two token tiles go to
 //     separate workgroups (grid z) instead of a K split (skinny_token_split);
-//     above 64 tokens (up to 256) every token tile does, with one split.
+//     above 64 tokens (up to 256) every token tile does, with one split or,
+//     for long rows, two (partials and counters per row and token tile).
 #include <algorithm>
 #include <utility>
 
@@ -262,8 +263,8 @@ __device__ __forceinline__ void skinny_step(const uint8_t *st, int lrow, int h, 
 }
 
 // MT token tiles of 32.  Grid: x = 32-row output tiles, y = K splits, z =
-// 32-token tiles taken by separate workgroups (only with one split): the
-// workgroup at z reads and writes the rows from 32 z on.
+// 32-token tiles taken by separate workgroups (then MT = 1): the workgroup
+// at z reads and writes the rows from 32 z on.
 template <int MT, class COPY, bool STORE_S>
 __global__ __launch_bounds__(512) void skinny_kernel(const SkinnyArgs a0) {
   SkinnyArgs a = a0;
@@ -351,10 +352,13 @@ __global__ __launch_bounds__(512) void skinny_kernel(const SkinnyArgs a0) {
     // before the barrier that precedes the arrival.  A fence at device scope
     // would write back and invalidate the whole L2 of the XCD in every
     // workgroup instead.
-    const int64_t tiles = gridDim.x;
+    // Output tiles: (32-row tile, 32-token tile) pairs of a grid with token
+    // tiles in z, else 32-row tiles.
+    const int64_t tiles = (int64_t)gridDim.x * gridDim.z;
+    const int64_t tile = (int64_t)blockIdx.z * gridDim.x + blockIdx.x;
     constexpr int VALS = MT * 16 * 64;  // floats per workgroup
     const int64_t slot = (int64_t)(PER * wave) * 64 + lane;
-    const int64_t mine_off = ((int64_t)blockIdx.y * tiles + blockIdx.x) * VALS + slot;
+    const int64_t mine_off = ((int64_t)blockIdx.y * tiles + tile) * VALS + slot;
 #pragma unroll
     for (int k = 0; k < PER; ++k)
       __hip_atomic_store(a.partials + mine_off + k * 64, v[k], __ATOMIC_RELAXED,
@@ -364,12 +368,12 @@ __global__ __launch_bounds__(512) void skinny_kernel(const SkinnyArgs a0) {
     __builtin_amdgcn_s_barrier();  // ... and every wave's
     asm volatile("" ::: "memory");
     if (threadIdx.x == 0)
-      arrived_before = __hip_atomic_fetch_add(a.arrivals + blockIdx.x, 1u, __ATOMIC_RELAXED,
+      arrived_before = __hip_atomic_fetch_add(a.arrivals + tile, 1u, __ATOMIC_RELAXED,
                                               __HIP_MEMORY_SCOPE_AGENT);
     __syncthreads();
     if (arrived_before != gridDim.y - 1) return;  // uniform: one LDS value
     float sum[PER];
-    const int64_t first = (int64_t)blockIdx.x * VALS + slot;
+    const int64_t first = tile * VALS + slot;
     for (int s0 = 0; s0 < (int)gridDim.y; s0 += 4) {
       float p[4][PER];
 #pragma unroll
@@ -389,7 +393,7 @@ __global__ __launch_bounds__(512) void skinny_kernel(const SkinnyArgs a0) {
           if (s0 + j < (int)gridDim.y) sum[k] = s0 + j == 0 ? p[j][k] : sum[k] + p[j][k];
     }
     if (threadIdx.x == 0)
-      __hip_atomic_store(a.arrivals + blockIdx.x, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(a.arrivals + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 #pragma unroll
     for (int k = 0; k < PER; ++k) v[k] = sum[k];
   }
@@ -467,10 +471,17 @@ bool skinny_supported(int64_t in_dim, int64_t n_tok) {
 // re-read many weights (1024 -> 32768: 24.2 against 37.1 us at 65 tokens)
 // and where long rows leave too few workgroups without a K split (32768 ->
 // 1024: 37.4 against 43.6 us); at 512 tokens 4096 -> 2048 is even (28.9 /
-// 29.3 us).  Hence: rows of at most 128 block pairs, at most 128 row tiles.
+// 29.3 us).  Hence rows of at most 128 block pairs and at most 128 row
+// tiles, with one split (a K split measured slower on them, or even).  Long
+// rows with few row tiles take two splits up to 128 tokens (partials per row
+// and token tile): 32768 -> 1024 at 65 / 128 tokens 39.2 / 37.1 -> 26.6 /
+// 29.5 us (4 and 8 splits slower; at 256 tokens the GEMM, 38.8 against
+// 48.8 us); with more row tiles (16384 -> 2048, -> 4096) the GEMM leads.
 bool skinny_many_tokens(int64_t in_dim, int64_t out_dim, int64_t n_tok) {
-  return n_tok > kSkinnyMaxTokens && n_tok <= kSkinnyWideMaxTokens && in_dim / 64 <= 128 &&
-         (out_dim + 31) / 32 <= 128;
+  if (n_tok <= kSkinnyMaxTokens || n_tok > kSkinnyWideMaxTokens) return false;
+  const int64_t pairs = in_dim / 64, tiles = (out_dim + 31) / 32;
+  if (pairs <= 128 && tiles <= 128) return true;
+  return n_tok <= 128 && pairs >= 256 && tiles <= 32;
 }
 
 // Token tiles in separate workgroups: from 33 tokens, with 64 to 128 output
@@ -496,7 +507,8 @@ bool skinny_token_split(int64_t out_dim, int64_t n_tok) {
 // split (a full step for each of the eight waves), at most 16 splits; none
 // where the token tiles go to separate workgroups.
 int skinny_auto_split(int64_t in_dim, int64_t out_dim, int64_t n_tok) {
-  if (n_tok > kSkinnyMaxTokens || skinny_token_split(out_dim, n_tok)) return 1;
+  if (n_tok > kSkinnyMaxTokens) return in_dim / 64 > 128 ? 2 : 1;
+  if (skinny_token_split(out_dim, n_tok)) return 1;
   const int64_t tiles = (out_dim + 31) / 32;
   const int64_t pairs = in_dim / 64;
   if (tiles >= 128) return 1;
@@ -508,14 +520,20 @@ int skinny_auto_split(int64_t in_dim, int64_t out_dim, int64_t n_tok) {
 
 // Workspace of a split-K launch: the arrival counters (zero between calls)
 // in the first kWsCounterBytes, then the partials, MT * 4 KiB per workgroup.
+// (4 KiB per 32-token tile and workgroup: with token tiles in workgroups of
+// their own one each, else MT each -- the same bytes.)
 size_t skinny_workspace_bytes(int64_t out_dim, int64_t n_tok, int split) {
   if (split <= 1) return 0;
   const int64_t tiles = (out_dim + 31) / 32;
-  return kWsCounterBytes + (size_t)split * (size_t)tiles * (size_t)skinny_mt(n_tok) * 4096;
+  return kWsCounterBytes + (size_t)split * (size_t)tiles * (size_t)((n_tok + 31) / 32) * 4096;
 }
 
-bool skinny_split_ok(int64_t out_dim, int split) {
-  return split <= 1 || (out_dim + 31) / 32 <= (int64_t)(kWsCounterBytes / 4);
+// One arrival counter per output tile: per 32-row tile, and per token tile
+// too where those have workgroups of their own (above kSkinnyMaxTokens).
+bool skinny_split_ok(int64_t out_dim, int64_t n_tok, int split) {
+  const int64_t tiles =
+      (out_dim + 31) / 32 * (n_tok > kSkinnyMaxTokens ? (n_tok + 31) / 32 : 1);
+  return split <= 1 || tiles <= (int64_t)(kWsCounterBytes / 4);
 }
 
 hipError_t launch_skinny(float *out, int32_t *blocksums, const void *w, int64_t in_dim,
@@ -528,7 +546,6 @@ hipError_t launch_skinny(float *out, int32_t *blocksums, const void *w, int64_t 
   // Splits are whole steps (the last one may be short).
   const int pps = ((a.n_pairs + split - 1) / split + kStepPairs - 1) / kStepPairs * kStepPairs;
   const int n_split = (a.n_pairs + pps - 1) / pps;
-  if (n_tok > kSkinnyMaxTokens && n_split > 1) return hipErrorInvalidValue;
   if (n_split > 1) {
     a.arrivals = static_cast<uint32_t *>(workspace);
     a.partials = reinterpret_cast<float *>(static_cast<uint8_t *>(workspace) + kWsCounterBytes);

@@ -254,11 +254,18 @@ def test_plan_regimes(q8):
     assert q8.q8_0_matmul_plan(4096, 2048, 257, 1 << 40)[0] == q8.KERNEL_MFMA
     assert q8.q8_0_matmul_plan(8256, 2048, 128, 1 << 40)[0] == q8.KERNEL_MFMA
     assert q8.q8_0_matmul_plan(4096, 4128, 128, 1 << 40)[0] == q8.KERNEL_MFMA
-    assert q8.q8_0_matmul_plan(32768, 1024, 128, 1 << 40)[0] == q8.KERNEL_MFMA
-    # A forced K split above 64 tokens is refused.
-    lib = q8.raw_library()
-    assert lib.q8_0_matmul_debug(FAKE, None, FAKE, 4096, 2048, FAKE, 100, FAKE, 1 << 30,
-                                 q8.KERNEL_SKINNY, 2, None) == q8.Q8_0_EINVAL
+    # Long rows with at most 32 row tiles: two splits up to 128 tokens.
+    assert q8.q8_0_matmul_plan(32768, 1024, 128, 1 << 40) == (q8.KERNEL_SKINNY, 2)
+    assert q8.q8_0_matmul_plan(32768, 1024, 128, 0) == (q8.KERNEL_SKINNY, 1)
+    assert q8.q8_0_matmul_plan(32768, 1024, 129, 1 << 40)[0] == q8.KERNEL_MFMA
+    assert q8.q8_0_matmul_plan(16384, 2048, 100, 1 << 40)[0] == q8.KERNEL_MFMA
+    # A K split above 64 tokens: partials and a counter per (row tile, token
+    # tile); at most 1024 counters.
+    assert q8.q8_0_matmul_debug_workspace_bytes(4096, 2048, 100, q8.KERNEL_SKINNY, 2) == \
+        4096 + 2 * 64 * 4 * 4096
+    assert q8.q8_0_matmul_debug_workspace_bytes(4096, 4096, 256, q8.KERNEL_SKINNY, 2) == \
+        4096 + 2 * 128 * 8 * 4096
+    assert q8.q8_0_matmul_debug_workspace_bytes(4096, 4128, 256, q8.KERNEL_SKINNY, 2) == 0
     # Above that the tiled GEMM; split-K aims for 256 workgroups.
     assert q8.q8_0_matmul_plan(1024, 32768, 128, 1 << 40) == (q8.KERNEL_MFMA, 1)
     assert q8.q8_0_matmul_plan(4096, 2048, 4096, 1 << 40) == (q8.KERNEL_MFMA, 1)
