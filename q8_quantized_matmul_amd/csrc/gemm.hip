@@ -731,7 +731,15 @@ int gemm_auto_split(int64_t in_dim, int64_t out_dim, int64_t n_tok) {
   const int64_t nb = in_dim / kBlockElems;
   const int tj = gemm_tj(n_tok);
   const int64_t tiles = ((out_dim + 127) / 128) * ((n_tok + 64 * tj - 1) / (64 * tj));
-  int64_t split = (256 + tiles - 1) / tiles;           // aim for >= 256 workgroups
+  // Aim for >= 256 workgroups, >= 512 from 256 tokens.  Forced splits, graph
+  // replays on one box: at 256 / 512 tokens 16384 -> 4096 69.6 -> 60.4 us
+  // (4 -> 8 splits), 16384 -> 2048 at 512 66.5 -> 56.8 (4 -> 8), 32768 ->
+  // 1024 at 512 65.2 -> 57.2 (8 -> 16), 4096 -> 8192 at 256 40.8 -> 39.0
+  // (2 -> 4) and at 512 59.7 -> 61.3 (1 -> 2); below 256 tokens 256
+  // workgroups measured best or even (16384 -> 4096 at 65: 43.5 us with 8
+  // splits, 49.7 with 16).
+  const int64_t want = n_tok >= 256 ? 512 : 256;
+  int64_t split = (want + tiles - 1) / tiles;
   split = std::max<int64_t>(split, (nb + 127) / 128);  // fp32 chains of <= 128 blocks
   split = std::min<int64_t>(split, nb / (2 * kStageBlocks));
   split = std::min<int64_t>(split, 16);
