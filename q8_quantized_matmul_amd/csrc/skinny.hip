@@ -263,13 +263,13 @@ __device__ __forceinline__ void skinny_step(const uint8_t *st, int lrow, int h, 
 }
 
 // MT token tiles of 32.  Grid: x = 32-row output tiles, y = K splits, z =
-// 32-token tiles taken by separate workgroups (then MT = 1): the workgroup
-// at z reads and writes the rows from 32 z on.
+// groups of MT token tiles taken by separate workgroups: the workgroup at z
+// reads and writes the token rows from 32 MT z on.
 template <int MT, class COPY, bool STORE_S>
 __global__ __launch_bounds__(512) void skinny_kernel(const SkinnyArgs a0) {
   SkinnyArgs a = a0;
   if (blockIdx.z > 0) {
-    const int64_t t0 = 32 * (int64_t)blockIdx.z;
+    const int64_t t0 = 32 * MT * (int64_t)blockIdx.z;
     a.x_q += t0 * a.row_bytes;
     a.out += t0 * a.out_dim;
     if (a.blocksums) a.blocksums += t0 * a.out_dim * 2 * a.n_pairs;
@@ -558,12 +558,21 @@ hipError_t launch_skinny(float *out, int32_t *blocksums, const void *w, int64_t 
   a.pairs_per_split = pps;
   const bool tsplit =
       n_tok > kSkinnyMaxTokens || (n_split == 1 && skinny_token_split(out_dim, n_tok));
-  const dim3 grid((uint32_t)((out_dim + 31) / 32), (uint32_t)n_split,
-                  tsplit ? (uint32_t)((n_tok + 31) / 32) : 1u);
+  // Above kSkinnyMaxTokens with one split, two token tiles per workgroup
+  // where that still leaves >= 192 workgroups (row tiles x 32-token tiles >=
+  // 384): the weights are read half as often.  Graph replays, one box, one
+  // tile -> two per workgroup: 2048 -> 4096 at 65 / 128 / 256 tokens 10.0 /
+  // 10.5 / 18.6 -> 8.7 / 9.0 / 15.6 us, 4096 -> 2048 at 192 / 256 14.9 /
+  // 15.7 -> 13.0 / 13.5, 8192 -> 2048 at 256 24.3 -> 23.0; with fewer tiles
+  // slower (4096 -> 2048 at 128: 9.0 -> 12.6, 4096 -> 1024: 8.0 -> 11.8).
+  const int64_t rtiles = (out_dim + 31) / 32, ttiles = (n_tok + 31) / 32;
+  const int tz = n_tok > kSkinnyMaxTokens && n_split == 1 && rtiles * ttiles >= 384 ? 2 : 1;
+  const dim3 grid((uint32_t)rtiles, (uint32_t)n_split,
+                  tsplit ? (uint32_t)((ttiles + tz - 1) / tz) : 1u);
   // 16-byte copies need rows of 8k blocks and 16-aligned bases.
   const bool wide = in_dim % 256 == 0 && (reinterpret_cast<uintptr_t>(w) & 15) == 0 &&
                     (reinterpret_cast<uintptr_t>(x_q) & 15) == 0;
-  const int mt = tsplit ? 1 : skinny_mt(n_tok);
+  const int mt = tsplit ? tz : skinny_mt(n_tok);
   const bool two_steps = pps > kStepPairs * (kWaves / mt);
   if (blocksums) launch_skinny_variant<true>(mt, two_steps, wide, grid, a, s);
   else launch_skinny_variant<false>(mt, two_steps, wide, grid, a, s);

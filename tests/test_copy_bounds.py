@@ -169,19 +169,21 @@ def test_skinny_dword_copies_stay_in_bounds(n_pairs):
 
 def test_skinny_token_tiles_in_separate_workgroups_stay_in_bounds():
     """From 33 tokens the launcher may give every 32-token tile workgroups of
-    its own (grid z, one split; always above 64 tokens, up to 256): the
-    workgroup at z reads the x rows from 32 z on, n_tok - 32 z of them, with
-    one token tile.  Its copies are those of a one-tile call on that slice."""
+    its own (grid z; always above 64 tokens, up to 256, then with one or two
+    token tiles per workgroup): the workgroup at z reads the x rows from
+    32 mt z on, n_tok - 32 mt z of them (possibly fewer than its mt tiles
+    hold).  Its copies are those of an mt-tile call on that slice."""
     for n_pairs in (1, 3, 5, 13, 64):
         for n_tok in (33, 40, 63, 64, 65, 100, 128, 200, 255, 256):
             for out_dim in (32, 67):
-                for z in range((n_tok + 31) // 32):
-                    rest = n_tok - 32 * z
-                    if n_pairs <= 13:
-                        check_shape(rest, 64 * n_pairs, out_dim, 1, mt=1)
-                    if n_pairs % 4 == 0:
-                        for pair0 in (0, n_pairs - STEP_PAIRS):
-                            check_chunk_copies(1, rest, out_dim, n_pairs, 0, pair0)
+                for mt in (1, 2):   # token tiles per workgroup
+                    for z in range((n_tok + 32 * mt - 1) // (32 * mt)):
+                        rest = n_tok - 32 * mt * z
+                        if n_pairs <= 13:
+                            check_shape(rest, 64 * n_pairs, out_dim, 1, mt=mt)
+                        if n_pairs % 4 == 0:
+                            for pair0 in (0, n_pairs - STEP_PAIRS):
+                                check_chunk_copies(mt, rest, out_dim, n_pairs, 0, pair0)
 
 
 def test_skinny_dword_copies_model_catches_an_unchecked_offset():
