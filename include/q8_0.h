@@ -66,7 +66,7 @@ enum {
     Q8_0_KERNEL_GENERIC = 1, /* one block per lane, any shape           */
     Q8_0_KERNEL_MATVEC = 2,  /* weight-streaming matvec, small n_tok     */
     Q8_0_KERNEL_MFMA = 3,    /* int8 MFMA GEMM, large n_tok              */
-    Q8_0_KERNEL_SKINNY = 4   /* int8 MFMA, rows staged in LDS, n_tok <= 64 */
+    Q8_0_KERNEL_SKINNY = 4   /* int8 MFMA, rows staged in LDS, n_tok <= 256 */
 };
 
 /* Quantize activations to Q8_0 ("Part 3: 模型架构", section 2 rule, per
@@ -272,8 +272,8 @@ int q8_0_matmul_list(const q8_0_matmul_item *items, int32_t n_items, int64_t n_t
  * The kernel that runs is the one the same call without blocksums would run
  * (its debug instantiation), so the S_b checked are those of the timed path.
  * Errors as q8_0_matmul, plus Q8_0_EINVAL when the forced variant cannot run
- * this shape (also a skinny split-K over more than 1024 output tiles of 32
- * rows), and Q8_0_EWORKSPACE when a forced split needs more workspace than
+ * this shape (also a skinny split-K over more than 1024 output tiles: tiles
+ * of 32 rows, and of 32 rows x 32 tokens above 64 tokens), and Q8_0_EWORKSPACE when a forced split needs more workspace than
  * q8_0_matmul_debug_workspace_bytes() reports for it. */
 int q8_0_matmul_debug(float *out, int32_t *blocksums, const void *w,
                       int64_t in_dim, int64_t out_dim, const void *x_q,
