@@ -164,7 +164,9 @@ def test_skinny_workspace_reuse_and_graph():
     the in-launch split-K arrival counters are back at zero after every call,
     so later calls and graph replays find them armed."""
     q8 = _q8()
-    shapes = [(4096, 2048, 64, 4), (2048, 256, 20, 8), (4160, 2048, 64, 4), (4096, 2048, 64, 4)]
+    # Above 64 tokens a split keeps one counter per (row tile, token tile).
+    shapes = [(4096, 2048, 64, 4), (2048, 256, 20, 8), (16384, 520, 100, 2), (4160, 2048, 64, 4),
+              (4096, 2048, 64, 4), (16384, 520, 100, 2)]
     need = max(q8.q8_0_matmul_debug_workspace_bytes(k, n, t, q8.KERNEL_SKINNY, sp)
                for k, n, t, sp in shapes)
     ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
@@ -186,25 +188,25 @@ def test_skinny_workspace_reuse_and_graph():
         if (k, n, t) in firsts:
             assert torch.equal(out.view(torch.int32), firsts[(k, n, t)].view(torch.int32))
         firsts[(k, n, t)] = out
-    # Graph capture of a split-K call; every replay equals the eager result.
-    k, n, t, sp = shapes[0]
-    wq, xq, _, _ = data[(k, n, t)]
-    out = torch.empty((t, n), device="cuda")
-    s = torch.cuda.Stream()
-    s.wait_stream(torch.cuda.current_stream())
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.stream(s):
-        with torch.cuda.graph(g, stream=s):
-            q8.q8_0_matmul_debug(wq, xq, k, n, t, variant=q8.KERNEL_SKINNY, split_k=sp,
-                                 blocksums=False, out=out, workspace=ws)
-    torch.cuda.current_stream().wait_stream(s)
-    for rep in range(3):
-        out.fill_(float("nan"))
-        torch.cuda.synchronize()
-        g.replay()
-        torch.cuda.synchronize()
-        assert torch.equal(out.view(torch.int32), firsts[(k, n, t)].view(torch.int32)), rep
-        assert not ws[:4096].any()
+    # Graph capture of split-K calls; every replay equals the eager result.
+    for k, n, t, sp in (shapes[0], shapes[2]):
+        wq, xq, _, _ = data[(k, n, t)]
+        out = torch.empty((t, n), device="cuda")
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(s):
+            with torch.cuda.graph(g, stream=s):
+                q8.q8_0_matmul_debug(wq, xq, k, n, t, variant=q8.KERNEL_SKINNY, split_k=sp,
+                                     blocksums=False, out=out, workspace=ws)
+        torch.cuda.current_stream().wait_stream(s)
+        for rep in range(3):
+            out.fill_(float("nan"))
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(out.view(torch.int32), firsts[(k, n, t)].view(torch.int32)), rep
+            assert not ws[:4096].any()
 
 
 @pytest.mark.parametrize("only_block", [None, 0, 1, 2, 3, 6, 7])
