@@ -69,7 +69,7 @@ Plan make_plan(int64_t in_dim, int64_t out_dim, int64_t n_tok, size_t ws_bytes, 
       q8::skinny_many_tokens(in_dim, out_dim, n_tok);
   if (skinny_regime && q8::skinny_supported(in_dim, n_tok)) {
     p.variant = Q8_0_KERNEL_SKINNY;
-    int split = q8::skinny_split_ok(out_dim, n_tok, 2) ? q8::skinny_auto_split(in_dim, out_dim, n_tok) : 1;
+    int split = q8::skinny_split_ok(in_dim, out_dim, n_tok, 2) ? q8::skinny_auto_split(in_dim, out_dim, n_tok) : 1;
     while (split > 1 && q8::skinny_workspace_bytes(out_dim, n_tok, split) > ws_bytes) --split;
     p.split = split;
   } else if (n_tok > q8::kSkinnyMaxTokens && q8::gemm_supported(in_dim)) {
@@ -101,7 +101,7 @@ int forced_plan(int64_t in_dim, int64_t out_dim, int64_t n_tok, size_t ws_bytes,
       return Q8_0_EINVAL;
     p.split = split_k;
   }
-  if (p.variant == Q8_0_KERNEL_SKINNY && !q8::skinny_split_ok(out_dim, n_tok, p.split)) return Q8_0_EINVAL;
+  if (p.variant == Q8_0_KERNEL_SKINNY && !q8::skinny_split_ok(in_dim, out_dim, n_tok, p.split)) return Q8_0_EINVAL;
   *out = p;
   return Q8_0_OK;
 }

@@ -105,7 +105,7 @@ bool skinny_supported(int64_t in_dim, int64_t n_tok);
 bool skinny_many_tokens(int64_t in_dim, int64_t out_dim, int64_t n_tok);
 int skinny_auto_split(int64_t in_dim, int64_t out_dim, int64_t n_tok);
 // A split needs one counter per 32-row output tile.
-bool skinny_split_ok(int64_t out_dim, int64_t n_tok, int split);
+bool skinny_split_ok(int64_t in_dim, int64_t out_dim, int64_t n_tok, int split);
 size_t skinny_workspace_bytes(int64_t out_dim, int64_t n_tok, int split);
 hipError_t launch_skinny(float *out, int32_t *blocksums, const void *w, int64_t in_dim,
                          int64_t out_dim, const void *x_q, int64_t n_tok, int split,

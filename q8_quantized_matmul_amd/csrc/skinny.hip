@@ -31,7 +31,9 @@
 //     workgroup of an output tile to arrive adds them in split order.  Every
 //     sum has a fixed order: results are deterministic.
 //   * From 33 tokens with 64 to 128 output tiles, the two token tiles go to
-//     separate workgroups (grid z) instead of a K split (skinny_token_split);
+//     separate workgroups (grid z) instead of a K split (skinny_token_split),
+//     and with fewer tiles too for rows of up to 64 pairs, beside their K
+//     split (skinny_tile_rows);
 //     above 64 tokens (up to 256) every token tile does, with one split or,
 //     for long rows, two (partials and counters per row and token tile).
 #include <algorithm>
@@ -494,7 +496,20 @@ bool skinny_many_tokens(int64_t in_dim, int64_t out_dim, int64_t n_tok) {
 // 1024: 7.5 -> 7.65 us) too few workgroups remain, and with 1024 tiles
 // (1024 -> 32768 at 40 tokens: 20.7 -> 25.8 us) the second read of the
 // weights costs more than it saves.
-bool skinny_token_split(int64_t out_dim, int64_t n_tok) {
+//
+// Below 64 row tiles, rows of up to 64 block pairs split their token tiles
+// the same way and keep their K split (graph replays, one box, both tiles in
+// one workgroup -> one per workgroup): 4096 -> 1024 at 64 tokens 7.59 ->
+// 6.63 us, 4096 -> 512 at 48 7.25 -> 5.80, 4096 -> 256 at 64 6.65 -> 5.53,
+// 1024 -> 520 at 40 4.93 -> 3.72; with the eight splits of longer rows it
+// was slower (8192 -> 1024 at 48: 9.6 -> 12.3 us, 32768 -> 1024 at 64:
+// 19.1 -> 22.9).
+static bool skinny_tile_rows(int64_t in_dim, int64_t out_dim, int64_t n_tok) {
+  const int64_t tiles = (out_dim + 31) / 32;
+  return n_tok > 32 && n_tok <= kSkinnyMaxTokens && tiles <= 128 &&
+         (tiles >= 64 || in_dim / 64 <= 64);
+}
+static bool skinny_token_split(int64_t out_dim, int64_t n_tok) {
   const int64_t tiles = (out_dim + 31) / 32;
   return n_tok > 32 && tiles >= 64 && tiles <= 128;
 }
@@ -529,10 +544,10 @@ size_t skinny_workspace_bytes(int64_t out_dim, int64_t n_tok, int split) {
 }
 
 // One arrival counter per output tile: per 32-row tile, and per token tile
-// too where those have workgroups of their own (above kSkinnyMaxTokens).
-bool skinny_split_ok(int64_t out_dim, int64_t n_tok, int split) {
-  const int64_t tiles =
-      (out_dim + 31) / 32 * (n_tok > kSkinnyMaxTokens ? (n_tok + 31) / 32 : 1);
+// too where those have workgroups of their own.
+bool skinny_split_ok(int64_t in_dim, int64_t out_dim, int64_t n_tok, int split) {
+  const bool own = n_tok > kSkinnyMaxTokens || skinny_tile_rows(in_dim, out_dim, n_tok);
+  const int64_t tiles = (out_dim + 31) / 32 * (own ? (n_tok + 31) / 32 : 1);
   return split <= 1 || tiles <= (int64_t)(kWsCounterBytes / 4);
 }
 
@@ -556,8 +571,7 @@ hipError_t launch_skinny(float *out, int32_t *blocksums, const void *w, int64_t 
   a.n_tok = n_tok;
   a.row_bytes = (in_dim / 32) * 34;
   a.pairs_per_split = pps;
-  const bool tsplit =
-      n_tok > kSkinnyMaxTokens || (n_split == 1 && skinny_token_split(out_dim, n_tok));
+  const bool tsplit = n_tok > kSkinnyMaxTokens || skinny_tile_rows(in_dim, out_dim, n_tok);
   // Above kSkinnyMaxTokens with one split, two token tiles per workgroup
   // where that still leaves >= 192 workgroups (row tiles x 32-token tiles >=
   // 384): the weights are read half as often.  Graph replays, one box, one

@@ -137,7 +137,7 @@ def _run_skinny(wq, xq, wq_o, xq_o, in_dim, out_dim, n_tok, split, where):
     (2048, 4096, 64, 1), (2048, 4096, 33, 1), (4096, 2050, 40, 1), (4160, 2048, 63, 1),
     (4096, 2048, 65, 1), (2048, 2048, 96, 0), (4160, 1000, 130, 0), (1024, 2050, 256, 0),
     (8192, 512, 200, 0), (192, 70, 129, 0), (16384, 520, 65, 0), (8192, 300, 130, 3),
-    (4160, 100, 250, 2), (2048, 4096, 65, 0), (4096, 2048, 200, 1)])
+    (4160, 100, 250, 2), (2048, 4096, 65, 0), (4096, 2048, 200, 1), (4096, 520, 40, 0)])
 def test_skinny_shapes(in_dim, out_dim, n_tok, split):
     # Ragged rows and token counts, one or two token tiles, waves with no
     # block pair (192 values = 3 pairs), and split-K with uneven splits; K
@@ -151,7 +151,8 @@ def test_skinny_shapes(in_dim, out_dim, n_tok, split):
     # there (partials and counters per row and token tile: the plan's two
     # splits for long rows, forced uneven splits, dword copies), and two
     # token tiles per workgroup where the grid is large (one token, then
-    # eight, in the last workgroup).
+    # eight, in the last workgroup).  From 33 tokens, rows of up to 64 pairs
+    # also split their token tiles beside a K split (4096 -> 520 at 40).
     w = workloads.normal((out_dim, in_dim), 0.02, "cuda", "sk", out_dim, in_dim, "w")
     x = workloads.normal((n_tok, in_dim), 1.0, "cuda", "sk", n_tok, in_dim, "x")
     x[min(3, n_tok - 1), 40:50] *= 30.0  # outlier block
